@@ -1,0 +1,26 @@
+"""CPU oracle for the quantized video-DiT linear layer.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, step-by-step NumPy
+statement of what the method computes.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code with
+the HIP library (it imports nothing from ``bit_quantized_linear_vq_amd``), and the
+library never calls it.
+
+Steps and the passages they follow:
+
+* ``numerics``  storage-dtype conversions (fp16/bf16 <-> fp32, round-to-nearest-even).
+* ``detect``    outlier input channels by modified z-score of channel L2 norms
+                (Q-ARVD page, Methodology: outlier-aware adaptive dual-scale quantization).
+* ``quantizer`` symmetric absmax quantizer; per-tensor activations, per-channel weights
+                (Q-ARVD page, Methodology and Technical details); dual-scale split
+                Q_dual(W) = [Q_outlier(W_outliers) | Q_normal(W_normal)] (same passage);
+                offline 4-bit weights (6Bit-Diffusion page, Methodology B.1, DMPQ).
+* ``fwht``      128-point block Hadamard rotation (6Bit-Diffusion page, Methodology B.1:
+                online block Hadamard transform against outliers).
+* ``gemm``      exact integer GEMM and the dequantization epilogue
+                (Q-ARVD page, Technical details: activation quantization and GEMM/dequantization kernels).
+* ``route``     relative-L1 routing statistic Gamma and the INT8-vs-4-bit decision
+                (6Bit-Diffusion page, Key Insights 1 and Methodology B.1, DMPQ).
+* ``linear``    the whole layer, chaining the steps above.
+"""
+from . import numerics, detect, quantizer, fwht, gemm, route, linear  # noqa: F401
