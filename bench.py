@@ -1,0 +1,262 @@
+"""Benchmark of the quantized video-DiT linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step is the whole online path of the layer on one batch: activation
+quantization (per-token int8 codes and scales) followed by the int8 MFMA GEMM with
+the fused dequantization epilogue.  Weight packing (and, where used, outlier
+detection) happens once before timing, as it would offline.  The default workload
+is the fused-QKV projection of a 2B video DiT: X bf16 [17776 x 1920] (1% of the
+channels x30), W [5760 x 1920], W8A8.  Inputs sit in HBM before timing; the
+activation tensor is rotated over four copies (273 MB, more than the 256 MB
+Infinity Cache) so that every step reads it from HBM.
+
+Prints one JSON line.  ``value`` = 2*M*N*K integer operations per step / step time
+(TOPS).  ``roofline`` describes the GEMM kernel (int8 MFMA peak 5000 TOPS), with its
+average duration taken from HIP events recorded around each launch on the launch
+stream.  ``act_quant`` gives the quantization kernel against the 8 TB/s HBM peak.
+``cpu_baseline`` times the CPU oracle on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def kernel_hash(name):
+    with open(os.path.join(ROOT, "bit_quantized_linear_vq_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_sha") != kernel_hash("k_qgemm.hip"):
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Layer:
+    """Device buffers and launch closures for one configuration."""
+
+    def __init__(self, cfg, vq, gen, torch, dev):
+        c = gen.CONFIGS[cfg]
+        self.cfg, self.c = cfg, c
+        self.M, self.K, self.N = c["M"], c["K"], c["N"]
+        self.vq, self.torch = vq, torch
+        xd = gen.make_x(cfg).to(dev)
+        self.x = [xd] + [xd.clone() for _ in range(3)]
+        self.idx = None
+        self.had = c["had"]
+        self.a_bits = c["a_bits"] or 8
+        self.gran = c["gran"]
+        self.layers = c.get("layers", 1)
+        if cfg == 5:
+            self.w = []
+            self.bits_dev = []
+            for l in range(self.layers):
+                w = gen.make_w(cfg, layer=l).to(dev)
+                self.w.append(vq.vq_pack_weights(w, c["w_bits"]))
+                del w
+                xp, yp, _ = gen.make_route_pair(cfg, l)
+                bits, _ = vq.vq_route_rel_l1(xp.to(dev), yp.to(dev), c["route_threshold"],
+                                             c["route_hi_bits"], c["route_lo_bits"])
+                self.bits_dev.append(bits)
+            torch.cuda.synchronize()
+            self.routes = [int(b.item()) for b in self.bits_dev]
+        else:
+            w = gen.make_w(cfg).to(dev)
+            if c["dual"]:
+                _, idx, _ = vq.vq_detect_outliers(w)
+                self.idx = idx.to(dev)
+            self.w = [vq.vq_pack_weights(w, c["w_bits"], self.idx, self.had)]
+            self.bits_dev = [None]
+            del w
+        n_out = 0 if self.idx is None else int(self.idx.numel())
+        self.kp = vq.vq_packed_k(self.K, n_out)
+        self.k0 = self.K if n_out else self.kp
+        self.codes = torch.empty((self.M, self.kp), dtype=torch.int8, device=dev)
+        if self.gran == "token":
+            self.scales = torch.empty((self.M, 2) if n_out else (self.M,), dtype=torch.float32, device=dev)
+        else:
+            self.scales = torch.empty((2 if n_out else 1,), dtype=torch.float32, device=dev)
+        self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16 if c["dtype"] == "bf16" else torch.float16,
+                             device=dev)
+        torch.cuda.synchronize()
+
+    def quant(self, step, layer):
+        self.vq.vq_quant_act(self.x[step % len(self.x)], self.a_bits, self.gran, self.had, self.idx,
+                             bits_dev=self.bits_dev[layer], codes=self.codes, scales=self.scales)
+
+    def gemm(self, layer):
+        wc, ws = self.w[layer]
+        self.vq.vq_qgemm_dequant(self.codes, self.scales, wc, ws, self.c["w_bits"], self.k0, self.y.dtype,
+                                 self.gran == "token", y=self.y)
+
+    def ops_per_step(self):
+        return 2.0 * self.M * self.N * self.K * self.layers
+
+    def quant_bytes(self):
+        # read 2 B per input element, write 1 B per code (padding included), 4 B per scale
+        return self.M * self.K * 2 + self.M * self.kp + self.scales.numel() * 4
+
+
+def cpu_baseline(cfg, budget_s):
+    """The CPU oracle, as it stands, on a bounded row sample of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import gen
+    import oracle
+
+    c = gen.CONFIGS[cfg]
+    if cfg == 5:
+        w = gen.make_w(cfg, layer=0)
+    else:
+        w = gen.make_w(cfg)
+    wnp = gen.as_numpy_bits(w)
+    idx = None
+    if c["dual"]:
+        idx = oracle.linear.detect_on(wnp, c["dtype"])["idx"]
+    wcodes, _, wscales = oracle.linear.prepare_weights(wnp, c["dtype"], c["w_bits"], c["had"], idx)
+    x = gen.as_numpy_bits(gen.make_x(cfg))
+    chunk = 256
+    rows = 0
+    t0 = time.perf_counter()
+    while rows < x.shape[0] and time.perf_counter() - t0 < budget_s:
+        xs = x[rows:rows + chunk]
+        oracle.linear.forward(xs, c["dtype"], c["a_bits"] or 8, c["gran"], wcodes, wscales, c["had"], idx)
+        rows += xs.shape[0]
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    tops = 2.0 * rows * c["N"] * c["K"] / dt / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {x.shape[0]} rows of X against the full W (one layer), {dt:.1f} s; "
+                      f"steps: activation quantization, exact integer GEMM (float64 BLAS), float32 epilogue"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import bit_quantized_linear_vq_amd as vq
+    import gen
+
+    dev = torch.device("cuda:0")
+    L = Layer(args.config, vq, gen, torch, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        for l in range(L.layers):
+            if ev is not None:
+                ev[0].record(stream)
+            L.quant(i, l)
+            if ev is not None:
+                ev[1].record(stream)
+            L.gemm(l)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps between two synchronizations.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # Per-kernel durations: HIP events around every launch on the launch stream.
+    evs = []
+    for i in range(args.steps):
+        for l in range(L.layers):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            L.quant(i, l)
+            e[1].record(stream)
+            L.gemm(l)
+            e[2].record(stream)
+            evs.append(e)
+    torch.cuda.synchronize()
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    g_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+
+    ops_layer = 2.0 * L.M * L.N * L.K
+    gemm_tops = ops_layer / (g_ms * 1e-3) / 1e12
+    quant_gbs = L.quant_bytes() / (q_ms * 1e-3) / 1e9
+    tops = L.ops_per_step() / (ms * 1e-3) / 1e12
+    workload = gen.CONFIGS[args.config]["name"]
+    traffic = load_traffic(workload)
+
+    out = {
+        "metric": "quantized-linear TOPS (int8 MFMA %peak) + act-quant GB/s (%HBM), 1 MI355X",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": workload, "M": L.M, "K": L.K, "N": L.N, "layers": L.layers,
+                   "w_bits": L.c["w_bits"], "a_bits": L.c["a_bits"] if L.c["a_bits"] else "routed 8/4",
+                   "act_granularity": L.gran, "hadamard_block": L.had,
+                   "outlier_channels": 0 if L.idx is None else int(L.idx.numel()),
+                   "out_dtype": str(L.y.dtype).replace("torch.", "")},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "kernel": "k_qgemm (int8 MFMA GEMM + dequant epilogue)", "avg_us": round(g_ms * 1e3, 2)},
+        "act_quant": {"bound": "hbm", "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "bytes": L.quant_bytes(),
+                      "avg_us": round(q_ms * 1e3, 2), "kernel": "k_rowquant"},
+    }
+    if args.config == 5:
+        out["config"]["routes_int8"] = L.routes.count(8)
+        out["config"]["routes_int4"] = L.routes.count(4)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

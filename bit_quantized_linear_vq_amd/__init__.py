@@ -1,0 +1,204 @@
+"""Python binding of libvq.so, the gfx950 quantized linear layer for video DiTs.
+
+Argument marshalling only: every function takes torch tensors on the GPU, checks
+their dtype/shape/contiguity, allocates missing outputs with torch (device memory
+is PyTorch's), and calls the C entry point of the same name on torch's current
+stream.  All arithmetic happens in the HIP kernels; if libvq.so is missing the
+import of this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvq.so")
+
+VQ_OK, VQ_ERR_INVALID_ARG, VQ_ERR_SHAPE, VQ_ERR_UNSUPPORTED, VQ_ERR_HIP = range(5)
+VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
+VQ_PER_TENSOR, VQ_PER_TOKEN, VQ_PER_TENSOR_STATIC = 0, 1, 2
+VQ_K_ALIGN = 64
+VQ_HAD_BLOCK = 128
+VQ_MAX_OUTLIERS = 128
+
+EXPORTS = (
+    "vq_outlier_part_len", "vq_packed_k", "vq_detect_workspace_elems", "vq_detect_outliers",
+    "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant",
+    "vq_route_workspace_elems", "vq_route_rel_l1", "vq_status_string", "vq_last_hip_error", "vq_version",
+)
+
+_DT = {torch.float16: VQ_F16, torch.bfloat16: VQ_BF16, torch.float32: VQ_F32}
+_GRAN = {"tensor": VQ_PER_TENSOR, "token": VQ_PER_TOKEN, "static": VQ_PER_TENSOR_STATIC}
+
+
+class VQError(RuntimeError):
+    def __init__(self, fn, status, text, hip):
+        super().__init__(f"{fn} failed: status {status} ({text}); last HIP error {hip}")
+        self.status = status
+        self.hip_error = hip
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m bit_quantized_linear_vq_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, I, D, F = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
+                            ctypes.c_double, ctypes.c_float)
+    sig = {
+        "vq_outlier_part_len": (I64, [I32]),
+        "vq_packed_k": (I64, [I64, I32]),
+        "vq_detect_workspace_elems": (I64, [I64, I64]),
+        "vq_detect_outliers": (I, [P, I, I64, I64, I64, D, D, D, P, P, P, P, P, P]),
+        "vq_pack_weights": (I, [P, I, I64, I64, I64, I, P, I32, I, P, P, P]),
+        "vq_quant_act": (I, [P, I, I64, I64, I64, I, P, I, I, P, I32, P, P, P, P]),
+        "vq_hadamard_block": (I, [P, I, I64, P, I, I64, I64, I64, I, I, P]),
+        "vq_qgemm_dequant": (I, [P, P, I, P, I, P, I64, I64, I64, I64, P, I, I64, P, P]),
+        "vq_route_workspace_elems": (I64, [I64]),
+        "vq_route_rel_l1": (I, [P, P, I, I64, D, I, I, P, P, P, P]),
+        "vq_status_string": (ctypes.c_char_p, [I]),
+        "vq_last_hip_error": (I, []),
+        "vq_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(fn, status):
+    if status != VQ_OK:
+        raise VQError(fn, status, _lib.vq_status_string(status).decode(), _lib.vq_last_hip_error())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    return t
+
+
+def vq_outlier_part_len(n_out: int) -> int:
+    return int(_lib.vq_outlier_part_len(n_out))
+
+
+def vq_packed_k(k: int, n_out: int) -> int:
+    return int(_lib.vq_packed_k(k, n_out))
+
+
+def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kfac: float = 1.0, ws=None):
+    """Outlier input channels (columns) of x.  Returns (mask uint8 [K], idx int32 [n_out], norms f64 [K]) on the host."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if ws is None:
+        ws = torch.empty(int(_lib.vq_detect_workspace_elems(rows, cols)), dtype=torch.float64, device=x.device)
+    norms = torch.empty(cols, dtype=torch.float64)
+    mask = torch.empty(cols, dtype=torch.uint8)
+    idx = torch.empty(cols, dtype=torch.int32)
+    n_out = ctypes.c_int32(0)
+    _check("vq_detect_outliers", _lib.vq_detect_outliers(
+        _ptr(x), _DT.get(x.dtype, -1), rows, cols, x.stride(0), tau, alpha, kfac, _ptr(ws),
+        _ptr(norms), _ptr(mask), _ptr(idx), ctypes.byref(n_out), _stream(x)))
+    return mask, idx[: n_out.value].clone(), norms
+
+
+def vq_pack_weights(w: torch.Tensor, bits: int, idx: torch.Tensor | None = None, had_block: int = 0,
+                    codes=None, scales=None):
+    """Per-output-channel codes of W [N x K].  Returns (codes, scales)."""
+    _dev(w, "w")
+    n, k = w.shape
+    n_out = 0 if idx is None else int(idx.numel())
+    kp = vq_packed_k(k, n_out)
+    if codes is None:
+        codes = (torch.empty((n, kp), dtype=torch.int8, device=w.device) if bits == 8
+                 else torch.empty((n, kp // 2), dtype=torch.uint8, device=w.device))
+    if scales is None:
+        scales = torch.empty((n, 2) if n_out else (n,), dtype=torch.float32, device=w.device)
+    _check("vq_pack_weights", _lib.vq_pack_weights(
+        _ptr(w), _DT.get(w.dtype, -1), n, k, w.stride(0), bits, _ptr(idx), n_out, had_block,
+        _ptr(codes), _ptr(scales), _stream(w)))
+    return codes, scales
+
+
+def vq_quant_act(x: torch.Tensor, bits: int, gran: str = "token", had_block: int = 0,
+                 idx: torch.Tensor | None = None, static_scale: torch.Tensor | None = None,
+                 bits_dev: torch.Tensor | None = None, codes=None, scales=None):
+    """Online activation codes of X [M x K].  Returns (codes int8 [M x kp], scales)."""
+    _dev(x, "x")
+    m, k = x.shape
+    n_out = 0 if idx is None else int(idx.numel())
+    kp = vq_packed_k(k, n_out)
+    g = _GRAN[gran]
+    if codes is None:
+        codes = torch.empty((m, kp), dtype=torch.int8, device=x.device)
+    if scales is None:
+        parts = 2 if n_out else 1
+        shape = ((m, 2) if n_out else (m,)) if g == VQ_PER_TOKEN else (parts,)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check("vq_quant_act", _lib.vq_quant_act(
+        _ptr(x), _DT.get(x.dtype, -1), m, k, x.stride(0), bits, _ptr(bits_dev), g, had_block,
+        _ptr(idx), n_out, _ptr(static_scale), _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def vq_hadamard_block(x: torch.Tensor, out_dtype=None, normalize: bool = True, block: int = 128, y=None):
+    """Block Hadamard rotation of the rows of x (128-element blocks)."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty((rows, cols), dtype=out_dtype or x.dtype, device=x.device)
+    _check("vq_hadamard_block", _lib.vq_hadamard_block(
+        _ptr(x), _DT.get(x.dtype, -1), x.stride(0), _ptr(y), _DT.get(y.dtype, -1), y.stride(0), rows, cols,
+        block, int(bool(normalize)), _stream(x)))
+    return y
+
+
+def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor, b_bits: int,
+                     k0: int | None = None, out_dtype=torch.bfloat16, sa_per_token: bool = True,
+                     acc_debug: bool = False, y=None, acc=None):
+    """Y = dequant(A_codes . B_codes^T).  Returns y, or (y, acc int32 [P x M x N]) with acc_debug."""
+    _dev(a, "a")
+    m, kp = a.shape
+    n = b.shape[0]
+    k0 = kp if k0 is None else k0
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if acc_debug and acc is None:
+        acc = torch.empty((2 if k0 < kp else 1, m, n), dtype=torch.int32, device=a.device)
+    _check("vq_qgemm_dequant", _lib.vq_qgemm_dequant(
+        _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
+        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None), _stream(a)))
+    return (y, acc) if acc_debug else y
+
+
+def vq_route_rel_l1(x: torch.Tensor, y: torch.Tensor, threshold: float = 0.1, bits_hi: int = 8, bits_lo: int = 4,
+                    ws=None, gamma=None, bits=None):
+    """Device-side DMPQ route: returns (bits int32 [1], gamma float64 [1]) on the device."""
+    _dev(x, "x")
+    n = x.numel()
+    if ws is None:
+        ws = torch.empty(int(_lib.vq_route_workspace_elems(n)), dtype=torch.float64, device=x.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float64, device=x.device)
+    if bits is None:
+        bits = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check("vq_route_rel_l1", _lib.vq_route_rel_l1(
+        _ptr(x), _ptr(y), _DT.get(x.dtype, -1), n, threshold, bits_hi, bits_lo, _ptr(ws), _ptr(gamma),
+        _ptr(bits), _stream(x)))
+    return bits, gamma
+
+
+def vq_version() -> str:
+    return _lib.vq_version().decode()

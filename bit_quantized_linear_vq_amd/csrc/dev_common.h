@@ -1,0 +1,184 @@
+// Device helpers shared by the gfx950 kernels of the quantized linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vqk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+
+enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+
+__device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
+
+// Materializes a float32 value in a register before it is narrowed: without it the
+// compiler may fold fptrunc(fmul) into v_fma_mix*, rounding the exact product once to
+// 16 bits instead of first to float32 and then to 16 bits.
+__device__ __forceinline__ float f32_fence(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
+
+// Two packed 16-bit values of a dword -> floats (element 2i in the low half).
+template <int DT>
+__device__ __forceinline__ void decode2(unsigned u, float& lo, float& hi) {
+  if constexpr (DT == DT_BF16) {
+    lo = bits_f(u << 16);
+    hi = bits_f(u & 0xFFFF0000u);
+  } else {
+    _Float16 a = __builtin_bit_cast(_Float16, (unsigned short)(u & 0xFFFFu));
+    _Float16 b = __builtin_bit_cast(_Float16, (unsigned short)(u >> 16));
+    lo = (float)a;
+    hi = (float)b;
+  }
+}
+
+// 16 consecutive elements starting at p (16-byte aligned) as float.
+template <int DT>
+__device__ __forceinline__ void load16(const void* p, float v[16]) {
+  if constexpr (DT == DT_F32) {
+    const u4v* q = reinterpret_cast<const u4v*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u4v w = __builtin_nontemporal_load(q + i);
+      v[4 * i + 0] = bits_f(w.x);
+      v[4 * i + 1] = bits_f(w.y);
+      v[4 * i + 2] = bits_f(w.z);
+      v[4 * i + 3] = bits_f(w.w);
+    }
+  } else {
+    const u4v* q = reinterpret_cast<const u4v*>(p);
+    u4v w0 = __builtin_nontemporal_load(q);
+    u4v w1 = __builtin_nontemporal_load(q + 1);
+    decode2<DT>(w0.x, v[0], v[1]);
+    decode2<DT>(w0.y, v[2], v[3]);
+    decode2<DT>(w0.z, v[4], v[5]);
+    decode2<DT>(w0.w, v[6], v[7]);
+    decode2<DT>(w1.x, v[8], v[9]);
+    decode2<DT>(w1.y, v[10], v[11]);
+    decode2<DT>(w1.z, v[12], v[13]);
+    decode2<DT>(w1.w, v[14], v[15]);
+  }
+}
+
+// One element of a storage dtype as float.
+template <int DT>
+__device__ __forceinline__ float load1(const void* p, int64_t i) {
+  if constexpr (DT == DT_BF16) {
+    return bits_f(((unsigned)reinterpret_cast<const unsigned short*>(p)[i]) << 16);
+  } else if constexpr (DT == DT_F16) {
+    return (float)reinterpret_cast<const _Float16*>(p)[i];
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+// Wave-wide maximum of non-negative floats (exact: max is order independent).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// 128-point Sylvester Hadamard butterflies held in registers.
+//
+// A 128-element block is spread over 8 consecutive lanes, 16 contiguous elements
+// per lane.  Lane slot l (0..7) holds element group g = perm8(l), i.e. elements
+// 16g .. 16g+15, with perm8 = (0,1,2,3,7,6,5,4).  With that assignment the three
+// cross-lane butterfly distances map onto single DPP moves:
+//   h = 16 (group bit 0): lane xor 1      -> quad_perm [1,0,3,2]
+//   h = 32 (group bit 1): lane xor 2      -> quad_perm [2,3,0,1]
+//   h = 64 (group bit 2): lane 7 - lane   -> row_half_mirror
+// Distances 1, 2, 4, 8 are inside a lane.  The stages run in ascending h.
+//
+// Cross-lane stages keep a per-lane sign: the lane holding the lower index of a
+// pair computes fl(mine + partner); the upper lane computes fl(mine - partner),
+// which is exactly -(z_lo - z_hi).  Partners always carry the same sign, so the
+// stored value is sigma * z with sigma = (-1)^popcount(g); negation is exact in
+// IEEE arithmetic, so sigma is folded into the consumer's multiplier.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int perm8(int l) { return l < 4 ? l : 11 - l; }
+
+__device__ __forceinline__ float had_sigma(int g) { return (__builtin_popcount(g) & 1) ? -1.0f : 1.0f; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return bits_f((unsigned)__builtin_amdgcn_update_dpp(0, (int)f_bits(v), CTRL, 0xF, 0xF, false));
+}
+
+// In-lane stages h = 1, 2, 4, 8 over 16 contiguous elements.
+__device__ __forceinline__ void fwht16_inlane(float v[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// All seven stages; g = this lane's element group (0..7).  Returns sigma.
+// Cross-lane stage: v = fl(partner * c + mine) with c = +1 on the lower lane of the
+// pair and -1 on the upper lane; partner * c is exact, so the fma rounds once.
+__device__ __forceinline__ float fwht128(float v[16], int g) {
+  fwht16_inlane(v);
+  const float c0 = (g & 1) ? -1.0f : 1.0f;
+  const float c1 = (g & 2) ? -1.0f : 1.0f;
+  const float c2 = (g & 4) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0xB1>(v[i]), c0, v[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x4E>(v[i]), c1, v[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x141>(v[i]), c2, v[i]);
+  return had_sigma(g);
+}
+
+// ---------------------------------------------------------------------------
+// Round-half-even quantization through the float32 magic constant 1.5 * 2^23:
+// for |t| <= 2^22, fl(t + 12582912) = 12582912 + rne(t) exactly (the sum is
+// rounded once, to an integer, and 12582912 is even), so the code's two's
+// complement byte is the low byte of the sum's bit pattern.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned qbyte(float x, float r, float qf) {
+  float t = x * r;
+  t = __builtin_amdgcn_fmed3f(t, -qf, qf);
+  return f_bits(t + 12582912.0f);
+}
+
+// Low bytes of four dwords -> one dword (byte i from u_i).
+__device__ __forceinline__ unsigned pack4_lo(unsigned u0, unsigned u1, unsigned u2, unsigned u3) {
+  unsigned lo = __builtin_amdgcn_perm(u1, u0, 0x0c0c0400u);
+  unsigned hi = __builtin_amdgcn_perm(u3, u2, 0x04000c0cu);
+  return lo | hi;
+}
+
+// Low nibbles of the low bytes of u[0..7] -> one dword of 8 packed 4-bit codes,
+// element 2j in the low nibble of byte j.
+__device__ __forceinline__ unsigned pack8_nibbles(const unsigned u[8]) {
+  unsigned r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    unsigned b = (u[2 * j] & 0xFu) | ((u[2 * j + 1] & 0xFu) << 4);
+    r |= b << (8 * j);
+  }
+  return r;
+}
+
+}  // namespace vqk

@@ -1,0 +1,370 @@
+// Row quantization kernels for gfx950: online activation quantization (per token,
+// per tensor, static), the dual-scale outlier partition, the fused 128-point block
+// Hadamard rotation, and offline per-output-channel weight packing (int8 / int4).
+//
+// Q-ARVD (aitrends.kr), Methodology and Technical details: per-tensor activation and
+// per-channel weight quantizers, Q_dual = [Q_outlier | Q_normal] over input channels,
+// an activation-quantization kernel ahead of the GEMM.  6Bit-Diffusion (gist.science,
+// arXiv 2603.18742), Methodology B.1: INT8 or 4-bit activations per block, online block
+// Hadamard, weights quantized offline to 4 bits.
+//
+// Work layout: a row of K elements is read in passes of 1024 elements; in a pass each
+// of the 64 lanes of a wave owns 16 contiguous elements (two 16-byte loads, one
+// 16-byte store of codes).  A row is owned by W waves (W = 1, 2, 4 or 8) so that every
+// lane keeps at most 4 passes (64 floats) in registers: the row is read from HBM once,
+// reduced to its absolute maximum, and quantized from registers.
+#include "dev_common.h"
+#include "vq_internal.h"
+
+namespace vqk {
+
+enum : int { MODE_ROW = 0, MODE_GLOBAL = 1, MODE_STATIC = 2 };
+constexpr int NPMAX = 4;
+constexpr int MAX_MASK_WORDS = 32768 / 32;
+
+struct RowArgs {
+  const void* x;
+  int64_t ldx;
+  int64_t rows;
+  int k;               // row length of x
+  int kp;              // code row length (k + p1)
+  int W;               // waves per row
+  int np;              // passes per wave
+  int qbits;           // bit width when bits_dev is null
+  const int32_t* bits_dev;
+  const int32_t* idx;  // dual: outlier channels (ascending)
+  int n_out;
+  int p1;              // outlier partition length (multiple of 64, <= 128)
+  const float* gsrc;   // MODE_GLOBAL: absmax bit patterns [P]; MODE_STATIC: scales [P]
+  float scale_mul;     // exact factor folded into the stored scale (1/128 after rotation)
+  void* codes;         // int8 [rows x kp] or packed uint8 [rows x kp/2]
+  float* scales;       // MODE_ROW: [rows] or [rows x 2]; MAXONLY: absmax target [P]
+};
+
+__device__ __forceinline__ float qmax_f(const RowArgs& a) {
+  int b = a.bits_dev ? *a.bits_dev : a.qbits;
+  b = (b == 4 || b == 6) ? b : 8;
+  return (float)((1 << (b - 1)) - 1);
+}
+
+// r and s of a dynamic group with absolute maximum amax (a = 0 or an overflowing
+// reciprocal give r = s = 0, so every code is 0).
+__device__ __forceinline__ void dyn_scale(float amax, float qf, float& r, float& s) {
+  r = qf / amax;
+  s = amax / qf;
+  if (!(amax > 0.0f) || __builtin_isinf(r)) {
+    r = 0.0f;
+    s = 0.0f;
+  }
+}
+
+__device__ __forceinline__ void static_scale(float sgiven, float& r, float& s) {
+  s = sgiven;
+  r = 1.0f / sgiven;
+  if (!(sgiven != 0.0f) || __builtin_isinf(r)) r = 0.0f;
+}
+
+template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
+__global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
+  __shared__ float s_red[8][2];
+  __shared__ unsigned s_mask[DUAL ? MAX_MASK_WORDS : 1];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int rpb = nwaves / a.W;  // rows per block
+  const int rib = wave / a.W;
+  const int wr = wave - rib * a.W;
+  const int slot = HAD ? ((lane & ~7) | perm8(lane & 7)) : lane;
+  const float sigma = HAD ? had_sigma(perm8(lane & 7)) : 1.0f;
+  const float qf = qmax_f(a);
+
+  if constexpr (DUAL) {
+    const int words = (a.k + 31) >> 5;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) s_mask[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.n_out; i += blockDim.x) {
+      const int c = a.idx[i];
+      atomicOr(&s_mask[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+  }
+
+  // Scales common to the whole tensor.
+  float r_g[2] = {0.0f, 0.0f}, s_g[2] = {0.0f, 0.0f};
+  if constexpr (MODE == MODE_GLOBAL && !MAXONLY) {
+    for (int p = 0; p < (DUAL ? 2 : 1); ++p) dyn_scale(a.gsrc[p], qf, r_g[p], s_g[p]);
+  } else if constexpr (MODE == MODE_STATIC && !MAXONLY) {
+    for (int p = 0; p < (DUAL ? 2 : 1); ++p) static_scale(a.gsrc[p], r_g[p], s_g[p]);
+  }
+
+  float run_max[2] = {0.0f, 0.0f};  // MAXONLY running maxima
+
+  for (int64_t rowbase = (int64_t)blockIdx.x * rpb; rowbase < a.rows; rowbase += (int64_t)gridDim.x * rpb) {
+    const int64_t row = rowbase + rib;
+    const bool row_ok = row < a.rows;
+    const char* xrow = reinterpret_cast<const char*>(a.x) + (row_ok ? row : 0) * a.ldx * (DT == DT_F32 ? 4 : 2);
+
+    float v[NPMAX][16];
+    float lmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPMAX; ++j) {
+      const int e = (wr + a.W * j) * 1024 + 16 * slot;
+      const bool act = j < a.np && row_ok && e < a.k;
+      if (act) {
+        load16<DT>(xrow + (int64_t)e * (DT == DT_F32 ? 4 : 2), v[j]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) v[j][t] = 0.0f;
+      }
+      if constexpr (HAD) {
+        if (j < a.np) fwht128(v[j], perm8(lane & 7));
+      }
+      if constexpr (DUAL) {
+        if (act) {
+          const unsigned bits16 = (s_mask[e >> 5] >> (e & 31)) & 0xFFFFu;
+          if (bits16) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+              if ((bits16 >> t) & 1u) v[j][t] = 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) lmax = fmaxf(lmax, fabsf(v[j][t]));
+    }
+
+    // Outlier partition: gathered by wave 0 of the row, at most 128 values.
+    float ov[2] = {0.0f, 0.0f};
+    float omax = 0.0f;
+    if constexpr (DUAL) {
+      if (wr == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int jj = lane + 64 * i;
+          if (row_ok && jj < a.n_out) ov[i] = load1<DT>(xrow, a.idx[jj]);
+          omax = fmaxf(omax, fabsf(ov[i]));
+        }
+        omax = wave_max(omax);
+      }
+    }
+
+    float amax = wave_max(lmax);
+    if (a.W > 1) {
+      if (lane == 0) s_red[wave][0] = amax;
+      __syncthreads();
+      float m = 0.0f;
+      for (int w = 0; w < a.W; ++w) m = fmaxf(m, s_red[rib * a.W + w][0]);
+      amax = m;
+      __syncthreads();
+    }
+
+    if constexpr (MAXONLY) {
+      if (row_ok) {
+        run_max[0] = fmaxf(run_max[0], amax);
+        run_max[1] = fmaxf(run_max[1], omax);
+      }
+      continue;
+    }
+
+    float r0, s0, r1 = 0.0f, s1 = 0.0f;
+    if constexpr (MODE == MODE_ROW) {
+      dyn_scale(amax, qf, r0, s0);
+      if constexpr (DUAL) dyn_scale(omax, qf, r1, s1);
+    } else {
+      r0 = r_g[0];
+      s0 = s_g[0];
+      r1 = r_g[1];
+      s1 = s_g[1];
+    }
+    const float rr = r0 * sigma;  // exact: sigma = +-1
+
+    if (row_ok) {
+#pragma unroll
+      for (int j = 0; j < NPMAX; ++j) {
+        const int e = (wr + a.W * j) * 1024 + 16 * slot;
+        if (j < a.np && e < a.k) {
+          unsigned u[16];
+#pragma unroll
+          for (int t = 0; t < 16; ++t) u[t] = qbyte(v[j][t], rr, qf);
+          if constexpr (OUT4) {
+            u2v w;
+            w.x = pack8_nibbles(u);
+            w.y = pack8_nibbles(u + 8);
+            *reinterpret_cast<u2v*>(reinterpret_cast<uint8_t*>(a.codes) + row * (a.kp / 2) + e / 2) = w;
+          } else {
+            u4v w;
+            w.x = pack4_lo(u[0], u[1], u[2], u[3]);
+            w.y = pack4_lo(u[4], u[5], u[6], u[7]);
+            w.z = pack4_lo(u[8], u[9], u[10], u[11]);
+            w.w = pack4_lo(u[12], u[13], u[14], u[15]);
+            *reinterpret_cast<u4v*>(reinterpret_cast<int8_t*>(a.codes) + row * a.kp + e) = w;
+          }
+        }
+      }
+      if constexpr (DUAL) {
+        if (wr == 0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int jj = lane + 64 * i;
+            const unsigned c = qbyte(ov[i], r1, qf) & 0xFFu;
+            if constexpr (OUT4) {
+              const unsigned nb = __shfl_down(c, 1, 64);
+              if (jj < a.p1 && (jj & 1) == 0)
+                reinterpret_cast<uint8_t*>(a.codes)[row * (a.kp / 2) + (a.k + jj) / 2] =
+                    (uint8_t)((c & 0xFu) | ((nb & 0xFu) << 4));
+            } else {
+              if (jj < a.p1) reinterpret_cast<int8_t*>(a.codes)[row * a.kp + a.k + jj] = (int8_t)c;
+            }
+          }
+        }
+      }
+      if constexpr (MODE == MODE_ROW) {
+        if (wr == 0 && lane == 0) {
+          if constexpr (DUAL) {
+            a.scales[2 * row] = s0 * a.scale_mul;
+            a.scales[2 * row + 1] = s1 * a.scale_mul;
+          } else {
+            a.scales[row] = s0 * a.scale_mul;
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (MAXONLY) {
+    // Block maximum, then one atomic per block and partition (non-negative floats
+    // order like their bit patterns, so an unsigned max is the float max).
+    float m0 = wave_max(run_max[0]);
+    float m1 = run_max[1];  // already a wave max (lanes agree)
+    if (lane == 0) {
+      s_red[wave][0] = m0;
+      s_red[wave][1] = m1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float b0 = 0.0f, b1 = 0.0f;
+      for (int w = 0; w < nwaves; ++w) {
+        b0 = fmaxf(b0, s_red[w][0]);
+        b1 = fmaxf(b1, s_red[w][1]);
+      }
+      atomicMax(reinterpret_cast<unsigned*>(a.scales), f_bits(b0));
+      if constexpr (DUAL) atomicMax(reinterpret_cast<unsigned*>(a.scales) + 1, f_bits(b1));
+    }
+  }
+}
+
+__global__ void k_fill_u32(unsigned* p, int n, unsigned v) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Per-tensor scales after the codes: dynamic s = fl32(amax / Q), static s = given.
+__global__ void k_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
+                                  const int32_t* bits_dev) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int b = bits_dev ? *bits_dev : qbits;
+  b = (b == 4 || b == 6) ? b : 8;
+  const float qf = (float)((1 << (b - 1)) - 1);
+  for (int p = 0; p < parts; ++p) {
+    float r, s;
+    if (static_src) {
+      static_scale(static_src[p], r, s);
+    } else {
+      dyn_scale(scales[p], qf, r, s);
+    }
+    scales[p] = s;
+  }
+}
+
+template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
+static hipError_t launch_row(const RowArgs& a, int grid, int block, hipStream_t st) {
+  hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY>), dim3(grid), dim3(block), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, bool HAD, bool DUAL>
+static hipError_t dispatch_mode(const RowArgs& a, int mode, bool out4, bool maxonly, int grid, int block,
+                                hipStream_t st) {
+  if (maxonly) return launch_row<DT, HAD, DUAL, MODE_ROW, false, true>(a, grid, block, st);
+  if (out4) return launch_row<DT, HAD, DUAL, MODE_ROW, true, false>(a, grid, block, st);
+  switch (mode) {
+    case MODE_ROW: return launch_row<DT, HAD, DUAL, MODE_ROW, false, false>(a, grid, block, st);
+    case MODE_GLOBAL: return launch_row<DT, HAD, DUAL, MODE_GLOBAL, false, false>(a, grid, block, st);
+    default: return launch_row<DT, HAD, DUAL, MODE_STATIC, false, false>(a, grid, block, st);
+  }
+}
+
+template <int DT>
+static hipError_t dispatch_dt(const RowArgs& a, bool had, bool dual, int mode, bool out4, bool maxonly, int grid,
+                              int block, hipStream_t st) {
+  if (had) return dispatch_mode<DT, true, false>(a, mode, out4, maxonly, grid, block, st);
+  if (dual) return dispatch_mode<DT, false, true>(a, mode, out4, maxonly, grid, block, st);
+  return dispatch_mode<DT, false, false>(a, mode, out4, maxonly, grid, block, st);
+}
+
+}  // namespace vqk
+
+namespace vq_internal {
+
+using namespace vqk;
+
+static void row_geometry(int k, int& W, int& np, int& block) {
+  const int passes = (k + 1023) / 1024;
+  W = passes <= 4 ? 1 : passes <= 8 ? 2 : passes <= 16 ? 4 : 8;
+  np = (passes + W - 1) / W;
+  block = W == 8 ? 512 : 256;
+}
+
+int row_quant_max_k() { return 8 * NPMAX * 1024; }
+
+static RowArgs make_args(const RowQuantParams& p) {
+  RowArgs a{};
+  a.x = p.x;
+  a.ldx = p.ldx;
+  a.rows = p.rows;
+  a.k = (int)p.k;
+  a.kp = (int)p.kp;
+  a.qbits = p.bits;
+  a.bits_dev = p.bits_dev;
+  a.idx = p.idx;
+  a.n_out = p.n_out;
+  a.p1 = p.p1;
+  a.gsrc = p.gsrc;
+  a.scale_mul = p.scale_mul;
+  a.codes = p.codes;
+  a.scales = p.scales;
+  return a;
+}
+
+hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st) {
+  RowArgs a = make_args(p);
+  int W, np, block;
+  row_geometry(a.k, W, np, block);
+  a.W = W;
+  a.np = np;
+  const int rpb = (block / 64) / W;
+  int64_t blocks = (p.rows + rpb - 1) / rpb;
+  if (p.maxonly && blocks > 2048) blocks = 2048;
+  if (blocks > (1 << 30)) blocks = 1 << 30;
+  const int grid = (int)blocks;
+  const int mode = p.mode;
+  switch (p.dtype) {
+    case DT_F16: return dispatch_dt<DT_F16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, grid, block, st);
+    case DT_BF16: return dispatch_dt<DT_BF16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, grid, block, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_u32, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
+                                  const int32_t* bits_dev, hipStream_t st) {
+  hipLaunchKernelGGL(k_tensor_finalize, dim3(1), dim3(64), 0, st, scales, static_src, parts, qbits, bits_dev);
+  return hipGetLastError();
+}
+
+}  // namespace vq_internal

@@ -1,0 +1,278 @@
+// C ABI of the quantized linear layer: argument validation, launch selection and
+// error mapping.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/vq.h"
+#include "vq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+vq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return VQ_OK;
+  g_last_hip = (int)e;
+  return VQ_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(vq_dtype dt) { return dt == VQ_F32 ? 4 : 2; }
+
+bool is_16bit(vq_dtype dt) { return dt == VQ_F16 || dt == VQ_BF16; }
+
+bool valid_dt(vq_dtype dt) { return dt == VQ_F16 || dt == VQ_BF16 || dt == VQ_F32; }
+
+int64_t part_len(int32_t n_out) { return n_out > 0 ? ((int64_t)n_out + VQ_K_ALIGN - 1) / VQ_K_ALIGN * VQ_K_ALIGN : 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+// Shared checks of the row-quantization entry points.
+vq_status check_rows(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, const int32_t* idx,
+                     int32_t n_out, int had_block, const void* codes, const float* scales) {
+  if (!x || !codes || !scales) return VQ_ERR_INVALID_ARG;
+  if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
+  if (rows < 1 || k < 1 || rows >= kMaxDim || k >= kMaxDim || ldx < k) return VQ_ERR_INVALID_ARG;
+  if (n_out < 0 || (n_out > 0 && !idx)) return VQ_ERR_INVALID_ARG;
+  if (had_block != 0 && had_block != VQ_HAD_BLOCK) return VQ_ERR_UNSUPPORTED;
+  if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
+  if (had_block && k % VQ_HAD_BLOCK) return VQ_ERR_SHAPE;
+  if (had_block && n_out > 0) return VQ_ERR_UNSUPPORTED;
+  if (n_out > VQ_MAX_OUTLIERS || n_out >= k) return VQ_ERR_UNSUPPORTED;
+  if (k > vq_internal::row_quant_max_k()) return VQ_ERR_UNSUPPORTED;
+  if (!aligned16(x) || ldx % 8 || !aligned16(codes)) return VQ_ERR_SHAPE;
+  return VQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t vq_outlier_part_len(int32_t n_out) { return part_len(n_out); }
+
+int64_t vq_packed_k(int64_t k, int32_t n_out) { return k + part_len(n_out); }
+
+const char* vq_status_string(vq_status s) {
+  switch (s) {
+    case VQ_OK: return "ok";
+    case VQ_ERR_INVALID_ARG: return "invalid argument";
+    case VQ_ERR_SHAPE: return "shape, stride or alignment not allowed by the layout";
+    case VQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case VQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int vq_last_hip_error(void) { return g_last_hip; }
+
+const char* vq_version(void) { return "vq 0.1 gfx950"; }
+
+// ------------------------------------------------------------------ detection
+
+int64_t vq_detect_workspace_elems(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1) return 0;
+  return ((int64_t)vq_internal::detect_row_chunks(rows) + 1) * cols;
+}
+
+vq_status vq_detect_outliers(const void* x, vq_dtype dt, int64_t rows, int64_t cols, int64_t ldx, double tau,
+                             double alpha, double kfac, double* ws_dev, double* norms_host, uint8_t* mask_host,
+                             int32_t* idx_host, int32_t* n_out, hipStream_t stream) {
+  if (!x || !ws_dev || !mask_host || !idx_host || !n_out) return VQ_ERR_INVALID_ARG;
+  if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1 || ldx < cols || rows >= kMaxDim || cols >= kMaxDim) return VQ_ERR_INVALID_ARG;
+  if (!std::isfinite(tau) || !std::isfinite(alpha) || !std::isfinite(kfac)) return VQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || ldx % 8) return VQ_ERR_SHAPE;
+
+  hipError_t e = vq_internal::launch_colsumsq(x, (int)dt, rows, cols, ldx, ws_dev, stream);
+  if (e != hipSuccess) return hip_status(e);
+  std::vector<double> v((size_t)cols);
+  const int chunks = vq_internal::detect_row_chunks(rows);
+  e = hipMemcpyAsync(v.data(), ws_dev + (int64_t)chunks * cols, sizeof(double) * (size_t)cols,
+                     hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e);
+
+  for (auto& s : v) s = std::sqrt(s);
+  auto median = [](std::vector<double> a) {
+    const size_t n = a.size();
+    std::sort(a.begin(), a.end());
+    return n % 2 ? a[n / 2] : 0.5 * (a[n / 2 - 1] + a[n / 2]);
+  };
+  const double med = median(v);
+  std::vector<double> dev(v.size());
+  for (size_t i = 0; i < v.size(); ++i) dev[i] = std::fabs(v[i] - med);
+  const double mad = median(dev);
+  int32_t cnt = 0;
+  for (int64_t i = 0; i < cols; ++i) {
+    double z;
+    if (mad == 0.0)
+      z = v[(size_t)i] > med ? INFINITY : 0.0;
+    else
+      z = kfac * (v[(size_t)i] - med) / mad;
+    const bool out = z > tau && v[(size_t)i] > alpha * med;
+    mask_host[i] = out ? 1 : 0;
+    if (out) idx_host[cnt++] = (int32_t)i;
+  }
+  int32_t j = cnt;
+  for (int64_t i = 0; i < cols; ++i)
+    if (!mask_host[i]) idx_host[j++] = (int32_t)i;
+  *n_out = cnt;
+  if (norms_host) std::memcpy(norms_host, v.data(), sizeof(double) * (size_t)cols);
+  return VQ_OK;
+}
+
+// ------------------------------------------------------------------ weights
+
+vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int64_t ldw, int bits,
+                          const int32_t* idx_dev, int32_t n_out, int had_block, void* codes, float* scales,
+                          hipStream_t stream) {
+  vq_status s = check_rows(w, dt, n, k, ldw, idx_dev, n_out, had_block, codes, scales);
+  if (s != VQ_OK) return s;
+  if (bits != 4 && bits != 8) return VQ_ERR_UNSUPPORTED;
+  vq_internal::RowQuantParams p{};
+  p.x = w;
+  p.dtype = (int)dt;
+  p.ldx = ldw;
+  p.rows = n;
+  p.k = k;
+  p.kp = k + part_len(n_out);
+  p.bits = bits;
+  p.idx = idx_dev;
+  p.n_out = n_out;
+  p.p1 = (int)part_len(n_out);
+  p.scale_mul = had_block ? 1.0f / (float)had_block : 1.0f;
+  p.codes = codes;
+  p.scales = scales;
+  p.mode = 0;
+  p.had = had_block != 0;
+  p.out4 = bits == 4;
+  return hip_status(vq_internal::launch_row_quant(p, stream));
+}
+
+// ------------------------------------------------------------------ activations
+
+vq_status vq_quant_act(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t ldx, int bits,
+                       const int32_t* bits_dev, vq_gran gran, int had_block, const int32_t* idx_dev, int32_t n_out,
+                       const float* static_scale_dev, int8_t* codes, float* scales, hipStream_t stream) {
+  vq_status s = check_rows(x, dt, m, k, ldx, idx_dev, n_out, had_block, codes, scales);
+  if (s != VQ_OK) return s;
+  if (bits != 4 && bits != 6 && bits != 8) return VQ_ERR_UNSUPPORTED;
+  if (gran != VQ_PER_TENSOR && gran != VQ_PER_TOKEN && gran != VQ_PER_TENSOR_STATIC) return VQ_ERR_INVALID_ARG;
+  if (gran == VQ_PER_TENSOR_STATIC && !static_scale_dev) return VQ_ERR_INVALID_ARG;
+
+  const int parts = n_out > 0 ? 2 : 1;
+  vq_internal::RowQuantParams p{};
+  p.x = x;
+  p.dtype = (int)dt;
+  p.ldx = ldx;
+  p.rows = m;
+  p.k = k;
+  p.kp = k + part_len(n_out);
+  p.bits = bits;
+  p.bits_dev = bits_dev;
+  p.idx = idx_dev;
+  p.n_out = n_out;
+  p.p1 = (int)part_len(n_out);
+  p.scale_mul = 1.0f;
+  p.codes = codes;
+  p.scales = scales;
+  p.had = had_block != 0;
+  p.out4 = false;
+
+  hipError_t e = hipSuccess;
+  if (gran == VQ_PER_TOKEN) {
+    p.mode = 0;
+    return hip_status(vq_internal::launch_row_quant(p, stream));
+  }
+  if (gran == VQ_PER_TENSOR) {
+    e = vq_internal::launch_fill_u32(reinterpret_cast<unsigned*>(scales), parts, 0u, stream);
+    if (e != hipSuccess) return hip_status(e);
+    vq_internal::RowQuantParams q = p;
+    q.maxonly = true;
+    e = vq_internal::launch_row_quant(q, stream);
+    if (e != hipSuccess) return hip_status(e);
+    p.mode = 1;
+    p.gsrc = scales;
+    e = vq_internal::launch_row_quant(p, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(vq_internal::launch_tensor_finalize(scales, nullptr, parts, bits, bits_dev, stream));
+  }
+  p.mode = 2;
+  p.gsrc = static_scale_dev;
+  e = vq_internal::launch_row_quant(p, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(vq_internal::launch_tensor_finalize(scales, static_scale_dev, parts, bits, bits_dev, stream));
+}
+
+// ------------------------------------------------------------------ Hadamard
+
+vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y, vq_dtype out_dt, int64_t ldy,
+                            int64_t rows, int64_t cols, int block, int normalize, hipStream_t stream) {
+  if (!x || !y) return VQ_ERR_INVALID_ARG;
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1 || ldx < cols || ldy < cols || rows >= kMaxDim || cols >= kMaxDim)
+    return VQ_ERR_INVALID_ARG;
+  if (normalize != 0 && normalize != 1) return VQ_ERR_INVALID_ARG;
+  if (block != VQ_HAD_BLOCK) return VQ_ERR_UNSUPPORTED;
+  if (cols % VQ_HAD_BLOCK) return VQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y) || (ldx * elem_size(in_dt)) % 16 || (ldy * elem_size(out_dt)) % 16)
+    return VQ_ERR_SHAPE;
+  if (x == y) return VQ_ERR_INVALID_ARG;
+  return hip_status(vq_internal::launch_hadamard(x, (int)in_dt, ldx, y, (int)out_dt, ldy, rows, cols, normalize,
+                                                 stream));
+}
+
+// ------------------------------------------------------------------ GEMM
+
+vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits,
+                           const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0, void* y, vq_dtype out_dt,
+                           int64_t ldy, int32_t* acc_debug, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !y) return VQ_ERR_INVALID_ARG;
+  if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
+  if (sa_per_token != 0 && sa_per_token != 1) return VQ_ERR_INVALID_ARG;
+  if (m < 1 || n < 1 || kp < 1 || k0 < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || kp >= kMaxDim)
+    return VQ_ERR_INVALID_ARG;
+  if (b_bits != 4 && b_bits != 8) return VQ_ERR_UNSUPPORTED;
+  if (kp % VQ_K_ALIGN || k0 % VQ_K_ALIGN || k0 > kp || kp - k0 > VQ_MAX_OUTLIERS) return VQ_ERR_SHAPE;
+  if (!aligned16(a) || !aligned16(b)) return VQ_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
+  vq_internal::GemmParams p{};
+  p.a = a;
+  p.sa = sa;
+  p.sa_per_token = sa_per_token;
+  p.b = b;
+  p.b_bits = b_bits;
+  p.sb = sb;
+  p.m = m;
+  p.n = n;
+  p.kp = kp;
+  p.k0 = k0;
+  p.y = y;
+  p.out_dt = (int)out_dt;
+  p.ldy = ldy;
+  p.acc_debug = acc_debug;
+  return hip_status(vq_internal::launch_qgemm(p, stream));
+}
+
+// ------------------------------------------------------------------ routing
+
+int64_t vq_route_workspace_elems(int64_t n) { return n < 1 ? 0 : 2 * (int64_t)vq_internal::route_blocks(); }
+
+vq_status vq_route_rel_l1(const void* x, const void* y, vq_dtype dt, int64_t n, double threshold, int bits_hi,
+                          int bits_lo, double* ws_dev, double* gamma_dev, int32_t* bits_dev, hipStream_t stream) {
+  if (!x || !y || !ws_dev || !bits_dev) return VQ_ERR_INVALID_ARG;
+  if (!valid_dt(dt) || n < 1) return VQ_ERR_INVALID_ARG;
+  auto ok_bits = [](int b) { return b == 4 || b == 6 || b == 8; };
+  if (!ok_bits(bits_hi) || !ok_bits(bits_lo) || !std::isfinite(threshold)) return VQ_ERR_INVALID_ARG;
+  return hip_status(vq_internal::launch_route(x, y, (int)dt, n, threshold, bits_hi, bits_lo, ws_dev, gamma_dev,
+                                              bits_dev, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Launch interface between the C-ABI layer (vq_api.cpp) and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vq_internal {
+
+struct RowQuantParams {
+  const void* x;
+  int dtype;  // 0 f16, 1 bf16
+  int64_t ldx;
+  int64_t rows;
+  int64_t k;
+  int64_t kp;
+  int bits;
+  const int32_t* bits_dev;
+  const int32_t* idx;
+  int n_out;
+  int p1;
+  const float* gsrc;
+  float scale_mul;
+  void* codes;
+  float* scales;
+  int mode;  // 0 per row dynamic, 1 global dynamic (absmax in gsrc), 2 static (scales in gsrc)
+  bool had;
+  bool out4;
+  bool maxonly;
+};
+
+int row_quant_max_k();
+hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st);
+hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st);
+hipError_t launch_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
+                                  const int32_t* bits_dev, hipStream_t st);
+
+hipError_t launch_hadamard(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, int64_t ldy,
+                           int64_t rows, int64_t cols, int normalize, hipStream_t st);
+
+struct GemmParams {
+  const int8_t* a;
+  const float* sa;
+  int sa_per_token;
+  const void* b;
+  int b_bits;
+  const float* sb;
+  int64_t m, n, kp, k0;
+  void* y;
+  int out_dt;
+  int64_t ldy;
+  int32_t* acc_debug;
+};
+hipError_t launch_qgemm(const GemmParams& g, hipStream_t st);
+
+int detect_row_chunks(int64_t rows);
+hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, double* ws,
+                           hipStream_t st);
+
+int route_blocks();
+hipError_t launch_route(const void* x, const void* y, int dt, int64_t n, double threshold, int hi, int lo,
+                        double* ws, double* gamma, int32_t* bits, hipStream_t st);
+
+}  // namespace vq_internal

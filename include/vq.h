@@ -1,0 +1,204 @@
+/*
+ * vq.h - C ABI of the MI355X (gfx950) quantized linear layer for video diffusion
+ * transformers: online activation quantization, block Hadamard rotation, dual-scale
+ * outlier channels, packed INT8/INT4 weights, integer MFMA GEMM with a fused
+ * dequantization epilogue, and per-layer INT8-vs-4-bit routing.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers marked "device" are device memory owned by the caller; the
+ *    library never allocates, frees or keeps them past the call.  Pointers marked
+ *    "host" are ordinary host memory owned by the caller.
+ *  - Tensors are row-major; K (input channels) is the contiguous dimension.  Strides
+ *    (ld*) are in elements and must be at least the row length.
+ *  - Every call enqueues its work asynchronously on `stream` (0 = the null stream)
+ *    and returns without waiting, except vq_detect_outliers, which waits on `stream`
+ *    because its result is host memory.
+ *  - Arguments are validated before anything is enqueued; on an error nothing is
+ *    enqueued and outputs are untouched.  Faults inside kernels are reported by the
+ *    caller's next synchronization, as for any HIP kernel.
+ *  - Element types: VQ_F16 = IEEE binary16, VQ_BF16 = bfloat16, VQ_F32 = binary32.
+ *  - Quantized codes: Q = 2^(bits-1) - 1 (127, 31, 7); code = clamp(rne(x * r), -Q, Q)
+ *    with r = fl32(Q / a) for the group absolute maximum a and scale s = fl32(a / Q);
+ *    a group whose maximum is 0 gets s = 0 and zero codes.  Activation codes of every
+ *    width are stored one per int8.  4-bit weight codes are packed two per byte, low
+ *    nibble = even k.
+ *  - Dual-scale layout: with n_out > 0 outlier input channels the K axis of both
+ *    operands has two partitions: partition 0 = the K channels in place with the
+ *    outlier positions holding code 0, partition 1 = the outlier channels gathered
+ *    in ascending channel order, zero-padded to vq_outlier_part_len(n_out).  Codes are
+ *    [rows x vq_packed_k(K, n_out)] and every group has two scales (row-major [rows x 2]).
+ *
+ * Sources: Q-ARVD (aitrends.kr article, "Q-ARVD: quantization of autoregressive video
+ * diffusion models"), sections Methodology and Technical details; 6Bit-Diffusion
+ * (gist.science summary of arXiv 2603.18742), Key Insights 1 and Methodology B.1 (DMPQ);
+ * S2Q-VDiT (gist.science summary of arXiv 2508.04016), the W4A6 setting.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vq_status {
+  VQ_OK = 0,
+  VQ_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, non-positive size, bad stride */
+  VQ_ERR_SHAPE = 2,       /* sizes that the layout forbids (K not a multiple of 64, ...) */
+  VQ_ERR_UNSUPPORTED = 3, /* a valid but unimplemented combination */
+  VQ_ERR_HIP = 4          /* a HIP runtime call failed; see vq_last_hip_error() */
+} vq_status;
+
+typedef enum vq_dtype { VQ_F16 = 0, VQ_BF16 = 1, VQ_F32 = 2 } vq_dtype;
+
+typedef enum vq_gran {
+  VQ_PER_TENSOR = 0,       /* one dynamic scale per partition over the whole tensor */
+  VQ_PER_TOKEN = 1,        /* one dynamic scale per row (token) and partition */
+  VQ_PER_TENSOR_STATIC = 2 /* caller-given scale per partition: r = fl32(1 / s) */
+} vq_gran;
+
+#define VQ_K_ALIGN 64        /* K and each K partition are multiples of this */
+#define VQ_HAD_BLOCK 128     /* the only Hadamard block size */
+#define VQ_MAX_OUTLIERS 128  /* largest n_out of the dual-scale path */
+
+/* Length of the outlier partition: n_out rounded up to a multiple of 64 (0 for 0). */
+int64_t vq_outlier_part_len(int32_t n_out);
+
+/* Total code length of a K-channel operand with n_out outlier channels. */
+int64_t vq_packed_k(int64_t k, int32_t n_out);
+
+/*
+ * Outlier input-channel detection (Q-ARVD, Methodology: outlier-aware adaptive
+ * dual-scale quantization).  For each column k of x [rows x cols]:
+ *   v_k = sqrt(sum_r x[r,k]^2)                       (float64 accumulation)
+ *   M_k = kfac * (v_k - median(v)) / MAD,  MAD = median(|v - median(v)|)
+ *   outlier  <=>  M_k > tau  and  v_k > alpha * median(v)     (both strict)
+ * An even count's median is the mean of the two middle values; MAD = 0 makes
+ * M_k = +inf where v_k > median, else 0.  kfac = 1 is the page's formula (0.6745 the
+ * textbook variant); typical tau = 3.5, alpha = 2.
+ *   x          device, dt in {F16, BF16}, [rows x cols], stride ldx
+ *   ws_dev     device scratch of vq_detect_workspace_elems(rows, cols) doubles
+ *   norms_host host [cols] or NULL: receives v
+ *   mask_host  host [cols]: 1 for an outlier channel, else 0
+ *   idx_host   host [cols]: first *n_out entries = outlier channels, ascending
+ *   n_out      host: number of outlier channels
+ * Waits on `stream` (the sums are copied to the host and the median is taken there).
+ * Errors: INVALID_ARG for null pointers / rows or cols < 1 / ldx < cols / bad dtype.
+ */
+int64_t vq_detect_workspace_elems(int64_t rows, int64_t cols);
+vq_status vq_detect_outliers(const void* x, vq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                             double tau, double alpha, double kfac, double* ws_dev,
+                             double* norms_host, uint8_t* mask_host, int32_t* idx_host,
+                             int32_t* n_out, hipStream_t stream);
+
+/*
+ * Offline per-output-channel weight quantization (Q-ARVD, Methodology and Technical
+ * details: per-channel weights, dual scale; 6Bit-Diffusion, Methodology B.1: weights
+ * quantized offline to 4 bits and activations rotated by an online block Hadamard).
+ *   w          device, dt in {F16, BF16}, [n x k], stride ldw; k % 64 == 0
+ *   bits       8 (codes int8 [n x kp]) or 4 (codes uint8 [n x kp/2], two per byte)
+ *   idx_dev    device int32 [n_out] outlier channels (ascending, < k), or NULL with n_out = 0
+ *   had_block  0, or 128: each row is first rotated by the unnormalized 128-point
+ *              Sylvester Hadamard butterflies; the scale then carries the exact 1/128
+ *              so that products with rotated activations equal the normalized rotation.
+ *              Not combined with n_out > 0.
+ *   codes      device, kp = vq_packed_k(k, n_out)
+ *   scales     device float [n] (n_out = 0) or [n x 2] (partition 0, partition 1)
+ * Errors: INVALID_ARG, SHAPE (k % 64, k % 128 with had_block), UNSUPPORTED (bits,
+ * had_block other than 0/128, had_block with n_out, n_out > VQ_MAX_OUTLIERS or >= k).
+ */
+vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int64_t ldw, int bits,
+                          const int32_t* idx_dev, int32_t n_out, int had_block, void* codes,
+                          float* scales, hipStream_t stream);
+
+/*
+ * Online activation quantization (Q-ARVD, Technical details: activation-quantization
+ * kernel, per-tensor activations; per-token rows; 6Bit-Diffusion, Methodology B.1:
+ * INT8 or 4-bit activations per block, online block Hadamard; S2Q-VDiT: 6-bit).
+ *   x          device, dt in {F16, BF16}, [m x k], stride ldx; k % 64 == 0
+ *   bits       4, 6 or 8
+ *   bits_dev   device int32 or NULL: when given, the kernels read the bit width from it
+ *              at run time (4, 6 or 8; any other value acts as 8) -- the DMPQ route
+ *              decided on the device by vq_route_rel_l1 without a host round trip
+ *   gran       VQ_PER_TOKEN, VQ_PER_TENSOR (dynamic) or VQ_PER_TENSOR_STATIC
+ *   had_block  0 or 128 (unnormalized rotation before quantizing; not with n_out > 0)
+ *   idx_dev    device int32 [n_out] outlier channels (ascending), or NULL with n_out = 0
+ *   static_scale_dev  device float [1 or 2] (static granularity only), else NULL
+ *   codes      device int8 [m x kp], row stride kp = vq_packed_k(k, n_out)
+ *   scales     device float: per token [m] or [m x 2]; per tensor [1] or [2]
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED as for vq_pack_weights.
+ */
+vq_status vq_quant_act(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t ldx, int bits,
+                       const int32_t* bits_dev, vq_gran gran, int had_block, const int32_t* idx_dev,
+                       int32_t n_out, const float* static_scale_dev, int8_t* codes, float* scales,
+                       hipStream_t stream);
+
+/*
+ * Standalone block Hadamard rotation (6Bit-Diffusion, Methodology B.1: online block
+ * Hadamard transform).  Per row and per contiguous 128-element block, z = H x by
+ * float32 butterflies with distances h = 1, 2, ..., 64 in that order, each pair
+ * (i, i+h) becoming (z_i + z_{i+h}, z_i - z_{i+h}).  normalize = 1 returns
+ * fl32(z * fl32(1/sqrt(128))), normalize = 0 returns z; then RNE to out_dt.
+ *   x   device, in_dt in {F16, BF16, F32}, [rows x cols], stride ldx
+ *   y   device, out_dt in {F16, BF16, F32}, [rows x cols], stride ldy; may not alias x
+ * Errors: INVALID_ARG, SHAPE (cols % 128), UNSUPPORTED (block != 128).
+ */
+vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y, vq_dtype out_dt,
+                            int64_t ldy, int64_t rows, int64_t cols, int block, int normalize,
+                            hipStream_t stream);
+
+/*
+ * Integer GEMM with fused dequantization (Q-ARVD, Technical details: GEMM and
+ * dequantization kernel; Methodology: Q_dual keeps separate scales for outlier and
+ * normal channels).  acc_P[i,j] = sum_{k in P} a[i,k] * b[j,k] exactly in int32 over
+ * partition 0 = [0, k0) and, when k0 < kp, partition 1 = [k0, kp).  Then, in float32
+ * without fused multiply-add: y_P = fl32(fl32(acc_P) * fl32(sa_P[i] * sb_P[j])),
+ * y = y_0 (+ y_1 when dual, added in float32), RNE to out_dt.
+ *   a        device int8 [m x kp] (row stride kp)
+ *   sa       device float: sa_per_token ? [m] or [m x 2] : [1] or [2]
+ *   b        device: b_bits 8 -> int8 [n x kp]; b_bits 4 -> uint8 [n x kp/2] packed nibbles
+ *   sb       device float [n] or [n x 2]
+ *   kp, k0   kp % 64 == 0, k0 % 64 == 0, 0 < k0 <= kp, kp - k0 <= 128
+ *   y        device out_dt in {F16, BF16, F32}, [m x n], row stride ldy (element aligned;
+ *            a 16-byte aligned y with ldy % 4 == 0 takes the vector-store path)
+ *   acc_debug device int32 [P x m x n] or NULL: receives the raw accumulators
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8, out_dt).
+ */
+vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b,
+                           int b_bits, const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0,
+                           void* y, vq_dtype out_dt, int64_t ldy, int32_t* acc_debug,
+                           hipStream_t stream);
+
+/*
+ * DMPQ routing on the device (6Bit-Diffusion, Key Insights 1 and Methodology B.1):
+ * Gamma = sum|y - x| / sum|x| over n elements (float64, fixed reduction order), then
+ * bits = Gamma > threshold ? bits_hi : bits_lo (strict: a tie takes bits_lo).  x and y
+ * are the block's input and output at the previous timestep.  sum|x| = 0 gives
+ * Gamma = +inf.
+ *   x, y       device, dt in {F16, BF16, F32}, [n]
+ *   ws_dev     device scratch of vq_route_workspace_elems(n) doubles
+ *   gamma_dev  device double [1] or NULL
+ *   bits_dev   device int32 [1]: the routed bit width, ready for vq_quant_act's bits_dev
+ * Errors: INVALID_ARG (null, n < 1, bits not 4/6/8).
+ */
+int64_t vq_route_workspace_elems(int64_t n);
+vq_status vq_route_rel_l1(const void* x, const void* y, vq_dtype dt, int64_t n, double threshold,
+                          int bits_hi, int bits_lo, double* ws_dev, double* gamma_dev,
+                          int32_t* bits_dev, hipStream_t stream);
+
+/* Text of a status code (static storage). */
+const char* vq_status_string(vq_status s);
+
+/* The hipError_t of the last failed HIP call on this thread (0 if none). */
+int vq_last_hip_error(void);
+
+/* Library version string (static storage). */
+const char* vq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQ_H */

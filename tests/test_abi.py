@@ -1,0 +1,195 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/vq.h declares,
+and rejects invalid arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vq.h")
+LIB = os.path.join(ROOT, "bit_quantized_linear_vq_amd", "libvq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libvq.so not built")
+
+OK, INVALID, SHAPE, UNSUP, HIP = range(5)
+F16, BF16, F32 = 0, 1, 2
+# A fake, 256-byte aligned address: only ever passed to calls that must fail validation.
+FAKE = ctypes.c_void_p(0x10000)
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(vq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import bit_quantized_linear_vq_amd as vq
+    return vq._lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+    import bit_quantized_linear_vq_amd as vq
+    assert set(names) == set(vq.EXPORTS)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert lib.vq_status_string(s)
+    assert b"gfx950" in lib.vq_version()
+
+
+def test_layout_helpers(lib):
+    assert lib.vq_outlier_part_len(0) == 0
+    assert lib.vq_outlier_part_len(1) == 64
+    assert lib.vq_outlier_part_len(64) == 64
+    assert lib.vq_outlier_part_len(65) == 128
+    assert lib.vq_packed_k(3072, 30) == 3136
+    assert lib.vq_packed_k(1920, 0) == 1920
+    assert lib.vq_detect_workspace_elems(12288, 3072) == (256 + 1) * 3072
+    assert lib.vq_detect_workspace_elems(10, 7) == 11 * 7
+    assert lib.vq_route_workspace_elems(65536) == 1024
+    assert lib.vq_detect_workspace_elems(0, 5) == 0
+
+
+def quant(lib, **kw):
+    a = dict(x=FAKE, dt=BF16, m=64, k=1920, ldx=1920, bits=8, bits_dev=NULL, gran=1, had=0, idx=NULL,
+             n_out=0, static=NULL, codes=FAKE, scales=FAKE, stream=NULL)
+    a.update(kw)
+    return lib.vq_quant_act(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["bits"], a["bits_dev"], a["gran"],
+                            a["had"], a["idx"], a["n_out"], a["static"], a["codes"], a["scales"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=NULL), INVALID),
+    (dict(codes=NULL), INVALID),
+    (dict(scales=NULL), INVALID),
+    (dict(dt=F32), INVALID),
+    (dict(dt=7), INVALID),
+    (dict(m=0), INVALID),
+    (dict(m=-5), INVALID),
+    (dict(ldx=1000), INVALID),
+    (dict(bits=5), UNSUP),
+    (dict(bits=3), UNSUP),
+    (dict(gran=9), INVALID),
+    (dict(gran=2, static=NULL), INVALID),
+    (dict(k=1000, ldx=1000), SHAPE),
+    (dict(k=1984, ldx=1984, had=128), SHAPE),
+    (dict(had=64), UNSUP),
+    (dict(had=128, idx=FAKE, n_out=3), UNSUP),
+    (dict(idx=NULL, n_out=3), INVALID),
+    (dict(idx=FAKE, n_out=129), UNSUP),
+    (dict(n_out=-1), INVALID),
+    (dict(k=65536, ldx=65536), UNSUP),
+    (dict(x=ctypes.c_void_p(0x10008)), SHAPE),
+    (dict(ldx=1924), SHAPE),
+    (dict(codes=ctypes.c_void_p(0x10004)), SHAPE),
+])
+def test_quant_act_validation(lib, kw, want):
+    assert quant(lib, **kw) == want
+
+
+def pack(lib, **kw):
+    a = dict(w=FAKE, dt=BF16, n=64, k=3072, ldw=3072, bits=4, idx=NULL, n_out=0, had=0, codes=FAKE,
+             scales=FAKE, stream=NULL)
+    a.update(kw)
+    return lib.vq_pack_weights(a["w"], a["dt"], a["n"], a["k"], a["ldw"], a["bits"], a["idx"], a["n_out"],
+                               a["had"], a["codes"], a["scales"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(w=NULL), INVALID),
+    (dict(bits=6), UNSUP),
+    (dict(bits=2), UNSUP),
+    (dict(k=100, ldw=100), SHAPE),
+    (dict(had=128, idx=FAKE, n_out=4), UNSUP),
+    (dict(n=0), INVALID),
+    (dict(idx=FAKE, n_out=3072), UNSUP),
+])
+def test_pack_weights_validation(lib, kw, want):
+    assert pack(lib, **kw) == want
+
+
+def gemm(lib, **kw):
+    a = dict(a=FAKE, sa=FAKE, tok=1, b=FAKE, bb=8, sb=FAKE, m=100, n=64, kp=1920, k0=1920, y=FAKE, odt=BF16,
+             ldy=64, acc=NULL, stream=NULL)
+    a.update(kw)
+    return lib.vq_qgemm_dequant(a["a"], a["sa"], a["tok"], a["b"], a["bb"], a["sb"], a["m"], a["n"], a["kp"],
+                                a["k0"], a["y"], a["odt"], a["ldy"], a["acc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(a=NULL), INVALID),
+    (dict(sb=NULL), INVALID),
+    (dict(y=NULL), INVALID),
+    (dict(odt=5), INVALID),
+    (dict(tok=2), INVALID),
+    (dict(m=0), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(ldy=32), INVALID),
+    (dict(bb=6), UNSUP),
+    (dict(kp=1900, k0=1900), SHAPE),
+    (dict(k0=1900), SHAPE),
+    (dict(k0=2048), SHAPE),
+    (dict(kp=3200, k0=3008), SHAPE),  # outlier partition longer than 128
+    (dict(y=ctypes.c_void_p(0x10001)), SHAPE),
+    (dict(a=ctypes.c_void_p(0x10008)), SHAPE),
+])
+def test_qgemm_validation(lib, kw, want):
+    assert gemm(lib, **kw) == want
+
+
+def had(lib, **kw):
+    a = dict(x=FAKE, idt=BF16, ldx=256, y=ctypes.c_void_p(0x20000), odt=BF16, ldy=256, rows=4, cols=256,
+             block=128, norm=1, stream=NULL)
+    a.update(kw)
+    return lib.vq_hadamard_block(a["x"], a["idt"], a["ldx"], a["y"], a["odt"], a["ldy"], a["rows"], a["cols"],
+                                 a["block"], a["norm"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=NULL), INVALID),
+    (dict(block=64), UNSUP),
+    (dict(cols=192, ldx=192, ldy=192), SHAPE),
+    (dict(norm=2), INVALID),
+    (dict(idt=4), INVALID),
+    (dict(y=FAKE), INVALID),  # in place is not allowed
+    (dict(ldx=100), INVALID),
+    (dict(ldx=260), SHAPE),
+])
+def test_hadamard_validation(lib, kw, want):
+    assert had(lib, **kw) == want
+
+
+def test_detect_and_route_validation(lib):
+    n_out = ctypes.c_int32(0)
+    buf = (ctypes.c_uint8 * 16)()
+    idx = (ctypes.c_int32 * 16)()
+    assert lib.vq_detect_outliers(NULL, BF16, 8, 16, 16, 3.5, 2.0, 1.0, FAKE, NULL, buf, idx,
+                                  ctypes.byref(n_out), NULL) == INVALID
+    assert lib.vq_detect_outliers(FAKE, F32, 8, 16, 16, 3.5, 2.0, 1.0, FAKE, NULL, buf, idx,
+                                  ctypes.byref(n_out), NULL) == INVALID
+    assert lib.vq_detect_outliers(FAKE, BF16, 8, 16, 8, 3.5, 2.0, 1.0, FAKE, NULL, buf, idx,
+                                  ctypes.byref(n_out), NULL) == INVALID
+    assert lib.vq_detect_outliers(FAKE, BF16, 8, 16, 16, float("nan"), 2.0, 1.0, FAKE, NULL, buf, idx,
+                                  ctypes.byref(n_out), NULL) == INVALID
+    assert lib.vq_route_rel_l1(FAKE, FAKE, BF16, 0, 0.1, 8, 4, FAKE, NULL, FAKE, NULL) == INVALID
+    assert lib.vq_route_rel_l1(FAKE, FAKE, BF16, 16, 0.1, 5, 4, FAKE, NULL, FAKE, NULL) == INVALID
+    assert lib.vq_route_rel_l1(FAKE, FAKE, BF16, 16, 0.1, 8, 4, FAKE, NULL, NULL, NULL) == INVALID
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present: a valid call would really launch")
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    """With no GPU, a call that passes validation must fail cleanly in the HIP runtime."""
+    st = quant(lib)
+    assert st == HIP
+    assert lib.vq_last_hip_error() != 0
+    assert gemm(lib) == HIP

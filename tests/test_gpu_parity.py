@@ -1,0 +1,397 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer results (codes, packed nibbles, masks, outlier indices, int32 accumulators,
+routed bit widths) must match bit for bit.  Float scales are produced by the same
+float32 operations on both sides and must match bit for bit too.  Outputs are checked
+against the published gate (max relative error 2e-3 elementwise) and, because the
+epilogue is pinned to one float32 operation order, also for bitwise identity.
+
+Sizes: small cases span several 256 x 256 GEMM tiles with ragged M and N tails; the
+full workload shapes are checked on sampled rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from oracle import detect as odetect
+from oracle import fwht as ofwht
+from oracle import gemm as ogemm
+from oracle import numerics as onum
+from oracle import quantizer as oq
+from oracle import route as oroute
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def vq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_linear_vq_amd as m
+    return m
+
+
+def npb(t):
+    return gen.as_numpy_bits(t.cpu())
+
+
+def dtname(t):
+    return {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[t.dtype]
+
+
+def assert_same(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.flatnonzero(got.reshape(-1) != want.reshape(-1))
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}: {got.reshape(-1)[bad[:5]]} vs {want.reshape(-1)[bad[:5]]}"
+
+
+def out_f32(t):
+    return onum.to_f32(npb(t), dtname(t)) if t.dtype != torch.float32 else t.cpu().numpy()
+
+
+def assert_outputs(y_gpu, y_ref_store, out_dtype, what):
+    """The 2e-3 relative gate, plus bitwise identity of the stored outputs."""
+    got = out_f32(y_gpu)
+    ref = onum.to_f32(y_ref_store, out_dtype)
+    err = np.abs(got.astype(np.float64) - ref)
+    tol = 2e-3 * np.abs(ref.astype(np.float64))
+    assert np.all((err <= tol) | ((ref == 0) & (got == 0))), f"{what}: gate violated, max rel {np.max(err / np.maximum(np.abs(ref), 1e-30))}"
+    assert_same(npb(y_gpu) if out_dtype != "fp32" else y_gpu.cpu().numpy(), y_ref_store, what + " (bitwise)")
+
+
+# ------------------------------------------------------------------ activation quantization
+
+
+@pytest.mark.parametrize("bits", [8, 6, 4])
+def test_quant_per_token_c2_small(vq, bits):
+    x = gen.make_x(2, m=549)
+    codes, scales = vq.vq_quant_act(x.to(DEV), bits, "token")
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(x), "bf16", bits, "token")
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scales")
+
+
+def test_quant_per_tensor_c1_full(vq):
+    x = gen.make_x(1)
+    codes, scales = vq.vq_quant_act(x.to(DEV), 8, "tensor")
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(x), "fp16", 8, "tensor")
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scale")
+
+
+def test_quant_static_scale(vq):
+    x = gen.make_x(1)
+    s = torch.tensor([0.05], dtype=torch.float32)
+    codes, scales = vq.vq_quant_act(x.to(DEV), 8, "static", static_scale=s.to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(x), "fp16", 8, "static", static_scale=s.numpy())
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scale")
+    assert np.abs(rc).max() == 127  # the static scale clips
+
+
+@pytest.mark.parametrize("gran", ["token", "tensor"])
+def test_quant_dual_c3_small(vq, gran):
+    x = gen.make_x(3, m=300)
+    idx = gen.w_outlier_channels(3).astype(np.int32)
+    codes, scales = vq.vq_quant_act(x.to(DEV), 8, gran, idx=torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(x), "bf16", 8, gran, 0, idx)
+    assert codes.shape == (300, 3136)
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scales")
+
+
+@pytest.mark.parametrize("bits,gran", [(6, "token"), (8, "token"), (4, "tensor")])
+def test_quant_hadamard_c4_small(vq, bits, gran):
+    x = gen.make_x(4, m=40)
+    codes, scales = vq.vq_quant_act(x.to(DEV), bits, gran, had_block=128)
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(x), "bf16", bits, gran, 128)
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scales")
+
+
+@pytest.mark.parametrize("k", [64, 128, 1024, 1088, 4160, 8192, 9216, 17408, 32768])
+def test_quant_row_lengths(vq, k):
+    """Every row-length regime (waves per row 1, 2, 4, 8; partial passes)."""
+    rng = np.random.default_rng(k)
+    x = gen.to_storage(rng.standard_normal((9, k)).astype(np.float32), "bf16")
+    for had in ([0, 128] if k % 128 == 0 else [0]):
+        codes, scales = vq.vq_quant_act(x.to(DEV), 8, "token", had_block=had)
+        torch.cuda.synchronize()
+        rc, rs = oq.quant_act(npb(x), "bf16", 8, "token", had)
+        assert_same(codes.cpu().numpy(), rc, f"codes k={k} had={had}")
+        assert_same(scales.cpu().numpy(), rs, f"scales k={k} had={had}")
+
+
+def test_quant_edge_rows(vq):
+    """All-zero rows, a single row, exact ties, and fp16 input."""
+    x = np.zeros((3, 128), dtype=np.float32)
+    x[1, :5] = [1.984375, -0.5, 0.2578125, -0.0234375, 0.0078125]  # ties 16.5, -1.5, 0.5
+    x[2, :] = -2.0
+    t = gen.to_storage(x, "fp16")
+    codes, scales = vq.vq_quant_act(t.to(DEV), 8, "token")
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(t), "fp16", 8, "token")
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scales")
+    assert rc[1, :5].tolist() == [127, -32, 16, -2, 0] and rs[0] == 0
+    one = gen.make_x(2, m=1)
+    codes, scales = vq.vq_quant_act(one.to(DEV), 8, "token")
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(one), "bf16", 8, "token")
+    assert_same(codes.cpu().numpy(), rc, "codes m=1")
+
+
+def test_runtime_bits_from_device(vq):
+    x = gen.make_x(5, m=70)
+    for b in (8, 4, 6):
+        bd = torch.tensor([b], dtype=torch.int32, device=DEV)
+        codes, scales = vq.vq_quant_act(x.to(DEV), 8, "token", bits_dev=bd)
+        torch.cuda.synchronize()
+        rc, rs = oq.quant_act(npb(x), "bf16", b, "token")
+        assert_same(codes.cpu().numpy(), rc, f"codes bits={b}")
+        assert_same(scales.cpu().numpy(), rs, f"scales bits={b}")
+
+
+# ------------------------------------------------------------------ weights
+
+
+@pytest.mark.parametrize("cfg,bits,had,dual,n", [(2, 8, 0, False, 320), (1, 8, 0, False, 512),
+                                                  (3, 4, 0, True, 320), (3, 4, 0, False, 64),
+                                                  (4, 4, 128, False, 96), (5, 4, 0, False, 130)])
+def test_pack_weights(vq, cfg, bits, had, dual, n):
+    w = gen.make_w(cfg, n=n)
+    idx = gen.w_outlier_channels(cfg).astype(np.int32) if dual else None
+    codes, scales = vq.vq_pack_weights(w.to(DEV), bits, None if idx is None else torch.from_numpy(idx).to(DEV), had)
+    torch.cuda.synchronize()
+    rcodes, rpacked, rs = oq.pack_weights(npb(w), dtname(w), bits, had, idx)
+    assert_same(codes.cpu().numpy(), rpacked, "packed codes")
+    assert_same(scales.cpu().numpy(), rs, "scales")
+
+
+# ------------------------------------------------------------------ Hadamard
+
+
+@pytest.mark.parametrize("in_dt,out_dt,norm", [(torch.bfloat16, torch.bfloat16, True),
+                                               (torch.bfloat16, torch.float32, False),
+                                               (torch.float16, torch.float16, True),
+                                               (torch.float32, torch.float32, True)])
+def test_hadamard_block(vq, in_dt, out_dt, norm):
+    rng = np.random.default_rng(3)
+    x32 = (rng.laplace(size=(37, 1152)) * 3).astype(np.float32)
+    x = torch.from_numpy(x32).to(in_dt)
+    y = vq.vq_hadamard_block(x.to(DEV), out_dt, norm)
+    torch.cuda.synchronize()
+    ref = ofwht.hadamard_block(onum.to_f32(npb(x), dtname(x)), 128, norm)
+    assert_same(npb(y) if out_dt != torch.float32 else y.cpu().numpy(),
+                onum.from_f32(ref, dtname(y)), "hadamard output")
+
+
+def test_hadamard_c4_rows(vq):
+    x = gen.make_x(4, m=16)
+    y = vq.vq_hadamard_block(x.to(DEV), torch.bfloat16, True)
+    torch.cuda.synchronize()
+    ref = ofwht.hadamard_block(onum.to_f32(npb(x), "bf16"), 128, True)
+    assert_same(npb(y), onum.from_f32(ref, "bf16"), "hadamard c4")
+
+
+# ------------------------------------------------------------------ GEMM
+
+
+def run_layer(vq, x, w, a_bits, w_bits, gran="token", had=0, idx=None, out_dtype=torch.bfloat16, acc=True):
+    xd, wd = x.to(DEV), w.to(DEV)
+    idx_d = None if idx is None else torch.from_numpy(idx).to(DEV)
+    wc, ws = vq.vq_pack_weights(wd, w_bits, idx_d, had)
+    ac, as_ = vq.vq_quant_act(xd, a_bits, gran, had, idx_d)
+    k0 = x.shape[1] if idx is not None else ac.shape[1]
+    res = vq.vq_qgemm_dequant(ac, as_, wc, ws, w_bits, k0, out_dtype, gran == "token", acc_debug=acc)
+    torch.cuda.synchronize()
+    return (ac, as_, wc, ws) + (res if acc else (res, None))
+
+
+def oracle_layer(x, w, a_bits, w_bits, gran="token", had=0, idx=None, out_dtype="bf16"):
+    wcodes, _, wscales = oracle.linear.prepare_weights(npb(w), dtname(w), w_bits, had, idx)
+    return oracle.linear.forward(npb(x), dtname(x), a_bits, gran, wcodes, wscales, had, idx, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("cfg,m,n", [(2, 549, 320), (2, 17, 5760 // 9), (5, 300, 320)])
+def test_gemm_w8a8_and_w4a8(vq, cfg, m, n):
+    x = gen.make_x(cfg, m=m)
+    w = gen.make_w(cfg, n=n)
+    wb = 8 if cfg == 2 else 4
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 8, wb)
+    r = oracle_layer(x, w, 8, wb)
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "accumulators")
+    assert_outputs(y, r["y_store"], "bf16", "output")
+
+
+def test_gemm_dual_c3_small(vq):
+    x = gen.make_x(3, m=300)
+    w = gen.make_w(3, n=320)
+    mask, idx_t, _ = vq.vq_detect_outliers(w.to(DEV))
+    idx = idx_t.numpy()
+    assert idx.tolist() == gen.w_outlier_channels(3).tolist()
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 8, 4, idx=idx)
+    r = oracle_layer(x, w, 8, 4, idx=idx)
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "partition 0 accumulators")
+    assert_same(acc[1].cpu().numpy(), r["accs"][1], "partition 1 accumulators")
+    assert_outputs(y, r["y_store"], "bf16", "output")
+
+
+def test_gemm_dual_two_outlier_steps(vq):
+    """An outlier partition of 128 codes (two 64-code steps) with int8 weights."""
+    x = gen.make_x(2, m=70)
+    w = gen.make_w(2, n=96)
+    idx = np.sort(np.random.default_rng(1).choice(1920, 100, replace=False)).astype(np.int32)
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 8, 8, idx=idx)
+    r = oracle_layer(x, w, 8, 8, idx=idx)
+    assert ac.shape[1] == 1920 + 128
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "partition 0")
+    assert_same(acc[1].cpu().numpy(), r["accs"][1], "partition 1")
+    assert_outputs(y, r["y_store"], "bf16", "output")
+
+
+def test_gemm_hadamard_w4a6_c4_small(vq):
+    x = gen.make_x(4, m=40)
+    w = gen.make_w(4, n=288)
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 6, 4, had=128)
+    r = oracle_layer(x, w, 6, 4, had=128)
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "accumulators")
+    assert_outputs(y, r["y_store"], "bf16", "output")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.float32])
+def test_gemm_per_tensor_c1_full(vq, out_dtype):
+    x = gen.make_x(1)
+    w = gen.make_w(1)
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 8, 8, gran="tensor", out_dtype=out_dtype)
+    name = "fp16" if out_dtype == torch.float16 else "fp32"
+    r = oracle_layer(x, w, 8, 8, gran="tensor", out_dtype=name)
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "accumulators")
+    assert_outputs(y, r["y_store"], name, "output")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 64), (1, 4, 64), (3, 7, 128), (255, 257, 192), (257, 255, 64),
+                                   (513, 100, 320)])
+def test_gemm_ragged_shapes(vq, m, n, k):
+    rng = np.random.default_rng(m * 1000 + n)
+    qa = torch.from_numpy(rng.integers(-127, 128, size=(m, k)).astype(np.int8))
+    qw = rng.integers(-7, 8, size=(n, k)).astype(np.int8)
+    sa = torch.from_numpy(rng.uniform(0.001, 0.1, size=m).astype(np.float32))
+    sb = torch.from_numpy(rng.uniform(0.001, 0.1, size=n).astype(np.float32))
+    for bits in (8, 4):
+        b = torch.from_numpy(qw if bits == 8 else oq.pack_int4(qw))
+        y, acc = vq.vq_qgemm_dequant(qa.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), bits, None, torch.bfloat16,
+                                     True, acc_debug=True)
+        torch.cuda.synchronize()
+        accs, yf, ys = ogemm.qgemm_dequant(qa.numpy(), sa.numpy(), True, qw, sb.numpy(), k, "bf16")
+        assert_same(acc[0].cpu().numpy(), accs[0], f"acc bits={bits}")
+        assert_outputs(y, ys, "bf16", f"y bits={bits}")
+
+
+def test_gemm_extreme_accumulators(vq):
+    """|acc| near the int32 bound of the largest K; int4 path's 16x scaling stays in range."""
+    m, n, k = 64, 64, 12288
+    qa = torch.full((m, k), 127, dtype=torch.int8)
+    qa[1::2] = -127
+    qw = np.full((n, k), 7, dtype=np.int8)
+    qw[::3] = -7
+    sa = torch.ones(m, dtype=torch.float32)
+    sb = torch.ones(n, dtype=torch.float32)
+    y, acc = vq.vq_qgemm_dequant(qa.to(DEV), sa.to(DEV), torch.from_numpy(oq.pack_int4(qw)).to(DEV), sb.to(DEV),
+                                 4, None, torch.float32, True, acc_debug=True)
+    torch.cuda.synchronize()
+    accs, yf, ys = ogemm.qgemm_dequant(qa.numpy(), sa.numpy(), True, qw, sb.numpy(), k, "fp32")
+    assert_same(acc[0].cpu().numpy(), accs[0], "acc")
+    assert np.abs(accs[0]).max() == 127 * 7 * 12288
+
+
+# ------------------------------------------------------------------ detection and routing
+
+
+def test_detect_full_c3_weights(vq):
+    w = gen.make_w(3)
+    mask, idx, norms = vq.vq_detect_outliers(w.to(DEV))
+    r = oracle.linear.detect_on(npb(w), "bf16")
+    assert_same(mask.numpy().astype(bool), r["mask"], "mask")
+    assert_same(idx.numpy(), r["idx"], "outlier indices")
+    np.testing.assert_allclose(norms.numpy(), r["norms"], rtol=1e-12)
+    assert odetect.decision_margin(r["norms"]) > 1e-6
+
+
+def test_detect_c2_activations_and_kfac(vq):
+    x = gen.make_x(2, m=2048)
+    for kfac in (1.0, 0.6745):
+        mask, idx, norms = vq.vq_detect_outliers(x.to(DEV), 3.5, 2.0, kfac)
+        r = oracle.linear.detect_on(npb(x), "bf16", 3.5, 2.0, kfac)
+        assert_same(idx.numpy(), r["idx"], f"indices kfac={kfac}")
+
+
+def test_detect_worked_example(vq):
+    # columns whose L2 norms are the first hand-worked vector: one row holding v.
+    v = np.array([[1.0, 1.1, 0.9, 1.2, 0.8, 1.05, 6.0, 0.95]], dtype=np.float32)
+    t = torch.zeros((1, 16), dtype=torch.float32)
+    t[0, :8] = torch.from_numpy(v[0])
+    t[0, 8:] = 1.0
+    mask, idx, norms = vq.vq_detect_outliers(t.to(torch.float16).to(DEV))
+    r = oracle.linear.detect_on(npb(t.to(torch.float16)), "fp16")
+    assert_same(idx.numpy(), r["idx"], "indices")
+
+
+def test_route_pairs_and_tie(vq):
+    got_bits = []
+    for layer in range(42):
+        x, y, g = gen.make_route_pair(5, layer)
+        bits, gamma = vq.vq_route_rel_l1(x.to(DEV), y.to(DEV), 0.1, 8, 4)
+        torch.cuda.synchronize()
+        gr = oroute.relative_l1(onum.to_f32(npb(x), "bf16"), onum.to_f32(npb(y), "bf16"))
+        assert gamma.item() == pytest.approx(gr, rel=1e-13)
+        assert bits.item() == oroute.route_bits(gr, 0.1)
+        got_bits.append(bits.item())
+    assert 8 in got_bits and 4 in got_bits
+    x = torch.tensor([1, -2, 3, -4], dtype=torch.float32)
+    for yv, want in (([2, -2, 3, -4], 4), ([3, -2, 3, -4], 8)):
+        bits, gamma = vq.vq_route_rel_l1(x.to(DEV), torch.tensor(yv, dtype=torch.float32).to(DEV), 0.1, 8, 4)
+        torch.cuda.synchronize()
+        assert bits.item() == want
+
+
+def test_routed_quant_matches_route(vq):
+    """The device route feeds the quantizer with no host round trip."""
+    x = gen.make_x(5, m=64)
+    for layer in (0, 1, 2, 3):
+        xp, yp, g = gen.make_route_pair(5, layer)
+        bits, gamma = vq.vq_route_rel_l1(xp.to(DEV), yp.to(DEV), 0.1, 8, 4)
+        codes, scales = vq.vq_quant_act(x.to(DEV), 8, "token", bits_dev=bits)
+        torch.cuda.synchronize()
+        b = oroute.route_bits(oroute.relative_l1(onum.to_f32(npb(xp), "bf16"), onum.to_f32(npb(yp), "bf16")))
+        rc, rs = oq.quant_act(npb(x), "bf16", b, "token")
+        assert_same(codes.cpu().numpy(), rc, f"codes layer {layer}")
+
+
+# ------------------------------------------------------------------ determinism
+
+
+def test_runs_are_bitwise_deterministic(vq):
+    x = gen.make_x(3, m=300).to(DEV)
+    w = gen.make_w(3, n=320).to(DEV)
+    idx = torch.from_numpy(gen.w_outlier_channels(3).astype(np.int32)).to(DEV)
+    outs = []
+    for _ in range(2):
+        wc, ws = vq.vq_pack_weights(w, 4, idx)
+        ac, as_ = vq.vq_quant_act(x, 8, "token", 0, idx)
+        y = vq.vq_qgemm_dequant(ac, as_, wc, ws, 4, 3072, torch.bfloat16, True)
+        torch.cuda.synchronize()
+        outs.append((ac.cpu(), as_.cpu(), wc.cpu(), ws.cpu(), y.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
