@@ -42,7 +42,7 @@ class VQError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m bit_quantized_linear_vq_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python bit_quantized_linear_vq_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, I, D, F = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
                             ctypes.c_double, ctypes.c_float)

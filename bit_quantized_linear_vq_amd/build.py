@@ -1,6 +1,6 @@
 """Build libvq.so (the gfx950 kernels and the C ABI) in-tree with hipcc.
 
-    python -m bit_quantized_linear_vq_amd.build
+    python bit_quantized_linear_vq_amd/build.py
 
 Every source is compiled to an object under _build/ (in parallel), then linked
 into bit_quantized_linear_vq_amd/libvq.so.

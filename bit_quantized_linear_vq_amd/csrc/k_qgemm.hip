@@ -9,13 +9,26 @@
 // are unpacked to int8 operands (each nibble placed in the high half of its byte, i.e.
 // 16 * code, and the accumulator shifted right by 4 afterwards, which is exact).
 //
-// Tiling: a 256-thread workgroup (4 waves) computes a 256 (M) x 256 (N) tile, each wave
-// 128 x 128 as 8 x 8 blocks of v_mfma_i32_16x16x64_i8.  The weights are the MFMA's A
-// operand and the activations its B operand, so a lane's four accumulators are four
-// consecutive output columns of one row: the epilogue stores 4 outputs per lane.
-// K advances 64 codes per step through a double-buffered LDS stage whose rows are
-// padded (80 B for 64 int8 codes, 40 B for 32 packed bytes) so that the 16-lane row
-// groups of the fragment reads fall in distinct banks.
+// Tiling: a 512-thread workgroup (8 waves, two per SIMD) computes a 256 (M) x 256 (N)
+// tile; the waves form a 2 (M) x 4 (N) grid, each wave 128 x 64 as 4 x 2 blocks of
+// v_mfma_i32_32x32x32_i8 (on gfx950 this form keeps the matrix pipe busier than
+// 16x16x64).  Two waves per SIMD let one wave's MFMAs cover the other's waits, and they
+// double the LDS read rate a CU reaches (one wave per SIMD cannot issue reads fast
+// enough).  The weights are the MFMA's A operand and the activations its B operand, so
+// each group of four accumulators of a lane holds four consecutive output columns of one
+// row.
+//
+// Pipeline: K advances 64 codes per step through a ring of NST LDS stages filled by
+// gfx950's direct global->LDS loads (global_load_lds_dwordx4) issued NST-1 steps ahead,
+// so several steps of HBM/L2 latency hide behind the MFMAs without staging registers.
+// Each wave waits for its own loads with an explicit vmcnt, then a plain s_barrier (no
+// fence) publishes the stage to the other waves.  LDS rows are dense (64 B of int8
+// codes, 32 B of packed nibbles) with the 16-byte chunks XOR-swizzled by the row index
+// so that the 16-row fragment reads hit distinct banks.
+//
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2; block b is mapped so that every XCD walks a contiguous range of tiles in a grouped
+// order (8 M-tiles per sweep over N), keeping the A and B slices it reuses in its L2.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -24,15 +37,44 @@
 namespace vqk {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int PA = 80;  // LDS pitch of a 64-code int8 row
-constexpr int A_ST = BM * PA;
+constexpr int NT = 512;           // threads per workgroup
+constexpr int WTM = 128, WTN = 64;  // wave tile
+constexpr int MBLK = WTM / 32, NBLK = WTN / 32;
 
 template <int BBITS>
-struct BTile {
-  static constexpr int PITCH = BBITS == 8 ? 80 : 40;
-  static constexpr int ST = BN * PITCH;
-  static constexpr int STAGE = A_ST + ST;
+struct GCfg {
+  static constexpr int A_BYTES = BM * 64;
+  static constexpr int B_ROW = BBITS == 8 ? 64 : 32;
+  static constexpr int B_BYTES = BN * B_ROW;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NST = BBITS == 8 ? 4 : 5;
+  static constexpr int LA = A_BYTES / (NT * 16);  // 16-byte loads per thread per step
+  static constexpr int LB = B_BYTES / (NT * 16);
+  static constexpr int L = LA + LB;
 };
+
+// Chunk swizzles: 16-byte chunk c of row r is stored at position c ^ swz(r).
+// Both depend only on r & 15, so a fragment read of rows 16*blk + (lane & 15) can use
+// the lane's constant swizzle for every block.
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz32(int r) { return (r >> 3) & 1; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS at ldst + 16 * lane (ldst is
+// wave-uniform).  A __device__ function, not a lambda: lambdas in kernels are also host
+// functions, and a device-only builtin there makes the host pass drop the kernel stub.
+__device__ __forceinline__ void dma16(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)ldst, 16, 0, 0);
+}
 
 struct GArgs {
   const int8_t* a;
@@ -85,114 +127,159 @@ __device__ __forceinline__ void store4(void* y, int64_t off, const float v[4], i
   }
 }
 
+// Block b -> tile (tm, tn): contiguous tile ranges per XCD, grouped order inside.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int q = T >> 3, r = T & 7;
+  const int x = b & 7, j = b >> 3;
+  const int t = x * q + min(x, r) + j;
+  constexpr int GROUP = 8;
+  const int width = GROUP * tiles_n;
+  const int first_m = (t / width) * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  tm = first_m + (t % width) % gsz;
+  tn = (t % width) / gsz;
+}
+
 template <int BBITS, int OUT_DT, bool DUAL>
-__global__ __launch_bounds__(256, 1) void k_qgemm(GArgs g) {
-  using BT = BTile<BBITS>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BT::STAGE];
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm(GArgs g) {
+  using C = GCfg<BBITS>;
+  constexpr int P = DUAL ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
+  __shared__ float s_sa[P][BM];
+  __shared__ float s_sb[P][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // wave grid 2 (M) x 4 (N)
 
-  // Grouped tile order: 8 M-tiles share each sweep over N.
-  constexpr int GROUP = 8;
-  const int tile = blockIdx.x;
-  const int width = GROUP * g.tiles_n;
-  const int first_m = (tile / width) * GROUP;
-  const int gsz = min(g.tiles_m - first_m, GROUP);
-  const int tm = first_m + (tile % width) % gsz;
-  const int tn = (tile % width) / gsz;
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Global -> LDS copy assignment.
-  const int8_t* ga[4];
-  int la[4];
+  // ---- direct-load assignment: instruction q of this wave fills 1 KB of a stage.
+  // A: 16 rows x 64 B per instruction, lane -> (row, position) = (lane >> 2, lane & 3).
+  const int8_t* ga[C::LA];
+  int la_off[C::LA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 2) + 64 * i;
-    const int c16 = tid & 3;
-    const int gr = min(m0 + row, g.m - 1);
-    ga[i] = g.a + (int64_t)gr * g.kp + 16 * c16;
-    la[i] = row * PA + 16 * c16;
+  for (int i = 0; i < C::LA; ++i) {
+    const int q = wave * C::LA + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ swz64(r);
+    const int gr = min(m0 + r, g.m - 1);
+    ga[i] = g.a + (int64_t)gr * g.kp + 16 * c;
+    la_off[i] = q * 1024;
   }
-  constexpr int NB = BBITS == 8 ? 4 : 2;
-  const uint8_t* gb[NB];
-  int lb[NB];
+  const uint8_t* gb[C::LB];
+  int lb_off[C::LB];
   const int64_t ldb = BBITS == 8 ? g.kp : g.kp / 2;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int row = BBITS == 8 ? (tid >> 2) + 64 * i : (tid >> 1) + 128 * i;
-    const int c16 = BBITS == 8 ? (tid & 3) : (tid & 1);
-    const int gr = min(n0 + row, g.n - 1);
-    gb[i] = g.b + (int64_t)gr * ldb + 16 * c16;
-    lb[i] = A_ST + row * BT::PITCH + 16 * c16;
+  for (int i = 0; i < C::LB; ++i) {
+    const int q = wave * C::LB + i;
+    int r, c;
+    if constexpr (BBITS == 8) {
+      r = 16 * q + (lane >> 2);
+      c = (lane & 3) ^ swz64(r);
+    } else {
+      r = 32 * q + (lane >> 1);
+      c = (lane & 1) ^ swz32(r);
+    }
+    const int gr = min(n0 + r, g.n - 1);
+    gb[i] = g.b + (int64_t)gr * ldb + 16 * c;
+    lb_off[i] = C::A_BYTES + q * 1024;
   }
 
-  u4v ra[4], rb[NB];
-  auto gload = [&](int k) {
+  auto issue = [&](int k, int slot) {
+    uint8_t* base = lds + slot * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u4v*>(ga[i] + k);
+    for (int i = 0; i < C::LA; ++i)
+      dma16(ga[i] + k, base + la_off[i]);
     const int kb = BBITS == 8 ? k : k / 2;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const u4v*>(gb[i] + kb);
-  };
-  auto swrite = [&](int stage) {
-    uint8_t* base = lds + stage * BT::STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u4v*>(base + la[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if constexpr (BBITS == 8) {
-        *reinterpret_cast<u4v*>(base + lb[i]) = rb[i];
-      } else {
-        u2v lo = {rb[i].x, rb[i].y}, hi = {rb[i].z, rb[i].w};
-        *reinterpret_cast<u2v*>(base + lb[i]) = lo;
-        *reinterpret_cast<u2v*>(base + lb[i] + 8) = hi;
-      }
-    }
+    for (int i = 0; i < C::LB; ++i)
+      dma16(gb[i] + kb, base + lb_off[i]);
   };
 
-  // Fragment addresses inside a stage.
-  const int fa = (wm * 128 + (lane & 15)) * PA + 16 * (lane >> 4);
-  const int fb = A_ST + (wn * 128 + (lane & 15)) * BT::PITCH + (BBITS == 8 ? 16 : 8) * (lane >> 4);
-
-  auto afrag = [&](int stage, int mb) -> v4i {
-    return *reinterpret_cast<const v4i*>(lds + stage * BT::STAGE + fa + mb * 16 * PA);
-  };
-  auto bfrag = [&](int stage, int nb) -> v4i {
-    const uint8_t* p = lds + stage * BT::STAGE + fb + nb * 16 * BT::PITCH;
+  // ---- fragment offsets (per lane, constant): rows 32*blk + (lane & 31), k-half h:
+  // 16-byte chunk 2h + (lane >> 5) of the 64-code row.
+  const int rl = lane & 31;
+  const int kc = lane >> 5;
+  int fa[2], fb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    fa[h] = (wm * WTM + rl) * 64 + 16 * ((2 * h + kc) ^ swz64(rl));
     if constexpr (BBITS == 8) {
-      return *reinterpret_cast<const v4i*>(p);
+      fb[h] = C::A_BYTES + (wn * WTN + rl) * 64 + 16 * ((2 * h + kc) ^ swz64(rl));
     } else {
-      return unpack_int4x16(*reinterpret_cast<const u2v*>(p));
+      fb[h] = C::A_BYTES + (wn * WTN + rl) * 32 + 16 * (h ^ swz32(rl)) + 8 * kc;
+    }
+  }
+  auto afrag = [&](int slot, int h, int mb) -> v4i {
+    return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fa[h] + mb * 32 * 64);
+  };
+  auto bfrag = [&](int slot, int h, int nb) -> v4i {
+    if constexpr (BBITS == 8) {
+      return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 64);
+    } else {
+      return unpack_int4x16(*reinterpret_cast<const u2v*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 32));
     }
   };
 
-  v4i acc[8][8];
+  v16i acc[MBLK][NBLK];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MBLK; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
 
   const int nk = g.k0 / BK;
-  gload(0);
-  swrite(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < C::NST - 1; ++s)
+    if (s < nk) issue(s * BK, s);
+
+  // Scales of the tile's rows and columns, read once (published by the first barrier).
+  for (int i = tid; i < P * BM; i += NT) {
+    const int p = i / BM, r = i - p * BM;
+    s_sa[p][r] = g.sa_tok ? g.sa[(int64_t)min(m0 + r, g.m - 1) * P + p] : g.sa[p];
+    s_sb[p][r] = g.sb[(int64_t)min(n0 + r, g.n - 1) * P + p];
+  }
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    v4i af[8];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) af[mb] = afrag(cur, mb);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const v4i bf = bfrag(cur, nb);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf, af[mb], acc[mb][nb], 0, 0, 0);
+    // Loads of step kt are complete once at most (steps issued after it) * L remain.
+    const int later = min(C::NST - 2, nk - 1 - kt);
+    if (later >= C::NST - 2) {
+      wait_vmcnt<(C::NST - 2) * C::L>();
+    } else if (later == 3) {
+      wait_vmcnt<3 * C::L>();
+    } else if (later == 2) {
+      wait_vmcnt<2 * C::L>();
+    } else if (later == 1) {
+      wait_vmcnt<C::L>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (kt + 1 < nk) swrite(cur ^ 1);
-    __syncthreads();
+    barrier_nofence();
+    // The slot refilled now held step kt-1, which every wave finished before the barrier.
+    if (kt + C::NST - 1 < nk) issue((kt + C::NST - 1) * BK, (kt + C::NST - 1) % C::NST);
+    const int slot = kt % C::NST;
+    // B fragments are read one block ahead of the MFMAs that use them.
+    v4i bcur = bfrag(slot, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4i af[MBLK];
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) af[mb] = afrag(slot, h, mb);
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb) {
+        v4i bnext = bcur;
+        if (nb < NBLK - 1) bnext = bfrag(slot, h, nb + 1);
+        else if (h == 0) bnext = bfrag(slot, 1, 0);
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bcur, af[mb], acc[mb][nb], 0, 0, 0);
+        bcur = bnext;
+      }
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -202,68 +289,103 @@ __global__ __launch_bounds__(256, 1) void k_qgemm(GArgs g) {
   int steps1 = 0;
   if constexpr (DUAL) {
     steps1 = (g.kp - g.k0) / BK;
-    gload(g.k0);
-    swrite(0);
-    if (steps1 > 1) {
-      gload(g.k0 + BK);
-      swrite(1);
-    }
-    __syncthreads();
+    barrier_nofence();  // every wave is done with the ring
+    issue(g.k0, 0);
+    if (steps1 > 1) issue(g.k0 + BK, 1);
+    wait_vmcnt<0>();
+    barrier_nofence();
   }
 
-  constexpr int P = DUAL ? 2 : 1;
-  const int mrow0 = m0 + wm * 128 + (lane & 15);
-  const int ncol0 = n0 + wn * 128 + 4 * (lane >> 4);
+  // Output layout of a 32 x 32 block: lane holds column m = lane & 31 (activation row)
+  // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows).
+  // 16-bit outputs go through a wave-private LDS buffer of 32 rows x 64 columns (row
+  // pitch 136 B, so the 32 row writes of an instruction fall in distinct banks) and
+  // leave as whole 128-byte row segments, 16 B per lane.
+  const int mrow = wm * WTM + (lane & 31);        // tile-local row of this lane
+  const int ncol = wn * WTN + 4 * (lane >> 5);    // tile-local first column of this lane
   const int64_t mn = (int64_t)g.m * g.n;
-
-  float sa_r[8][P];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    const int mc = min(mrow0 + mb * 16, g.m - 1);
-#pragma unroll
-    for (int p = 0; p < P; ++p) sa_r[mb][p] = g.sa_tok ? g.sa[(int64_t)mc * P + p] : g.sa[p];
-  }
+  constexpr bool STAGED = OUT_DT != DT_F32;
+  constexpr int SPITCH = WTN * 2 + 8;
+  uint8_t* stg = lds + (DUAL ? 2 * C::STAGE : 0) + wave * 32 * SPITCH;
 
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const int n = ncol0 + nb * 16;
-    float sb_r[4][P];
+  for (int mb = 0; mb < MBLK; ++mb) {
+    const int ml = mrow + mb * 32;
+    const int m = m0 + ml;
+    float sa0[P];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int p = 0; p < P; ++p) sa0[p] = s_sa[p][ml];
 #pragma unroll
-      for (int p = 0; p < P; ++p) sb_r[r][p] = g.sb[(int64_t)min(n + r, g.n - 1) * P + p];
-    v4i bf1[2];
-    if constexpr (DUAL) {
-      bf1[0] = bfrag(0, nb);
-      bf1[1] = steps1 > 1 ? bfrag(1, nb) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int m = mrow0 + mb * 16;
-      v4i t1 = v4i{0, 0, 0, 0};
+    for (int nb = 0; nb < NBLK; ++nb) {
+      v16i t1 = v16i{};
       if constexpr (DUAL) {
-        t1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf1[0], afrag(0, mb), t1, 0, 0, 0);
-        if (steps1 > 1) t1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf1[1], afrag(1, mb), t1, 0, 0, 0);
-      }
-      float out[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int a0 = acc[mb][nb][r];
-        if constexpr (BBITS == 4) a0 >>= 4;
-        const float t0 = sa_r[mb][0] * sb_r[r][0];
-        float yv = (float)a0 * t0;
-        if constexpr (DUAL) {
-          int a1 = t1[r];
-          if constexpr (BBITS == 4) a1 >>= 4;
-          const float tt = sa_r[mb][P - 1] * sb_r[r][P - 1];
-          const float y1 = (float)a1 * tt;
-          yv = yv + y1;
-          if (g.accd && m < g.m && n + r < g.n) g.accd[mn + (int64_t)m * g.n + n + r] = a1;
+        for (int s1 = 0; s1 < 2; ++s1) {
+          if (s1 < steps1) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(s1, h, nb), afrag(s1, h, mb), t1, 0, 0, 0);
+          }
         }
-        if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
-        out[r] = yv;
       }
-      if (m < g.m && n < g.n) store4<OUT_DT>(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = ncol + nb * 32 + 8 * q;
+        const int n = n0 + nl;
+        const v4f sb0 = *reinterpret_cast<const v4f*>(&s_sb[0][nl]);
+        v4f sb1 = sb0;
+        if constexpr (DUAL) sb1 = *reinterpret_cast<const v4f*>(&s_sb[1][nl]);
+        float out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int a0 = acc[mb][nb][4 * q + r];
+          if constexpr (BBITS == 4) a0 >>= 4;
+          const float t0 = sa0[0] * sb0[r];
+          float yv = (float)a0 * t0;
+          if constexpr (DUAL) {
+            int a1 = t1[4 * q + r];
+            if constexpr (BBITS == 4) a1 >>= 4;
+            const float tt = sa0[P - 1] * sb1[r];
+            const float y1 = (float)a1 * tt;
+            yv = yv + y1;
+            if (g.accd && m < g.m && n + r < g.n) g.accd[mn + (int64_t)m * g.n + n + r] = a1;
+          }
+          if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
+          out[r] = yv;
+        }
+        if constexpr (STAGED) {
+          typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+          h_t hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[r] = (h_t)f32_fence(out[r]);
+          u2v w = {(unsigned)__builtin_bit_cast(unsigned short, hv[0]) | ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
+                   (unsigned)__builtin_bit_cast(unsigned short, hv[2]) | ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
+          *reinterpret_cast<u2v*>(stg + (lane & 31) * SPITCH + (nl - wn * WTN) * 2) = w;
+        } else {
+          if (m < g.m && n < g.n) store4<OUT_DT>(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
+        }
+      }
+    }
+    if constexpr (STAGED) {
+      // 32 rows x 128 B: each lane stores 16 B, eight rows per instruction.
+      typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 8 * i + (lane >> 3);
+        const int cc = 8 * (lane & 7);
+        const u4v w = *reinterpret_cast<const u4v*>(stg + rr * SPITCH + cc * 2);
+        const int mo = m0 + wm * WTM + mb * 32 + rr;
+        const int no = n0 + wn * WTN + cc;
+        if (mo < g.m && no < g.n) {
+          h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)mo * g.ldy + no;
+          if (g.vec_store && no + 8 <= g.n) {
+            *reinterpret_cast<u4v*>(dst) = w;
+          } else {
+            const unsigned short* hs = reinterpret_cast<const unsigned short*>(&w);
+            for (int e = 0; e < 8 && no + e < g.n; ++e) dst[e] = __builtin_bit_cast(h_t, hs[e]);
+          }
+        }
+      }
     }
   }
 }
@@ -271,9 +393,9 @@ __global__ __launch_bounds__(256, 1) void k_qgemm(GArgs g) {
 template <int BBITS, int OUT_DT>
 static hipError_t launch_dual(const GArgs& a, bool dual, int grid, hipStream_t st) {
   if (dual)
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true>), dim3(grid), dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false>), dim3(grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
