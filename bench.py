@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (five times) and exit; "
+                        "rocprofv3 counters of that copy scale FETCH_SIZE/WRITE_SIZE to bytes")
     return p.parse_args()
 
 
@@ -51,16 +54,23 @@ def kernel_hash(name):
 
 
 def load_traffic(workload):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if current."""
+    """HBM bytes per launch (GEMM, quantization) from the committed rocprofv3 counter runs.
+
+    Each figure is None unless it was measured on the kernel source as it is now.
+    """
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     e = t.get(workload)
-    if not e or e.get("kernel_sha") != kernel_hash("k_qgemm.hip"):
-        return None
-    return e.get("bytes_per_launch")
+    if not e:
+        return None, None
+    g = e.get("bytes_per_launch") if e.get("kernel_sha") == kernel_hash("k_qgemm.hip") else None
+    q = None
+    if e.get("quant_kernel_sha") == kernel_hash("k_quant.hip") and "quant_fetch_bytes" in e:
+        q = e["quant_fetch_bytes"] + e["quant_write_bytes"]
+    return g, q
 
 
 class Layer:
@@ -170,6 +180,16 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
     import bit_quantized_linear_vq_amd as vq
     import gen
 
@@ -223,7 +243,7 @@ def main():
     quant_gbs = L.quant_bytes() / (q_ms * 1e-3) / 1e9
     tops = L.ops_per_step() / (ms * 1e-3) / 1e12
     workload = gen.CONFIGS[args.config]["name"]
-    traffic = load_traffic(workload)
+    traffic, q_traffic = load_traffic(workload)
 
     out = {
         "metric": "quantized-linear TOPS (int8 MFMA %peak) + act-quant GB/s (%HBM), 1 MI355X",
@@ -248,7 +268,7 @@ def main():
                      "kernel": "k_qgemm (int8 MFMA GEMM + dequant epilogue)", "avg_us": round(g_ms * 1e3, 2)},
         "act_quant": {"bound": "hbm", "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "bytes": L.quant_bytes(),
-                      "avg_us": round(q_ms * 1e3, 2), "kernel": "k_rowquant"},
+                      "avg_us": round(q_ms * 1e3, 2), "kernel": "k_rowquant", "traffic": q_traffic},
     }
     if args.config == 5:
         out["config"]["routes_int8"] = L.routes.count(8)
