@@ -70,10 +70,14 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 16 bytes per lane from global memory straight into LDS at ldst + 16 * lane (ldst is
-// wave-uniform).  A __device__ function, not a lambda: lambdas in kernels are also host
-// functions, and a device-only builtin there makes the host pass drop the kernel stub.
+// wave-uniform).  Written as inline asm: the compiler cannot tell these LDS writes from
+// the fragment reads of other stages and would otherwise drain every outstanding load
+// (vmcnt(0)) before each read.  The instruction has no register outputs (the data goes
+// to LDS), its completion is tracked with explicit vmcnt waits, and m0 is set inside
+// the statement; no other code of this kernel reads m0.
 __device__ __forceinline__ void dma16(const void* gsrc, void* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)ldst, 16, 0, 0);
+  const unsigned la = (unsigned)(size_t)(lds_ptr_t)ldst;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(gsrc) : "memory");
 }
 
 struct GArgs {
@@ -218,19 +222,50 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto afrag = [&](int slot, int h, int mb) -> v4i {
     return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fa[h] + mb * 32 * 64);
   };
-  auto bfrag = [&](int slot, int h, int nb) -> v4i {
+  // B fragment as stored (int8 codes, or the 8 packed bytes in .xy for 4-bit weights).
+  auto braw = [&](int slot, int h, int nb) -> v4i {
     if constexpr (BBITS == 8) {
       return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 64);
     } else {
-      return unpack_int4x16(*reinterpret_cast<const u2v*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 32));
+      const u2v w = *reinterpret_cast<const u2v*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 32);
+      return v4i{(int)w.x, (int)w.y, 0, 0};
     }
   };
+  auto bval = [&](v4i raw) -> v4i {
+    if constexpr (BBITS == 8) {
+      return raw;
+    } else {
+      return unpack_int4x16(u2v{(unsigned)raw.x, (unsigned)raw.y});
+    }
+  };
+  auto bfrag = [&](int slot, int h, int nb) -> v4i { return bval(braw(slot, h, nb)); };
 
   v16i acc[MBLK][NBLK];
 #pragma unroll
   for (int i = 0; i < MBLK; ++i)
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
+
+  // Fragments of one k-half (32 codes) of a stage.
+  struct Frag {
+    v4i a[MBLK];
+    v4i b[NBLK];
+  };
+  auto load_half = [&](int slot, int h, Frag& f) {
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb) f.b[nb] = braw(slot, h, nb);
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) f.a[mb] = afrag(slot, h, mb);
+  };
+  auto mma_half = [&](const Frag& f) {
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb) {
+      const v4i bv = bval(f.b[nb]);
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, f.a[mb], acc[mb][nb], 0, 0, 0);
+    }
+  };
 
   const int nk = g.k0 / BK;
 #pragma unroll
@@ -244,12 +279,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     s_sb[p][r] = g.sb[(int64_t)min(n0 + r, g.n - 1) * P + p];
   }
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // Loads of step kt are complete once at most (steps issued after it) * L remain.
-    const int later = min(C::NST - 2, nk - 1 - kt);
-    if (later >= C::NST - 2) {
-      wait_vmcnt<(C::NST - 2) * C::L>();
-    } else if (later == 3) {
+  // Half-step software pipeline.  Step kt uses stage kt % NST; its second half's
+  // fragments are read while the first half's MFMAs run.  In the middle of the step
+  // every wave waits for its loads of step kt+1 and meets the others at a barrier,
+  // which publishes stage kt+1 and certifies that stage kt-1 is no longer read; that
+  // stage then receives step kt+NST-1, and the first half of step kt+1 is read while
+  // the second half of step kt runs.
+  auto wait_loads = [&](int later) {  // at most `later` load groups may stay in flight
+    if (later >= 3) {
       wait_vmcnt<3 * C::L>();
     } else if (later == 2) {
       wait_vmcnt<2 * C::L>();
@@ -258,28 +295,53 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     } else {
       wait_vmcnt<0>();
     }
-    barrier_nofence();
-    // The slot refilled now held step kt-1, which every wave finished before the barrier.
-    if (kt + C::NST - 1 < nk) issue((kt + C::NST - 1) * BK, (kt + C::NST - 1) % C::NST);
-    const int slot = kt % C::NST;
-    // B fragments are read one block ahead of the MFMAs that use them.
-    v4i bcur = bfrag(slot, 0, 0);
+  };
+  Frag f0, f1;
+  wait_loads(min(C::NST - 2, nk - 1));
+  barrier_nofence();
+  load_half(0, 0, f0);
+  int kt = 0, slot = 0;
+  // Steady state: every step refills a stage and keeps NST-3 load groups in flight.
+  // The body has no branch, so the waits the compiler inserts for the fragments stay
+  // partial (lgkmcnt of the reads issued later) instead of draining all LDS reads.
+  for (; kt < nk - (C::NST - 1); ++kt) {
+    const int next = slot + 1 == C::NST ? 0 : slot + 1;
+    const int refill = slot == 0 ? C::NST - 1 : slot - 1;
+    // First half: MFMAs on f0 with the reads of f1 interleaved between them.
+    load_half(slot, 1, f1);
+    mma_half(f0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v4i af[MBLK];
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) af[mb] = afrag(slot, h, mb);
-#pragma unroll
-      for (int nb = 0; nb < NBLK; ++nb) {
-        v4i bnext = bcur;
-        if (nb < NBLK - 1) bnext = bfrag(slot, h, nb + 1);
-        else if (h == 0) bnext = bfrag(slot, 1, 0);
-#pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bcur, af[mb], acc[mb][nb], 0, 0, 0);
-        bcur = bnext;
-      }
+    for (int i = 0; i < MBLK + NBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
+    wait_vmcnt<(C::NST - 3) * C::L>();
+    barrier_nofence();
+    issue((kt + C::NST - 1) * BK, refill);
+    // Second half: MFMAs on f1 with the reads of the next step's f0 interleaved.
+    load_half(next, 0, f0);
+    mma_half(f1);
+#pragma unroll
+    for (int i = 0; i < MBLK + NBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
+    slot = next;
+  }
+  // Last NST-1 steps: nothing left to load; fewer groups in flight each step.
+  for (; kt < nk; ++kt) {
+    const int next = slot + 1 == C::NST ? 0 : slot + 1;
+    load_half(slot, 1, f1);
+    mma_half(f0);
+    if (kt + 1 < nk) {
+      wait_loads(nk - 2 - kt);
+      barrier_nofence();
+      load_half(next, 0, f0);
+    }
+    mma_half(f1);
+    slot = next;
   }
 
   // ---------------------------------------------------------------- epilogue
