@@ -149,60 +149,91 @@ template <int BBITS, int OUT_DT, bool DUAL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm(GArgs g) {
   using C = GCfg<BBITS>;
   constexpr int P = DUAL ? 2 : 1;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
-  __shared__ float s_sa[P][BM];
-  __shared__ float s_sb[P][BN];
+  constexpr bool STAGED = OUT_DT != DT_F32;
+  constexpr int SPITCH = WTN * 2 + 8;  // staging row pitch: 32 row writes hit distinct banks
+  constexpr int SROWS = 16;            // staging rows per pass
+  constexpr int STG_WAVE = SROWS * SPITCH;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE + 8 * STG_WAVE];
+  __shared__ float s_sa[2][P][BM];
+  __shared__ float s_sb[2][P][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // wave grid 2 (M) x 4 (N)
-
-  int tm, tn;
-  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int T = g.tiles_m * g.tiles_n;
+  const int nk = g.k0 / BK;
 
   // ---- direct-load assignment: instruction q of this wave fills 1 KB of a stage.
   // A: 16 rows x 64 B per instruction, lane -> (row, position) = (lane >> 2, lane & 3).
-  const int8_t* ga[C::LA];
-  int la_off[C::LA];
+  int ra[C::LA], rb[C::LB];  // tile-local rows loaded by this lane
+  int la_off[C::LA], lb_off[C::LB], ca[C::LA], cb[C::LB];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
     const int q = wave * C::LA + i;
-    const int r = 16 * q + (lane >> 2);
-    const int c = (lane & 3) ^ swz64(r);
-    const int gr = min(m0 + r, g.m - 1);
-    ga[i] = g.a + (int64_t)gr * g.kp + 16 * c;
+    ra[i] = 16 * q + (lane >> 2);
+    ca[i] = 16 * ((lane & 3) ^ swz64(ra[i]));
     la_off[i] = q * 1024;
   }
-  const uint8_t* gb[C::LB];
-  int lb_off[C::LB];
-  const int64_t ldb = BBITS == 8 ? g.kp : g.kp / 2;
 #pragma unroll
   for (int i = 0; i < C::LB; ++i) {
     const int q = wave * C::LB + i;
-    int r, c;
     if constexpr (BBITS == 8) {
-      r = 16 * q + (lane >> 2);
-      c = (lane & 3) ^ swz64(r);
+      rb[i] = 16 * q + (lane >> 2);
+      cb[i] = 16 * ((lane & 3) ^ swz64(rb[i]));
     } else {
-      r = 32 * q + (lane >> 1);
-      c = (lane & 1) ^ swz32(r);
+      rb[i] = 32 * q + (lane >> 1);
+      cb[i] = 16 * ((lane & 1) ^ swz32(rb[i]));
     }
-    const int gr = min(n0 + r, g.n - 1);
-    gb[i] = g.b + (int64_t)gr * ldb + 16 * c;
     lb_off[i] = C::A_BYTES + q * 1024;
   }
-
+  const int64_t ldb = BBITS == 8 ? g.kp : g.kp / 2;
+  const int8_t* ga[C::LA];
+  const uint8_t* gb[C::LB];
+  int m0 = 0, n0 = 0;
+  auto set_tile = [&](int vt) {
+    int tm, tn;
+    tile_of(vt, g.tiles_m, g.tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) ga[i] = g.a + (int64_t)min(m0 + ra[i], g.m - 1) * g.kp + ca[i];
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * ldb + cb[i];
+  };
   auto issue = [&](int k, int slot) {
     uint8_t* base = lds + slot * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i)
-      dma16(ga[i] + k, base + la_off[i]);
+    for (int i = 0; i < C::LA; ++i) dma16(ga[i] + k, base + la_off[i]);
     const int kb = BBITS == 8 ? k : k / 2;
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i)
-      dma16(gb[i] + kb, base + lb_off[i]);
+    for (int i = 0; i < C::LB; ++i) dma16(gb[i] + kb, base + lb_off[i]);
+  };
+  auto issue_prologue = [&]() {
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+      if (s < nk) issue(s * BK, s);
+  };
+  // Scales of a tile's rows and columns: loaded into registers early, written to LDS late.
+  float sc_a[P], sc_b[P];
+  const int srow = tid & (BM - 1);  // 512 threads: each loads one row scale or one column scale
+  auto load_scales = [&]() {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (tid < BM)
+        sc_a[p] = g.sa_tok ? g.sa[(int64_t)min(m0 + srow, g.m - 1) * P + p] : g.sa[p];
+      else
+        sc_b[p] = g.sb[(int64_t)min(n0 + srow, g.n - 1) * P + p];
+    }
+  };
+  auto store_scales = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (tid < BM)
+        s_sa[buf][p][srow] = sc_a[p];
+      else
+        s_sb[buf][p][srow] = sc_b[p];
+    }
   };
 
   // ---- fragment offsets (per lane, constant): rows 32*blk + (lane & 31), k-half h:
@@ -241,10 +272,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto bfrag = [&](int slot, int h, int nb) -> v4i { return bval(braw(slot, h, nb)); };
 
   v16i acc[MBLK][NBLK];
-#pragma unroll
-  for (int i = 0; i < MBLK; ++i)
-#pragma unroll
-    for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
 
   // Fragments of one k-half (32 codes) of a stage.
   struct Frag {
@@ -266,25 +293,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, f.a[mb], acc[mb][nb], 0, 0, 0);
     }
   };
-
-  const int nk = g.k0 / BK;
-#pragma unroll
-  for (int s = 0; s < C::NST - 1; ++s)
-    if (s < nk) issue(s * BK, s);
-
-  // Scales of the tile's rows and columns, read once (published by the first barrier).
-  for (int i = tid; i < P * BM; i += NT) {
-    const int p = i / BM, r = i - p * BM;
-    s_sa[p][r] = g.sa_tok ? g.sa[(int64_t)min(m0 + r, g.m - 1) * P + p] : g.sa[p];
-    s_sb[p][r] = g.sb[(int64_t)min(n0 + r, g.n - 1) * P + p];
-  }
-
-  // Half-step software pipeline.  Step kt uses stage kt % NST; its second half's
-  // fragments are read while the first half's MFMAs run.  In the middle of the step
-  // every wave waits for its loads of step kt+1 and meets the others at a barrier,
-  // which publishes stage kt+1 and certifies that stage kt-1 is no longer read; that
-  // stage then receives step kt+NST-1, and the first half of step kt+1 is read while
-  // the second half of step kt runs.
   auto wait_loads = [&](int later) {  // at most `later` load groups may stay in flight
     if (later >= 3) {
       wait_vmcnt<3 * C::L>();
@@ -296,159 +304,218 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       wait_vmcnt<0>();
     }
   };
-  Frag f0, f1;
-  wait_loads(min(C::NST - 2, nk - 1));
-  barrier_nofence();
-  load_half(0, 0, f0);
-  int kt = 0, slot = 0;
-  // Steady state: every step refills a stage and keeps NST-3 load groups in flight.
-  // The body has no branch, so the waits the compiler inserts for the fragments stay
-  // partial (lgkmcnt of the reads issued later) instead of draining all LDS reads.
-  for (; kt < nk - (C::NST - 1); ++kt) {
-    const int next = slot + 1 == C::NST ? 0 : slot + 1;
-    const int refill = slot == 0 ? C::NST - 1 : slot - 1;
-    // First half: MFMAs on f0 with the reads of f1 interleaved between them.
-    load_half(slot, 1, f1);
-    mma_half(f0);
+
+  // Persistent loop: block b takes tiles b, b + gridDim.x, ...  The next tile's scales
+  // and first NST-1 stages are requested before the current tile's epilogue, so its
+  // load latency and this tile's output stores overlap.
+  int vt = blockIdx.x;
+  if (vt >= T) return;
+  set_tile(vt);
+  issue_prologue();
+  load_scales();
+  store_scales(0);
+  int buf = 0;
+  for (;;) {
 #pragma unroll
-    for (int i = 0; i < MBLK + NBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
-    wait_vmcnt<(C::NST - 3) * C::L>();
+    for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
+
+    // Half-step software pipeline.  Step kt uses stage kt % NST; its second half's
+    // fragments are read while the first half's MFMAs run.  In the middle of the step
+    // every wave waits for its loads of step kt+1 and meets the others at a barrier,
+    // which publishes stage kt+1 and certifies that stage kt-1 is no longer read; that
+    // stage then receives step kt+NST-1, and the first half of step kt+1 is read while
+    // the second half of step kt runs.
+    Frag f0, f1;
+    wait_loads(min(C::NST - 2, nk - 1));
     barrier_nofence();
-    issue((kt + C::NST - 1) * BK, refill);
-    // Second half: MFMAs on f1 with the reads of the next step's f0 interleaved.
-    load_half(next, 0, f0);
-    mma_half(f1);
+    load_half(0, 0, f0);
+    int kt = 0, slot = 0;
+    // Steady state: every step refills a stage and keeps NST-3 load groups in flight.
+    // The body has no branch, so the waits the compiler inserts for the fragments stay
+    // partial (lgkmcnt of the reads issued later) instead of draining all LDS reads.
+    for (; kt < nk - (C::NST - 1); ++kt) {
+      const int next = slot + 1 == C::NST ? 0 : slot + 1;
+      const int refill = slot == 0 ? C::NST - 1 : slot - 1;
+      // First half: MFMAs on f0 with the reads of f1 interleaved between them.
+      load_half(slot, 1, f1);
+      mma_half(f0);
 #pragma unroll
-    for (int i = 0; i < MBLK + NBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
-    slot = next;
-  }
-  // Last NST-1 steps: nothing left to load; fewer groups in flight each step.
-  for (; kt < nk; ++kt) {
-    const int next = slot + 1 == C::NST ? 0 : slot + 1;
-    load_half(slot, 1, f1);
-    mma_half(f0);
-    if (kt + 1 < nk) {
-      wait_loads(nk - 2 - kt);
+      for (int i = 0; i < MBLK + NBLK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
+      wait_vmcnt<(C::NST - 3) * C::L>();
       barrier_nofence();
+      issue((kt + C::NST - 1) * BK, refill);
+      // Second half: MFMAs on f1 with the reads of the next step's f0 interleaved.
       load_half(next, 0, f0);
-    }
-    mma_half(f1);
-    slot = next;
-  }
-
-  // ---------------------------------------------------------------- epilogue
-  // Each 16 x 16 block is dequantized and stored on its own; with dual scale the
-  // outlier partition [k0, kp) (at most two 64-code steps) is staged in LDS first and
-  // its block product is added in float32: y = fl(y_0 + y_1).
-  int steps1 = 0;
-  if constexpr (DUAL) {
-    steps1 = (g.kp - g.k0) / BK;
-    barrier_nofence();  // every wave is done with the ring
-    issue(g.k0, 0);
-    if (steps1 > 1) issue(g.k0 + BK, 1);
-    wait_vmcnt<0>();
-    barrier_nofence();
-  }
-
-  // Output layout of a 32 x 32 block: lane holds column m = lane & 31 (activation row)
-  // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows).
-  // 16-bit outputs go through a wave-private LDS buffer of 32 rows x 64 columns (row
-  // pitch 136 B, so the 32 row writes of an instruction fall in distinct banks) and
-  // leave as whole 128-byte row segments, 16 B per lane.
-  const int mrow = wm * WTM + (lane & 31);        // tile-local row of this lane
-  const int ncol = wn * WTN + 4 * (lane >> 5);    // tile-local first column of this lane
-  const int64_t mn = (int64_t)g.m * g.n;
-  constexpr bool STAGED = OUT_DT != DT_F32;
-  constexpr int SPITCH = WTN * 2 + 8;
-  uint8_t* stg = lds + (DUAL ? 2 * C::STAGE : 0) + wave * 32 * SPITCH;
-
+      mma_half(f1);
 #pragma unroll
-  for (int mb = 0; mb < MBLK; ++mb) {
-    const int ml = mrow + mb * 32;
-    const int m = m0 + ml;
-    float sa0[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) sa0[p] = s_sa[p][ml];
-#pragma unroll
-    for (int nb = 0; nb < NBLK; ++nb) {
-      v16i t1 = v16i{};
-      if constexpr (DUAL) {
-#pragma unroll
-        for (int s1 = 0; s1 < 2; ++s1) {
-          if (s1 < steps1) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(s1, h, nb), afrag(s1, h, mb), t1, 0, 0, 0);
-          }
-        }
+      for (int i = 0; i < MBLK + NBLK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = ncol + nb * 32 + 8 * q;
-        const int n = n0 + nl;
-        const v4f sb0 = *reinterpret_cast<const v4f*>(&s_sb[0][nl]);
-        v4f sb1 = sb0;
-        if constexpr (DUAL) sb1 = *reinterpret_cast<const v4f*>(&s_sb[1][nl]);
-        float out[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int a0 = acc[mb][nb][4 * q + r];
-          if constexpr (BBITS == 4) a0 >>= 4;
-          const float t0 = sa0[0] * sb0[r];
-          float yv = (float)a0 * t0;
-          if constexpr (DUAL) {
-            int a1 = t1[4 * q + r];
-            if constexpr (BBITS == 4) a1 >>= 4;
-            const float tt = sa0[P - 1] * sb1[r];
-            const float y1 = (float)a1 * tt;
-            yv = yv + y1;
-            if (g.accd && m < g.m && n + r < g.n) g.accd[mn + (int64_t)m * g.n + n + r] = a1;
-          }
-          if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
-          out[r] = yv;
-        }
-        if constexpr (STAGED) {
-          typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
-          h_t hv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = (h_t)f32_fence(out[r]);
-          u2v w = {(unsigned)__builtin_bit_cast(unsigned short, hv[0]) | ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
-                   (unsigned)__builtin_bit_cast(unsigned short, hv[2]) | ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
-          *reinterpret_cast<u2v*>(stg + (lane & 31) * SPITCH + (nl - wn * WTN) * 2) = w;
-        } else {
-          if (m < g.m && n < g.n) store4<OUT_DT>(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
-        }
+      __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
+      slot = next;
+    }
+    // Last NST-1 steps: nothing left to load; fewer groups in flight each step.
+    for (; kt < nk; ++kt) {
+      const int next = slot + 1 == C::NST ? 0 : slot + 1;
+      load_half(slot, 1, f1);
+      mma_half(f0);
+      if (kt + 1 < nk) {
+        wait_loads(nk - 2 - kt);
+        barrier_nofence();
+        load_half(next, 0, f0);
+      }
+      mma_half(f1);
+      slot = next;
+    }
+
+    // ------------------------------------------------------------ epilogue
+    const int nvt = vt + (int)gridDim.x;
+    const bool has_next = nvt < T;
+    const int cm0 = m0, cn0 = n0;  // this tile
+    barrier_nofence();             // every wave is done with the ring
+    int steps1 = 0;
+    if constexpr (DUAL) {
+      // Outlier partition [k0, kp): at most two 64-code steps, staged in stages 0-1.
+      steps1 = (g.kp - g.k0) / BK;
+      issue(g.k0, 0);
+      if (steps1 > 1) issue(g.k0 + BK, 1);
+      wait_vmcnt<0>();
+      barrier_nofence();
+    } else {
+      if (has_next) {
+        set_tile(nvt);
+        load_scales();
+        issue_prologue();
       }
     }
-    if constexpr (STAGED) {
-      // 32 rows x 128 B: each lane stores 16 B, eight rows per instruction.
-      typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+
+    // Output layout of a 32 x 32 block: lane holds column m = lane & 31 (activation row)
+    // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows).
+    // 16-bit outputs pass through a wave-private LDS buffer, 16 rows at a time, and leave
+    // as whole 128-byte row segments, 16 B per lane.
+    const int mrow = wm * WTM + (lane & 31);
+    const int ncol = wn * WTN + 4 * (lane >> 5);
+    const int64_t mn = (int64_t)g.m * g.n;
+    uint8_t* stg = lds + C::NST * C::STAGE + wave * STG_WAVE;
+    typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 8 * i + (lane >> 3);
-        const int cc = 8 * (lane & 7);
-        const u4v w = *reinterpret_cast<const u4v*>(stg + rr * SPITCH + cc * 2);
-        const int mo = m0 + wm * WTM + mb * 32 + rr;
-        const int no = n0 + wn * WTN + cc;
-        if (mo < g.m && no < g.n) {
-          h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)mo * g.ldy + no;
-          if (g.vec_store && no + 8 <= g.n) {
-            *reinterpret_cast<u4v*>(dst) = w;
+    for (int mb = 0; mb < MBLK; ++mb) {
+      const int ml = mrow + mb * 32;
+      const int m = cm0 + ml;
+      float sa0[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) sa0[p] = s_sa[buf][p][ml];
+      u2v hw[NBLK][4];  // this lane's 16-bit outputs of the slice
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb) {
+        v16i t1 = v16i{};
+        if constexpr (DUAL) {
+#pragma unroll
+          for (int s1 = 0; s1 < 2; ++s1) {
+            if (s1 < steps1) {
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(s1, h, nb), afrag(s1, h, mb), t1, 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = ncol + nb * 32 + 8 * q;
+          const int n = cn0 + nl;
+          const v4f sb0 = *reinterpret_cast<const v4f*>(&s_sb[buf][0][nl]);
+          v4f sb1 = sb0;
+          if constexpr (DUAL) sb1 = *reinterpret_cast<const v4f*>(&s_sb[buf][1][nl]);
+          float out[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int a0 = acc[mb][nb][4 * q + r];
+            if constexpr (BBITS == 4) a0 >>= 4;
+            const float t0 = sa0[0] * sb0[r];
+            float yv = (float)a0 * t0;
+            if constexpr (DUAL) {
+              int a1 = t1[4 * q + r];
+              if constexpr (BBITS == 4) a1 >>= 4;
+              const float tt = sa0[P - 1] * sb1[r];
+              const float y1 = (float)a1 * tt;
+              yv = yv + y1;
+              if (g.accd && m < g.m && n + r < g.n) g.accd[mn + (int64_t)m * g.n + n + r] = a1;
+            }
+            if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
+            out[r] = yv;
+          }
+          if constexpr (STAGED) {
+            h_t hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = (h_t)f32_fence(out[r]);
+            hw[nb][q] = u2v{(unsigned)__builtin_bit_cast(unsigned short, hv[0]) |
+                                ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
+                            (unsigned)__builtin_bit_cast(unsigned short, hv[2]) |
+                                ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
           } else {
-            const unsigned short* hs = reinterpret_cast<const unsigned short*>(&w);
-            for (int e = 0; e < 8 && no + e < g.n; ++e) dst[e] = __builtin_bit_cast(h_t, hs[e]);
+            if (m < g.m && n < g.n) store4<OUT_DT>(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
+          }
+        }
+      }
+      if constexpr (STAGED) {
+#pragma unroll
+        for (int pass = 0; pass < 32 / SROWS; ++pass) {
+          // Rows pass*16 .. pass*16+15 of the slice: written by the lanes that hold them.
+          if ((lane & 31) / SROWS == pass) {
+#pragma unroll
+            for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u2v*>(stg + ((lane & 31) - pass * SROWS) * SPITCH +
+                                        (nb * 32 + 8 * q + 4 * (lane >> 5)) * 2) = hw[nb][q];
+          }
+          wave_lds_sync();
+          // 16 rows x 128 B: each lane stores 16 B, eight rows per instruction.
+          u4v w[SROWS / 8];
+#pragma unroll
+          for (int i = 0; i < SROWS / 8; ++i)
+            w[i] = *reinterpret_cast<const u4v*>(stg + (8 * i + (lane >> 3)) * SPITCH + 16 * (lane & 7));
+          wave_lds_sync();  // the staging rows are read before the next pass overwrites them
+#pragma unroll
+          for (int i = 0; i < SROWS / 8; ++i) {
+            const int rr = 8 * i + (lane >> 3);
+            const int cc = 8 * (lane & 7);
+            const int mo = cm0 + wm * WTM + mb * 32 + pass * SROWS + rr;
+            const int no = cn0 + wn * WTN + cc;
+            if (mo < g.m && no < g.n) {
+              h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)mo * g.ldy + no;
+              if (g.vec_store && no + 8 <= g.n) {
+                *reinterpret_cast<u4v*>(dst) = w[i];
+              } else {
+                for (int e = 0; e < 8 && no + e < g.n; ++e) {
+                  const unsigned d = e < 2 ? w[i].x : e < 4 ? w[i].y : e < 6 ? w[i].z : w[i].w;
+                  dst[e] = __builtin_bit_cast(h_t, (unsigned short)(d >> (16 * (e & 1))));
+                }
+              }
+            }
           }
         }
       }
     }
+
+    if (!has_next) break;
+    if constexpr (DUAL) {
+      barrier_nofence();  // stages 0-1 (outlier partition) are no longer read
+      set_tile(nvt);
+      load_scales();
+      issue_prologue();
+    }
+    store_scales(buf ^ 1);  // the next tile's epilogue reads them after several barriers
+    buf ^= 1;
+    vt = nvt;
   }
 }
 
@@ -476,6 +543,18 @@ namespace vq_internal {
 
 using namespace vqk;
 
+// One persistent workgroup per compute unit (each needs most of a CU's LDS).
+static int persistent_blocks() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    n = cus;
+  }
+  return n;
+}
+
 hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   GArgs a{};
   a.a = p.a;
@@ -493,7 +572,8 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.vec_store = ((reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 && p.ldy % 4 == 0) ? 1 : 0;
   a.tiles_m = (int)((p.m + BM - 1) / BM);
   a.tiles_n = (int)((p.n + BN - 1) / BN);
-  const int grid = a.tiles_m * a.tiles_n;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int grid = tiles < persistent_blocks() ? tiles : persistent_blocks();
   const bool dual = p.k0 < p.kp;
   if (p.b_bits == 8) return launch_out<8>(a, p.out_dt, dual, grid, st);
   return launch_out<4>(a, p.out_dt, dual, grid, st);
