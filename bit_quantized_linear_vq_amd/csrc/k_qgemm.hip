@@ -90,7 +90,7 @@ struct GArgs {
   int m, n, kp, k0;
   int64_t ldy;
   int sa_tok;
-  int vec_store;  // 4-wide stores are aligned (y 16-byte aligned, ldy % 4 == 0)
+  int vec_store;  // 16-byte stores are aligned (y 16-byte aligned, row pitch a multiple of 16 B)
   int tiles_m, tiles_n;
 };
 
@@ -105,29 +105,13 @@ __device__ __forceinline__ v4i unpack_int4x16(u2v w) {
   return r;
 }
 
-template <int OUT_DT>
-__device__ __forceinline__ void store4(void* y, int64_t off, const float v[4], int cnt, bool vec) {
-  if constexpr (OUT_DT == DT_F32) {
-    float* p = reinterpret_cast<float*>(y) + off;
-    if (vec && cnt == 4) {
-      v4f w = {v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<v4f*>(p) = w;
-    } else {
-      for (int i = 0; i < cnt; ++i) p[i] = v[i];
-    }
+// Four consecutive float32 outputs of one row (16 B when aligned and whole).
+__device__ __forceinline__ void store4_f32(void* y, int64_t off, const float v[4], int cnt, bool vec) {
+  float* p = reinterpret_cast<float*>(y) + off;
+  if (vec && cnt == 4) {
+    *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
   } else {
-    typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
-    h_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = (h_t)f32_fence(v[i]);
-    h_t* p = reinterpret_cast<h_t*>(y) + off;
-    if (vec && cnt == 4) {
-      u2v w = {(unsigned)__builtin_bit_cast(unsigned short, h[0]) | ((unsigned)__builtin_bit_cast(unsigned short, h[1]) << 16),
-               (unsigned)__builtin_bit_cast(unsigned short, h[2]) | ((unsigned)__builtin_bit_cast(unsigned short, h[3]) << 16)};
-      *reinterpret_cast<u2v*>(p) = w;
-    } else {
-      for (int i = 0; i < cnt; ++i) p[i] = h[i];
-    }
+    for (int i = 0; i < cnt; ++i) p[i] = v[i];
   }
 }
 
@@ -149,11 +133,8 @@ template <int BBITS, int OUT_DT, bool DUAL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm(GArgs g) {
   using C = GCfg<BBITS>;
   constexpr int P = DUAL ? 2 : 1;
-  constexpr bool STAGED = OUT_DT != DT_F32;
-  constexpr int SPITCH = WTN * 2 + 8;  // staging row pitch: 32 row writes hit distinct banks
-  constexpr int SROWS = 16;            // staging rows per pass
-  constexpr int STG_WAVE = SROWS * SPITCH;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE + 8 * STG_WAVE];
+  constexpr bool HALF_OUT = OUT_DT != DT_F32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
   __shared__ float s_sa[2][P][BM];
   __shared__ float s_sb[2][P][BN];
 
@@ -397,13 +378,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
 
     // Output layout of a 32 x 32 block: lane holds column m = lane & 31 (activation row)
-    // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows).
-    // 16-bit outputs pass through a wave-private LDS buffer, 16 rows at a time, and leave
-    // as whole 128-byte row segments, 16 B per lane.
+    // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows).  16-bit
+    // outputs leave straight from registers, 16 B per lane (32 contiguous bytes per row
+    // and instruction); a detour through LDS for full-row stores measured slower.
     const int mrow = wm * WTM + (lane & 31);
     const int ncol = wn * WTN + 4 * (lane >> 5);
     const int64_t mn = (int64_t)g.m * g.n;
-    uint8_t* stg = lds + C::NST * C::STAGE + wave * STG_WAVE;
     typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
 
 #pragma unroll
@@ -413,7 +393,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       float sa0[P];
 #pragma unroll
       for (int p = 0; p < P; ++p) sa0[p] = s_sa[buf][p][ml];
-      u2v hw[NBLK][4];  // this lane's 16-bit outputs of the slice
 #pragma unroll
       for (int nb = 0; nb < NBLK; ++nb) {
         v16i t1 = v16i{};
@@ -427,6 +406,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             }
           }
         }
+        u2v hw[4];  // 16-bit outputs of group q: columns 8q + 4 * (lane >> 5) + 0..3
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nl = ncol + nb * 32 + 8 * q;
@@ -452,51 +432,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
             out[r] = yv;
           }
-          if constexpr (STAGED) {
+          if constexpr (HALF_OUT) {
             h_t hv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) hv[r] = (h_t)f32_fence(out[r]);
-            hw[nb][q] = u2v{(unsigned)__builtin_bit_cast(unsigned short, hv[0]) |
-                                ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
-                            (unsigned)__builtin_bit_cast(unsigned short, hv[2]) |
-                                ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
+            hw[q] = u2v{(unsigned)__builtin_bit_cast(unsigned short, hv[0]) |
+                            ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
+                        (unsigned)__builtin_bit_cast(unsigned short, hv[2]) |
+                            ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
           } else {
-            if (m < g.m && n < g.n) store4<OUT_DT>(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
+            if (m < g.m && n < g.n) store4_f32(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
           }
         }
-      }
-      if constexpr (STAGED) {
+        if constexpr (HALF_OUT) {
+          // Groups (q, q+1) of the two half-waves are exchanged so that each lane holds eight
+          // consecutive columns: lanes 0-31 columns 16pr + 0..7, lanes 32-63 16pr + 8..15.
 #pragma unroll
-        for (int pass = 0; pass < 32 / SROWS; ++pass) {
-          // Rows pass*16 .. pass*16+15 of the slice: written by the lanes that hold them.
-          if ((lane & 31) / SROWS == pass) {
-#pragma unroll
-            for (int nb = 0; nb < NBLK; ++nb)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u2v*>(stg + ((lane & 31) - pass * SROWS) * SPITCH +
-                                        (nb * 32 + 8 * q + 4 * (lane >> 5)) * 2) = hw[nb][q];
-          }
-          wave_lds_sync();
-          // 16 rows x 128 B: each lane stores 16 B, eight rows per instruction.
-          u4v w[SROWS / 8];
-#pragma unroll
-          for (int i = 0; i < SROWS / 8; ++i)
-            w[i] = *reinterpret_cast<const u4v*>(stg + (8 * i + (lane >> 3)) * SPITCH + 16 * (lane & 7));
-          wave_lds_sync();  // the staging rows are read before the next pass overwrites them
-#pragma unroll
-          for (int i = 0; i < SROWS / 8; ++i) {
-            const int rr = 8 * i + (lane >> 3);
-            const int cc = 8 * (lane & 7);
-            const int mo = cm0 + wm * WTM + mb * 32 + pass * SROWS + rr;
-            const int no = cn0 + wn * WTN + cc;
-            if (mo < g.m && no < g.n) {
-              h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)mo * g.ldy + no;
+          for (int pr = 0; pr < 2; ++pr) {
+            const u2v X = hw[2 * pr], Y = hw[2 * pr + 1];
+            const auto s0 = __builtin_amdgcn_permlane32_swap(X.x, Y.x, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(X.y, Y.y, false, false);
+            const u4v w = {s0[0], s1[0], s0[1], s1[1]};
+            const int no = cn0 + wn * WTN + nb * 32 + 16 * pr + 8 * (lane >> 5);
+            if (m < g.m && no < g.n) {
+              h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + no;
               if (g.vec_store && no + 8 <= g.n) {
-                *reinterpret_cast<u4v*>(dst) = w[i];
+                *reinterpret_cast<u4v*>(dst) = w;
               } else {
                 for (int e = 0; e < 8 && no + e < g.n; ++e) {
-                  const unsigned d = e < 2 ? w[i].x : e < 4 ? w[i].y : e < 6 ? w[i].z : w[i].w;
+                  const unsigned d = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
                   dst[e] = __builtin_bit_cast(h_t, (unsigned short)(d >> (16 * (e & 1))));
                 }
               }
@@ -569,7 +533,8 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.k0 = (int)p.k0;
   a.ldy = p.ldy;
   a.sa_tok = p.sa_per_token;
-  a.vec_store = ((reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 && p.ldy % 4 == 0) ? 1 : 0;
+  const int64_t esize = p.out_dt == DT_F32 ? 4 : 2;
+  a.vec_store = ((reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 && (p.ldy * esize) % 16 == 0) ? 1 : 0;
   a.tiles_m = (int)((p.m + BM - 1) / BM);
   a.tiles_n = (int)((p.n + BN - 1) / BN);
   const int tiles = a.tiles_m * a.tiles_n;
