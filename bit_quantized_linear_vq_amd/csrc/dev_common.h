@@ -25,16 +25,6 @@ __device__ __forceinline__ float f32_fence(float v) {
 }
 __device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
 
-// Separates the LDS accesses of one wave before and after an exchange between its lanes.
-// A wave's LDS instructions execute in order, so no wait is needed; the fences keep the
-// compiler from moving LDS accesses across this point or reusing a value loaded before it
-// (without them, a lane that wrote nothing in between may be given its earlier load).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Two packed 16-bit values of a dword -> floats (element 2i in the low half).
 template <int DT>
 __device__ __forceinline__ void decode2(unsigned u, float& lo, float& hi) {

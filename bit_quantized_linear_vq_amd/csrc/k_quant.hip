@@ -64,7 +64,7 @@ __device__ __forceinline__ void static_scale(float sgiven, float& r, float& s) {
   if (!(sgiven != 0.0f) || __builtin_isinf(r)) r = 0.0f;
 }
 
-template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
+template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY, int NP>
 __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   __shared__ float s_red[8][2];
   __shared__ unsigned s_mask[DUAL ? MAX_MASK_WORDS : 1];
@@ -79,16 +79,27 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   const float sigma = HAD ? had_sigma(perm8(lane & 7)) : 1.0f;
   const float qf = qmax_f(a);
 
+  // Outlier channels gathered by this lane (the same for every row).
+  int oidx[2] = {0, 0};
   if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i < a.n_out) oidx[i] = a.idx[lane + 64 * i];
+  }
+  // Bit mask of the outlier channels in LDS, built once the first row's loads are in
+  // flight (the index loads above are then the only ones it waits for).
+  bool mask_ready = !DUAL;
+  auto build_mask = [&]() {
     const int words = (a.k + 31) >> 5;
     for (int i = threadIdx.x; i < words; i += blockDim.x) s_mask[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < a.n_out; i += blockDim.x) {
-      const int c = a.idx[i];
-      atomicOr(&s_mask[c >> 5], 1u << (c & 31));
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (lane + 64 * i < a.n_out) atomicOr(&s_mask[oidx[i] >> 5], 1u << (oidx[i] & 31));
     }
     __syncthreads();
-  }
+  };
 
   // Scales common to the whole tensor.
   float r_g[2] = {0.0f, 0.0f}, s_g[2] = {0.0f, 0.0f};
@@ -105,20 +116,30 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
     const bool row_ok = row < a.rows;
     const char* xrow = reinterpret_cast<const char*>(a.x) + (row_ok ? row : 0) * a.ldx * (DT == DT_F32 ? 4 : 2);
 
-    float v[NPMAX][16];
+    float v[NP][16];
     float lmax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NPMAX; ++j) {
+    for (int j = 0; j < NP; ++j) {
       const int e = (wr + a.W * j) * 1024 + 16 * slot;
-      const bool act = j < a.np && row_ok && e < a.k;
-      if (act) {
+      if (row_ok && e < a.k) {
         load16<DT>(xrow + (int64_t)e * (DT == DT_F32 ? 4 : 2), v[j]);
       } else {
 #pragma unroll
         for (int t = 0; t < 16; ++t) v[j][t] = 0.0f;
       }
+    }
+    if constexpr (DUAL) {
+      if (!mask_ready) {  // block-uniform: every thread of the block runs the same rows loop
+        build_mask();
+        mask_ready = true;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int e = (wr + a.W * j) * 1024 + 16 * slot;
+      const bool act = row_ok && e < a.k;
       if constexpr (HAD) {
-        if (j < a.np) fwht128(v[j], perm8(lane & 7));
+        fwht128(v[j], perm8(lane & 7));
       }
       if constexpr (DUAL) {
         if (act) {
@@ -142,7 +163,7 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int jj = lane + 64 * i;
-          if (row_ok && jj < a.n_out) ov[i] = load1<DT>(xrow, a.idx[jj]);
+          if (row_ok && jj < a.n_out) ov[i] = load1<DT>(xrow, oidx[i]);
           omax = fmaxf(omax, fabsf(ov[i]));
         }
         omax = wave_max(omax);
@@ -181,9 +202,9 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
 
     if (row_ok) {
 #pragma unroll
-      for (int j = 0; j < NPMAX; ++j) {
+      for (int j = 0; j < NP; ++j) {
         const int e = (wr + a.W * j) * 1024 + 16 * slot;
-        if (j < a.np && e < a.k) {
+        if (e < a.k) {
           unsigned u[16];
 #pragma unroll
           for (int t = 0; t < 16; ++t) u[t] = qbyte(v[j][t], rr, qf);
@@ -279,7 +300,13 @@ __global__ void k_tensor_finalize(float* scales, const float* static_src, int pa
 
 template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
 static hipError_t launch_row(const RowArgs& a, int grid, int block, hipStream_t st) {
-  hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY>), dim3(grid), dim3(block), 0, st, a);
+  // The pass count is a compile-time constant so that a lane holds exactly its passes.
+  switch (a.np) {
+    case 1: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 1>), dim3(grid), dim3(block), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 2>), dim3(grid), dim3(block), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 3>), dim3(grid), dim3(block), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, NPMAX>), dim3(grid), dim3(block), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
