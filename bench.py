@@ -223,7 +223,10 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    # Per-kernel durations: HIP events around every launch on the launch stream.
+    # Per-kernel durations: HIP events around every launch on the launch stream.  One
+    # untimed step is queued first so that the GPU is busy while the host enqueues the
+    # bracketed launches (otherwise the first interval holds the host's launch latency).
+    step(0)
     evs = []
     for i in range(args.steps):
         for l in range(L.layers):
