@@ -22,5 +22,7 @@ Steps and the passages they follow:
 * ``route``     relative-L1 routing statistic Gamma and the INT8-vs-4-bit decision
                 (6Bit-Diffusion page, Key Insights 1 and Methodology B.1, DMPQ).
 * ``linear``    the whole layer, chaining the steps above.
+* ``decompose`` residual re-quantization of selected tokens, added back through a
+                second accumulator (SemanticDialect page, Methodology 2.2).
 """
-from . import numerics, detect, quantizer, fwht, gemm, route, linear  # noqa: F401
+from . import numerics, detect, quantizer, fwht, gemm, route, linear, decompose  # noqa: F401
