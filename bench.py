@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--residual-frac", type=float, default=0.0, metavar="F",
+                   help="decompose a seeded fraction F of the tokens (residual re-quantization added back "
+                        "in the epilogue); per-token workloads without dual scale or rotation only")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times) and exit; "
                         "rocprofv3 counters of that copy scale FETCH_SIZE/WRITE_SIZE to bytes")
@@ -76,7 +79,7 @@ def load_traffic(workload):
 class Layer:
     """Device buffers and launch closures for one configuration."""
 
-    def __init__(self, cfg, vq, gen, torch, dev):
+    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0):
         c = gen.CONFIGS[cfg]
         self.cfg, self.c = cfg, c
         self.M, self.K, self.N = c["M"], c["K"], c["N"]
@@ -119,23 +122,48 @@ class Layer:
             self.scales = torch.empty((2 if n_out else 1,), dtype=torch.float32, device=dev)
         self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16 if c["dtype"] == "bf16" else torch.float16,
                              device=dev)
+        # Activation decomposition of a seeded set of tokens.
+        self.R = int(round(residual_frac * self.M))
+        if self.R:
+            if self.gran != "token" or n_out or self.had or cfg == 5:
+                raise SystemExit("--residual-frac needs a per-token workload without dual scale or rotation")
+            import numpy as np
+            rows = np.sort(np.random.default_rng(1000 * cfg + 20).choice(self.M, self.R, replace=False))
+            self.rows = torch.from_numpy(rows.astype(np.int32)).to(dev)
+            self.codes2 = torch.empty((self.R, self.K), dtype=torch.int8, device=dev)
+            self.scales2 = torch.empty((self.R,), dtype=torch.float32, device=dev)
+            self.ws = torch.empty(vq.vq_residual_workspace_bytes(self.M, self.R, self.N), dtype=torch.uint8,
+                                  device=dev)
         torch.cuda.synchronize()
 
     def quant(self, step, layer):
-        self.vq.vq_quant_act(self.x[step % len(self.x)], self.a_bits, self.gran, self.had, self.idx,
+        x = self.x[step % len(self.x)]
+        self.vq.vq_quant_act(x, self.a_bits, self.gran, self.had, self.idx,
                              bits_dev=self.bits_dev[layer], codes=self.codes, scales=self.scales)
+        if self.R:
+            self.vq.vq_quant_residual(x, self.rows, self.a_bits, self.a_bits, self.codes2, self.scales2)
 
     def gemm(self, layer):
         wc, ws = self.w[layer]
+        if self.R:
+            self.vq.vq_qgemm_dequant_residual(self.codes, self.scales, wc, ws, self.c["w_bits"], self.codes2,
+                                              self.scales2, self.rows, self.y.dtype, y=self.y, ws=self.ws)
+            return
         self.vq.vq_qgemm_dequant(self.codes, self.scales, wc, ws, self.c["w_bits"], self.k0, self.y.dtype,
                                  self.gran == "token", y=self.y)
 
     def ops_per_step(self):
         return 2.0 * self.M * self.N * self.K * self.layers
 
+    def gemm_ops(self):
+        # integer operations the GEMM phase executes: the layer plus the residual rows' product
+        return 2.0 * (self.M + self.R) * self.N * self.K
+
     def quant_bytes(self):
-        # read 2 B per input element, write 1 B per code (padding included), 4 B per scale
-        return self.M * self.K * 2 + self.M * self.kp + self.scales.numel() * 4
+        # read 2 B per input element, write 1 B per code (padding included), 4 B per scale;
+        # decomposed rows read their input once more and write K residual codes and a scale
+        return (self.M * self.K * 2 + self.M * self.kp + self.scales.numel() * 4
+                + self.R * (self.K * 2 + self.K + 4))
 
 
 def cpu_baseline(cfg, budget_s):
@@ -175,7 +203,7 @@ def cpu_baseline(cfg, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "one GPU only: runs on more than one GPU are not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
@@ -194,7 +222,7 @@ def main():
     import gen
 
     dev = torch.device("cuda:0")
-    L = Layer(args.config, vq, gen, torch, dev)
+    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
@@ -241,12 +269,14 @@ def main():
     q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
     g_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
 
-    ops_layer = 2.0 * L.M * L.N * L.K
-    gemm_tops = ops_layer / (g_ms * 1e-3) / 1e12
+    gemm_tops = L.gemm_ops() / (g_ms * 1e-3) / 1e12
     quant_gbs = L.quant_bytes() / (q_ms * 1e-3) / 1e9
     tops = L.ops_per_step() / (ms * 1e-3) / 1e12
     workload = gen.CONFIGS[args.config]["name"]
     traffic, q_traffic = load_traffic(workload)
+    if L.R:
+        workload += f"+decompose_{L.R}_tokens"
+        traffic = q_traffic = None  # the counter runs cover the plain layer only
 
     out = {
         "metric": "quantized-linear TOPS (int8 MFMA %peak) + act-quant GB/s (%HBM), 1 MI355X",
@@ -273,6 +303,10 @@ def main():
                       "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "bytes": L.quant_bytes(),
                       "avg_us": round(q_ms * 1e3, 2), "kernel": "k_rowquant", "traffic": q_traffic},
     }
+    if L.R:
+        out["config"]["decomposed_tokens"] = L.R
+        out["roofline"]["kernel"] = "slot map + residual-row GEMM + k_qgemm with residual epilogue"
+        out["act_quant"]["kernel"] = "k_rowquant + k_residual_quant"
     if args.config == 5:
         out["config"]["routes_int8"] = L.routes.count(8)
         out["config"]["routes_int4"] = L.routes.count(4)

@@ -26,7 +26,8 @@ VQ_MAX_OUTLIERS = 128
 EXPORTS = (
     "vq_outlier_part_len", "vq_packed_k", "vq_detect_workspace_elems", "vq_detect_outliers",
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant",
-    "vq_route_workspace_elems", "vq_route_rel_l1", "vq_status_string", "vq_last_hip_error", "vq_version",
+    "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
+    "vq_qgemm_dequant_residual", "vq_status_string", "vq_last_hip_error", "vq_version",
 )
 
 _DT = {torch.float16: VQ_F16, torch.bfloat16: VQ_BF16, torch.float32: VQ_F32}
@@ -57,6 +58,9 @@ def _load():
         "vq_qgemm_dequant": (I, [P, P, I, P, I, P, I64, I64, I64, I64, P, I, I64, P, P]),
         "vq_route_workspace_elems": (I64, [I64]),
         "vq_route_rel_l1": (I, [P, P, I, I64, D, I, I, P, P, P, P]),
+        "vq_quant_residual": (I, [P, I, I64, I64, I64, I, I, P, I64, P, P, P]),
+        "vq_residual_workspace_bytes": (I64, [I64, I64, I64]),
+        "vq_qgemm_dequant_residual": (I, [P, P, P, I, P, I64, I64, I64, P, P, P, I64, P, I, I64, P, P]),
         "vq_status_string": (ctypes.c_char_p, [I]),
         "vq_last_hip_error": (I, []),
         "vq_version": (ctypes.c_char_p, []),
@@ -202,3 +206,41 @@ def vq_route_rel_l1(x: torch.Tensor, y: torch.Tensor, threshold: float = 0.1, bi
 
 def vq_version() -> str:
     return _lib.vq_version().decode()
+
+
+def vq_quant_residual(x: torch.Tensor, rows: torch.Tensor, bits1: int, bits2: int, codes=None, scales=None):
+    """Decomposition operand of the listed rows.  Returns (codes int8 [2R x K], scales f32 [2R]):
+    rows 0..R-1 hold the first quantizer's codes of the listed rows, rows R..2R-1 their residual codes."""
+    _dev(x, "x")
+    m, k = x.shape
+    n_rows = int(rows.numel())
+    if codes is None:
+        codes = torch.empty((2 * n_rows, k), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((2 * n_rows,), dtype=torch.float32, device=x.device)
+    _check("vq_quant_residual", _lib.vq_quant_residual(
+        _ptr(x), _DT.get(x.dtype, -1), m, k, x.stride(0), bits1, bits2, _ptr(rows), n_rows,
+        _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def vq_residual_workspace_bytes(m: int, n_rows: int, n: int) -> int:
+    return int(_lib.vq_residual_workspace_bytes(m, n_rows, n))
+
+
+def vq_qgemm_dequant_residual(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor, b_bits: int,
+                              a2: torch.Tensor, sa2: torch.Tensor, rows: torch.Tensor,
+                              out_dtype=torch.bfloat16, y=None, ws=None):
+    """Y = dequant(A . B^T); listed rows get both terms of the stacked operand (a2, sa2) added before rounding."""
+    _dev(a, "a")
+    m, kp = a.shape
+    n = b.shape[0]
+    n_rows = int(rows.numel())
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if ws is None and n_rows:
+        ws = torch.empty(vq_residual_workspace_bytes(m, n_rows, n), dtype=torch.uint8, device=a.device)
+    _check("vq_qgemm_dequant_residual", _lib.vq_qgemm_dequant_residual(
+        _ptr(a), _ptr(sa), _ptr(b), b_bits, _ptr(sb), m, n, kp, _ptr(a2), _ptr(sa2), _ptr(rows), n_rows,
+        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(ws), _stream(a)))
+    return y

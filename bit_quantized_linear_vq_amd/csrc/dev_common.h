@@ -163,6 +163,17 @@ __device__ __forceinline__ unsigned qbyte(float x, float r, float qf) {
   return f_bits(t + 12582912.0f);
 }
 
+// r and s of a dynamic group with absolute maximum amax (a = 0 or an overflowing
+// reciprocal give r = s = 0, so every code is 0).
+__device__ __forceinline__ void dyn_scale(float amax, float qf, float& r, float& s) {
+  r = qf / amax;
+  s = amax / qf;
+  if (!(amax > 0.0f) || __builtin_isinf(r)) {
+    r = 0.0f;
+    s = 0.0f;
+  }
+}
+
 // Low bytes of four dwords -> one dword (byte i from u_i).
 __device__ __forceinline__ unsigned pack4_lo(unsigned u0, unsigned u1, unsigned u2, unsigned u3) {
   unsigned lo = __builtin_amdgcn_perm(u1, u0, 0x0c0c0400u);

@@ -47,17 +47,6 @@ __device__ __forceinline__ float qmax_f(const RowArgs& a) {
   return (float)((1 << (b - 1)) - 1);
 }
 
-// r and s of a dynamic group with absolute maximum amax (a = 0 or an overflowing
-// reciprocal give r = s = 0, so every code is 0).
-__device__ __forceinline__ void dyn_scale(float amax, float qf, float& r, float& s) {
-  r = qf / amax;
-  s = amax / qf;
-  if (!(amax > 0.0f) || __builtin_isinf(r)) {
-    r = 0.0f;
-    s = 0.0f;
-  }
-}
-
 __device__ __forceinline__ void static_scale(float sgiven, float& r, float& s) {
   s = sgiven;
   r = 1.0f / sgiven;

@@ -261,6 +261,53 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
   return hip_status(vq_internal::launch_qgemm(p, stream));
 }
 
+// ------------------------------------------------------------------ decomposition
+
+namespace {
+bool ok_bits(int b) { return b == 4 || b == 6 || b == 8; }
+}  // namespace
+
+int64_t vq_residual_workspace_bytes(int64_t m, int64_t n_rows, int64_t n) {
+  if (m < 1 || n_rows < 0 || n < 1 || m >= kMaxDim || n >= kMaxDim || n_rows > m) return 0;
+  return 8 * n_rows * n;  // float32 [2 * n_rows x n]: the two terms of every listed row
+}
+
+vq_status vq_quant_residual(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t ldx, int bits1, int bits2,
+                            const int32_t* rows_dev, int64_t n_rows, int8_t* codes, float* scales,
+                            hipStream_t stream) {
+  if (!x) return VQ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (!rows_dev || !codes || !scales)) return VQ_ERR_INVALID_ARG;
+  if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
+  if (m < 1 || k < 1 || m >= kMaxDim || k >= kMaxDim || ldx < k || n_rows < 0 || n_rows > m)
+    return VQ_ERR_INVALID_ARG;
+  if (!ok_bits(bits1) || !ok_bits(bits2)) return VQ_ERR_UNSUPPORTED;
+  if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
+  if (!aligned16(x) || ldx % 8 || (n_rows > 0 && reinterpret_cast<uintptr_t>(codes) % 8)) return VQ_ERR_SHAPE;
+  if (n_rows == 0) return VQ_OK;
+  return hip_status(vq_internal::launch_residual_quant(x, (int)dt, ldx, m, k, rows_dev, n_rows, bits1, bits2, codes,
+                                                       scales, stream));
+}
+
+vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void* b, int b_bits, const float* sb,
+                                    int64_t m, int64_t n, int64_t kp, const int8_t* a2, const float* sa2,
+                                    const int32_t* rows_dev, int64_t n_rows, void* y, vq_dtype out_dt, int64_t ldy,
+                                    void* ws, hipStream_t stream) {
+  if (n_rows < 0 || n_rows > m) return VQ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (!a2 || !sa2 || !rows_dev || !ws)) return VQ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (2 * n_rows >= kMaxDim || (n >= 1 && n_rows * ((n + 1023) / 1024) >= kMaxDim)))
+    return VQ_ERR_UNSUPPORTED;
+  if (n_rows > 0 && (!aligned16(a2) || !aligned16(ws))) return VQ_ERR_SHAPE;
+  // Every row as without decomposition (this also validates a, sa, b, sb, y and the sizes).
+  vq_status st = vq_qgemm_dequant(a, sa, 1, b, b_bits, sb, m, n, kp, kp, y, out_dt, ldy, nullptr, stream);
+  if (st != VQ_OK || n_rows == 0) return st;
+  // Both terms of every listed row in float32: y12 = fl32(acc * fl32(s * sw)) over the
+  // stacked operand [q1 rows; q2 rows].
+  float* y12 = reinterpret_cast<float*>(ws);
+  st = vq_qgemm_dequant(a2, sa2, 1, b, b_bits, sb, 2 * n_rows, n, kp, kp, y12, VQ_F32, n, nullptr, stream);
+  if (st != VQ_OK) return st;
+  return hip_status(vq_internal::launch_residual_merge(y12, n_rows, n, rows_dev, m, y, (int)out_dt, ldy, stream));
+}
+
 // ------------------------------------------------------------------ routing
 
 int64_t vq_route_workspace_elems(int64_t n) { return n < 1 ? 0 : 2 * (int64_t)vq_internal::route_blocks(); }

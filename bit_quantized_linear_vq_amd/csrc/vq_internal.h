@@ -52,6 +52,12 @@ struct GemmParams {
 };
 hipError_t launch_qgemm(const GemmParams& g, hipStream_t st);
 
+hipError_t launch_residual_quant(const void* x, int dtype, int64_t ldx, int64_t m, int64_t k, const int32_t* rows,
+                                 int64_t n_rows, int bits1, int bits2, int8_t* codes2, float* scales2,
+                                 hipStream_t st);
+hipError_t launch_residual_merge(const float* y12, int64_t n_rows, int64_t n, const int32_t* rows, int64_t m, void* y,
+                                 int out_dt, int64_t ldy, hipStream_t st);
+
 int detect_row_chunks(int64_t rows);
 hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, double* ws,
                            hipStream_t st);

@@ -31,7 +31,8 @@
  * Sources: Q-ARVD (aitrends.kr article, "Q-ARVD: quantization of autoregressive video
  * diffusion models"), sections Methodology and Technical details; 6Bit-Diffusion
  * (gist.science summary of arXiv 2603.18742), Key Insights 1 and Methodology B.1 (DMPQ);
- * S2Q-VDiT (gist.science summary of arXiv 2508.04016), the W4A6 setting.
+ * S2Q-VDiT (gist.science summary of arXiv 2508.04016), the W4A6 setting; SemanticDialect
+ * (gist.science summary of arXiv 2603.02883), Methodology 2.2 (activation decomposition).
  */
 #ifndef VQ_H
 #define VQ_H
@@ -162,7 +163,8 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
  *   sb       device float [n] or [n x 2]
  *   kp, k0   kp % 64 == 0, k0 % 64 == 0, 0 < k0 <= kp, kp - k0 <= 128
  *   y        device out_dt in {F16, BF16, F32}, [m x n], row stride ldy (element aligned;
- *            a 16-byte aligned y with ldy % 4 == 0 takes the vector-store path)
+ *            a 16-byte aligned y whose row pitch is a multiple of 16 bytes takes the
+ *            vector-store path)
  *   acc_debug device int32 [P x m x n] or NULL: receives the raw accumulators
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8, out_dt).
  */
@@ -170,6 +172,52 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
                            int b_bits, const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0,
                            void* y, vq_dtype out_dt, int64_t ldy, int32_t* acc_debug,
                            hipStream_t stream);
+
+/*
+ * Activation decomposition (SemanticDialect, gist.science summary of arXiv 2603.02883,
+ * Methodology 2.2: the quantization error of the activation is quantized again and its
+ * contribution added to the output, for selected tokens only).  For each listed row
+ * x = rows_dev[i]: (q1, s1) = the per-token quantizer with bits1 (exactly the codes and
+ * scale of vq_quant_act with VQ_PER_TOKEN, no rotation, no dual scale); deq =
+ * fl32(q1 * s1); residual r = fl32(x - deq); (q2, s2) = the per-token quantizer of r with
+ * bits2.  The output is a stacked operand of 2 * n_rows rows:
+ *   codes  device int8 [2 n_rows x k] (8-byte aligned): row i = q1 of listed row i,
+ *          row n_rows + i = its q2
+ *   scales device float [2 n_rows]: s1 of listed row i, then s2
+ *   x      device, dt in {F16, BF16}, [m x k], stride ldx; 16-byte aligned, ldx % 8 == 0
+ *   rows_dev  device int32 [n_rows]: distinct rows of x (the salient tokens, chosen by
+ *          the caller); an index outside [0, m) yields zero codes and scales
+ * n_rows = 0 enqueues nothing.  Errors: INVALID_ARG, SHAPE (k % 64, alignment),
+ * UNSUPPORTED (bits not 4/6/8).
+ */
+vq_status vq_quant_residual(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t ldx, int bits1,
+                            int bits2, const int32_t* rows_dev, int64_t n_rows, int8_t* codes,
+                            float* scales, hipStream_t stream);
+
+/*
+ * GEMM with the decomposed rows added back (same passage).  Every row i first gets
+ * vq_qgemm_dequant's output (single partition, per-token scales):
+ *   y1 = fl32(fl32(acc1[i,j]) * fl32(sa[i] * sb[j])),  acc1 = a . b,  rounded to out_dt;
+ * then every listed row i = rows_dev[t] is rewritten as
+ *   y = RNE_out(fl32(y1 + y2)),  y2 = fl32(fl32(acc2[t,j]) * fl32(s2[t] * sb[j])),
+ * with acc1 and acc2 taken from the stacked operand of vq_quant_residual (one small GEMM
+ * over its 2 n_rows rows, float32 results in ws, then a merge kernel).
+ *   a, sa     the per-token codes [m x kp] and scales [m] of vq_quant_act (kp % 64 == 0)
+ *   b, sb     packed weights as for vq_qgemm_dequant (b_bits 8 or 4), scales [n]
+ *   a2, sa2   the stacked codes [2 n_rows x kp] and scales [2 n_rows] of vq_quant_residual
+ *   rows_dev  device int32 [n_rows], distinct, the same list as for vq_quant_residual
+ *   y         as for vq_qgemm_dequant
+ *   ws        device scratch, 16-byte aligned, vq_residual_workspace_bytes(m, n_rows, n)
+ *             bytes (float32 [2 n_rows x n]); contents not kept
+ * Launches on `stream`: the GEMM of all rows, the GEMM of the stacked rows, the merge.
+ * n_rows = 0 is vq_qgemm_dequant.  Errors: INVALID_ARG, SHAPE, UNSUPPORTED as for
+ * vq_qgemm_dequant, plus UNSUPPORTED when 2 n_rows does not fit the launch grid.
+ */
+int64_t vq_residual_workspace_bytes(int64_t m, int64_t n_rows, int64_t n);
+vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void* b, int b_bits,
+                                    const float* sb, int64_t m, int64_t n, int64_t kp, const int8_t* a2,
+                                    const float* sa2, const int32_t* rows_dev, int64_t n_rows, void* y,
+                                    vq_dtype out_dt, int64_t ldy, void* ws, hipStream_t stream);
 
 /*
  * DMPQ routing on the device (6Bit-Diffusion, Key Insights 1 and Methodology B.1):

@@ -193,3 +193,71 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     assert st == HIP
     assert lib.vq_last_hip_error() != 0
     assert gemm(lib) == HIP
+
+
+def test_decomposition_workspace_size(lib):
+    # float32 [2 n_rows x n]: both terms of every listed row.
+    assert lib.vq_residual_workspace_bytes(17776, 0, 5760) == 0
+    assert lib.vq_residual_workspace_bytes(17776, 889, 5760) == 8 * 889 * 5760
+    assert lib.vq_residual_workspace_bytes(10, 3, 7) == 168
+    assert lib.vq_residual_workspace_bytes(0, 0, 8) == 0
+    assert lib.vq_residual_workspace_bytes(8, 9, 8) == 0  # more rows listed than exist
+
+
+def resid(lib, **kw):
+    a = dict(x=FAKE, dt=BF16, m=64, k=1920, ldx=1920, bits1=8, bits2=8, rows=FAKE, n_rows=4, codes=FAKE,
+             scales=FAKE, stream=NULL)
+    a.update(kw)
+    return lib.vq_quant_residual(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["bits1"], a["bits2"], a["rows"],
+                                 a["n_rows"], a["codes"], a["scales"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=NULL), INVALID),
+    (dict(rows=NULL), INVALID),
+    (dict(codes=NULL), INVALID),
+    (dict(scales=NULL), INVALID),
+    (dict(dt=F32), INVALID),
+    (dict(m=0), INVALID),
+    (dict(ldx=1000), INVALID),
+    (dict(n_rows=-1), INVALID),
+    (dict(n_rows=65), INVALID),
+    (dict(bits1=5), UNSUP),
+    (dict(bits2=2), UNSUP),
+    (dict(k=1000, ldx=1000), SHAPE),
+    (dict(ldx=1924), SHAPE),
+    (dict(x=ctypes.c_void_p(0x10008)), SHAPE),
+    (dict(codes=ctypes.c_void_p(0x10004)), SHAPE),
+    (dict(n_rows=0, rows=NULL, codes=NULL, scales=NULL), OK),  # nothing to do, nothing enqueued
+])
+def test_quant_residual_validation(lib, kw, want):
+    assert resid(lib, **kw) == want
+
+
+def gemm_res(lib, **kw):
+    a = dict(a=FAKE, sa=FAKE, b=FAKE, bits=8, sb=FAKE, m=256, n=512, kp=512, a2=FAKE, sa2=FAKE, rows=FAKE,
+             n_rows=3, y=FAKE, out=BF16, ldy=512, ws=FAKE, stream=NULL)
+    a.update(kw)
+    return lib.vq_qgemm_dequant_residual(a["a"], a["sa"], a["b"], a["bits"], a["sb"], a["m"], a["n"], a["kp"],
+                                         a["a2"], a["sa2"], a["rows"], a["n_rows"], a["y"], a["out"], a["ldy"],
+                                         a["ws"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n_rows=-1), INVALID),
+    (dict(n_rows=257), INVALID),
+    (dict(a2=NULL), INVALID),
+    (dict(sa2=NULL), INVALID),
+    (dict(rows=NULL), INVALID),
+    (dict(ws=NULL), INVALID),
+    (dict(a=NULL), INVALID),
+    (dict(out=9), INVALID),
+    (dict(ldy=100), INVALID),
+    (dict(bits=6), UNSUP),
+    (dict(kp=500), SHAPE),
+    (dict(a2=ctypes.c_void_p(0x10004)), SHAPE),
+    (dict(ws=ctypes.c_void_p(0x10008)), SHAPE),
+    (dict(y=ctypes.c_void_p(0x10001)), SHAPE),
+])
+def test_qgemm_residual_validation(lib, kw, want):
+    assert gemm_res(lib, **kw) == want
