@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+FP4_FP6_PEAK_TFLOPS = 10100.0  # dense MFMA rate of the FP4/FP6 (MX) operand formats
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
 
 
@@ -45,6 +46,9 @@ def parse():
     p.add_argument("--residual-frac", type=float, default=0.0, metavar="F",
                    help="decompose a seeded fraction F of the tokens (residual re-quantization added back "
                         "in the epilogue); per-token workloads without dual scale or rotation only")
+    p.add_argument("--mx", choices=["fp4", "fp6"], default=None,
+                   help="route the activations through the MX block formats (MXFP4 weights) on the scaled "
+                        "MFMA; with --config 5 the layers routed to 4 bits take MXFP4, the others INT8")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times) and exit; "
                         "rocprofv3 counters of that copy scale FETCH_SIZE/WRITE_SIZE to bytes")
@@ -79,8 +83,9 @@ def load_traffic(workload):
 class Layer:
     """Device buffers and launch closures for one configuration."""
 
-    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0):
+    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0, mx=None):
         c = gen.CONFIGS[cfg]
+        self.mx = mx
         self.cfg, self.c = cfg, c
         self.M, self.K, self.N = c["M"], c["K"], c["N"]
         self.vq, self.torch = vq, torch
@@ -104,6 +109,22 @@ class Layer:
                 self.bits_dev.append(bits)
             torch.cuda.synchronize()
             self.routes = [int(b.item()) for b in self.bits_dev]
+            if mx:  # layers routed to 4 bits use MXFP4 weights and activations
+                self.mx_w = [None] * self.layers
+                for l in range(self.layers):
+                    if self.routes[l] == 4:
+                        w = gen.make_w(cfg, layer=l).to(dev)
+                        self.mx_w[l] = vq.vq_mx_quant(w, "fp4")
+                        del w
+        elif mx:
+            if c["dual"] or c["gran"] != "token":
+                raise SystemExit("--mx needs a per-token workload without dual scale")
+            w = gen.make_w(cfg).to(dev)
+            self.mx_w = [vq.vq_mx_quant(w, "fp4")]
+            self.w = [None]
+            self.bits_dev = [None]
+            self.had = 0  # the MX blocks carry their own scales; no rotation on this route
+            del w
         else:
             w = gen.make_w(cfg).to(dev)
             if c["dual"]:
@@ -122,6 +143,11 @@ class Layer:
             self.scales = torch.empty((2 if n_out else 1,), dtype=torch.float32, device=dev)
         self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16 if c["dtype"] == "bf16" else torch.float16,
                              device=dev)
+        if mx:
+            fmt = "fp4" if cfg == 5 else mx
+            self.mx_fmt = fmt
+            self.mx_codes = torch.empty((self.M, vq.vq_mx_code_bytes(1, self.K, fmt)), dtype=torch.uint8, device=dev)
+            self.mx_scales = torch.empty(vq.vq_mx_scale_bytes(self.M, self.K), dtype=torch.uint8, device=dev)
         # Activation decomposition of a seeded set of tokens.
         self.R = int(round(residual_frac * self.M))
         if self.R:
@@ -136,14 +162,24 @@ class Layer:
                                   device=dev)
         torch.cuda.synchronize()
 
+    def use_mx(self, layer):
+        return self.mx is not None and (self.cfg != 5 or self.routes[layer] == 4)
+
     def quant(self, step, layer):
         x = self.x[step % len(self.x)]
+        if self.use_mx(layer):
+            self.vq.vq_mx_quant(x, self.mx_fmt, self.mx_codes, self.mx_scales)
+            return
         self.vq.vq_quant_act(x, self.a_bits, self.gran, self.had, self.idx,
                              bits_dev=self.bits_dev[layer], codes=self.codes, scales=self.scales)
         if self.R:
             self.vq.vq_quant_residual(x, self.rows, self.a_bits, self.a_bits, self.codes2, self.scales2)
 
     def gemm(self, layer):
+        if self.use_mx(layer):
+            bc, bs = self.mx_w[layer]
+            self.vq.vq_mx_gemm(self.mx_codes, self.mx_scales, self.mx_fmt, bc, bs, "fp4", self.y.dtype, y=self.y)
+            return
         wc, ws = self.w[layer]
         if self.R:
             self.vq.vq_qgemm_dequant_residual(self.codes, self.scales, wc, ws, self.c["w_bits"], self.codes2,
@@ -162,6 +198,8 @@ class Layer:
     def quant_bytes(self):
         # read 2 B per input element, write 1 B per code (padding included), 4 B per scale;
         # decomposed rows read their input once more and write K residual codes and a scale
+        if self.mx and self.cfg != 5:  # MX: 2 B read, w/8 B of code and 1/32 B of scale written per element
+            return self.M * self.K * 2 + self.mx_codes.numel() + self.M * self.K // 32
         return (self.M * self.K * 2 + self.M * self.kp + self.scales.numel() * 4
                 + self.R * (self.K * 2 + self.K + 4))
 
@@ -222,7 +260,7 @@ def main():
     import gen
 
     dev = torch.device("cuda:0")
-    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac)
+    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
@@ -277,6 +315,9 @@ def main():
     if L.R:
         workload += f"+decompose_{L.R}_tokens"
         traffic = q_traffic = None  # the counter runs cover the plain layer only
+    if L.mx:
+        workload += "+mx_" + ("fp4_route" if args.config == 5 else f"{L.mx_fmt}_act_fp4_weights")
+        traffic = q_traffic = None
 
     out = {
         "metric": "quantized-linear TOPS (int8 MFMA %peak) + act-quant GB/s (%HBM), 1 MI355X",
@@ -303,6 +344,16 @@ def main():
                       "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "bytes": L.quant_bytes(),
                       "avg_us": round(q_ms * 1e3, 2), "kernel": "k_rowquant", "traffic": q_traffic},
     }
+    if L.mx and args.config != 5:
+        out["dtype"] = L.mx_fmt
+        out["config"]["w_bits"] = "mxfp4"
+        out["config"]["a_bits"] = "mx" + L.mx_fmt
+        out["config"]["hadamard_block"] = 0
+        out["roofline"].update({"peak": FP4_FP6_PEAK_TFLOPS, "frac": round(gemm_tops / FP4_FP6_PEAK_TFLOPS, 4),
+                                "kernel": "k_mxgemm (scaled MFMA f8f6f4, MX block scales)"})
+        out["act_quant"]["kernel"] = "k_mxquant"
+    if L.mx and args.config == 5:
+        out["config"]["route_4bit"] = "mxfp4 x mxfp4 on the scaled MFMA"
     if L.R:
         out["config"]["decomposed_tokens"] = L.R
         out["roofline"]["kernel"] = "slot map + residual-row GEMM + k_qgemm with residual epilogue"
@@ -310,7 +361,7 @@ def main():
     if args.config == 5:
         out["config"]["routes_int8"] = L.routes.count(8)
         out["config"]["routes_int4"] = L.routes.count(4)
-    if not args.no_cpu:
+    if not args.no_cpu and not L.mx and not L.R:  # the oracle baseline is the plain integer layer
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

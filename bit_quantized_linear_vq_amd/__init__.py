@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libvq.so")
 VQ_OK, VQ_ERR_INVALID_ARG, VQ_ERR_SHAPE, VQ_ERR_UNSUPPORTED, VQ_ERR_HIP = range(5)
 VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 VQ_PER_TENSOR, VQ_PER_TOKEN, VQ_PER_TENSOR_STATIC = 0, 1, 2
+VQ_MXFP6, VQ_MXFP4 = 2, 4
 VQ_K_ALIGN = 64
 VQ_HAD_BLOCK = 128
 VQ_MAX_OUTLIERS = 128
@@ -27,11 +28,14 @@ EXPORTS = (
     "vq_outlier_part_len", "vq_packed_k", "vq_detect_workspace_elems", "vq_detect_outliers",
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
-    "vq_qgemm_dequant_residual", "vq_status_string", "vq_last_hip_error", "vq_version",
+    "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
+    "vq_status_string", "vq_last_hip_error", "vq_version",
 )
 
 _DT = {torch.float16: VQ_F16, torch.bfloat16: VQ_BF16, torch.float32: VQ_F32}
 _GRAN = {"tensor": VQ_PER_TENSOR, "token": VQ_PER_TOKEN, "static": VQ_PER_TENSOR_STATIC}
+_MX = {"fp4": VQ_MXFP4, "fp6": VQ_MXFP6}
+_MX_BITS = {"fp4": 4, "fp6": 6}
 
 
 class VQError(RuntimeError):
@@ -61,6 +65,10 @@ def _load():
         "vq_quant_residual": (I, [P, I, I64, I64, I64, I, I, P, I64, P, P, P]),
         "vq_residual_workspace_bytes": (I64, [I64, I64, I64]),
         "vq_qgemm_dequant_residual": (I, [P, P, P, I, P, I64, I64, I64, P, P, P, I64, P, I, I64, P, P]),
+        "vq_mx_code_bytes": (I64, [I64, I64, I]),
+        "vq_mx_scale_bytes": (I64, [I64, I64]),
+        "vq_mx_quant": (I, [P, I, I64, I64, I64, I, P, P, P]),
+        "vq_mx_gemm": (I, [P, P, I, P, P, I, I64, I64, I64, P, I, I64, P]),
         "vq_status_string": (ctypes.c_char_p, [I]),
         "vq_last_hip_error": (I, []),
         "vq_version": (ctypes.c_char_p, []),
@@ -243,4 +251,40 @@ def vq_qgemm_dequant_residual(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor
     _check("vq_qgemm_dequant_residual", _lib.vq_qgemm_dequant_residual(
         _ptr(a), _ptr(sa), _ptr(b), b_bits, _ptr(sb), m, n, kp, _ptr(a2), _ptr(sa2), _ptr(rows), n_rows,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(ws), _stream(a)))
+    return y
+
+
+def vq_mx_code_bytes(rows: int, k: int, fmt: str) -> int:
+    return int(_lib.vq_mx_code_bytes(rows, k, _MX[fmt]))
+
+
+def vq_mx_scale_bytes(rows: int, k: int) -> int:
+    return int(_lib.vq_mx_scale_bytes(rows, k))
+
+
+def vq_mx_quant(x: torch.Tensor, fmt: str = "fp4", codes=None, scales=None):
+    """MX codes of X [rows x K].  Returns (codes uint8 [rows x K*w/8], scales uint8 E8M0 in step-major order)."""
+    _dev(x, "x")
+    rows, k = x.shape
+    if codes is None:
+        codes = torch.empty((rows, k * _MX_BITS[fmt] // 8), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(max(vq_mx_scale_bytes(rows, k), 1), dtype=torch.uint8, device=x.device)
+    _check("vq_mx_quant", _lib.vq_mx_quant(
+        _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), _MX.get(fmt, -1), _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: torch.Tensor, fb: str = "fp4",
+               out_dtype=torch.bfloat16, y=None):
+    """Y = dec(A) . dec(B)^T on the scaled MFMA; a, b are the MX code buffers of vq_mx_quant."""
+    _dev(a, "a")
+    m = a.shape[0]
+    n = b.shape[0]
+    k = a.shape[1] * 8 // _MX_BITS[fa]
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _check("vq_mx_gemm", _lib.vq_mx_gemm(
+        _ptr(a), _ptr(sa), _MX.get(fa, -1), _ptr(b), _ptr(sb), _MX.get(fb, -1), m, n, k,
+        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _stream(a)))
     return y

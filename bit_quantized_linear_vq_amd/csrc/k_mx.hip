@@ -1,0 +1,457 @@
+// MX block-format route for gfx950: MXFP4 / MXFP6 quantization and the GEMM on the
+// scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// 6Bit-Diffusion (gist.science, arXiv 2603.18742), Introduction and Methodology B.1:
+// recent GPUs replaced INT4 by a 4-bit floating-point block format, DMPQ routes
+// activations between INT8 and that format, and the weights are kept in it offline.
+// gfx950's counterpart is the OCP MX family: blocks of 32 elements along K share one
+// E8M0 scale 2^e, e = floor(log2(max|v|)) - emax (emax = 2 for FP4 E2M1 and FP6 E2M3),
+// and each element is v / 2^e rounded to nearest even and clamped to the largest value
+// (6 for E2M1, 7.5 for E2M3).  The matrix cores take the element codes and the scale
+// bytes directly, at twice the int8 rate.
+//
+// Layouts (both operands K-contiguous, "TN"):
+//   codes   row-major, element p of a row at bits [w*p, w*p+w) of the row's little-endian
+//           bit string (w = 4: two per byte, low nibble first; w = 6: 3 bytes per 4);
+//   scales  E8M0 bytes in k-step-major order [K/64][rows8][2] (rows8 = rows rounded up to
+//           8): the two block scales of every row for each 64-deep step are adjacent, so
+//           a tile's scales for one step are 512 contiguous bytes that the GEMM moves into
+//           LDS with the same direct loads as the codes.
+//
+// Measured on gfx950 (lane-layout probe of the scaled MFMA): for FP4 and FP6 E2M3 the
+// A operand of lane l holds row l % 32 and K values 32 * (l / 32) + p, the B operand
+// column l % 32 likewise, and each lane's scale byte applies to its 32 values (one MX
+// block); the 32 x 32 float32 result is laid out as for the other 32x32 MFMA forms.
+#include <type_traits>
+
+#include "dev_common.h"
+#include "gemm_common.h"
+#include "vq_internal.h"
+
+namespace vqk {
+
+enum : int { MX_FP6 = 2, MX_FP4 = 4 };  // the scaled MFMA's operand format codes
+
+template <int FMT>
+struct MxFmt {
+  static constexpr int M = FMT == MX_FP4 ? 1 : 3;  // mantissa bits (both have 2 exponent bits, bias 1)
+  static constexpr int W = 3 + M;                  // bits per element
+  static constexpr float VMAX = FMT == MX_FP4 ? 6.0f : 7.5f;
+  static constexpr int STEP_BYTES = 64 * W / 8;    // bytes of one row per 64-deep step
+};
+
+// Element code of a scaled value t: nearest value (ties to even) of the binade of |t|,
+// clamped to the largest magnitude; codes grow monotonically with the magnitude, so the
+// code is e * 2^M + n with n = rne(|t| / 2^(e - M)).
+template <int FMT>
+__device__ __forceinline__ unsigned mx_code(float t) {
+  using F = MxFmt<FMT>;
+  const unsigned sign = f_bits(t) >> 31;
+  const float a = fminf(fabsf(t), F::VMAX);
+  int e = (int)((f_bits(a) >> 23) & 0xFF) - 127;  // floor(log2 a) for a >= 1
+  e = e < 0 ? 0 : e;
+  const float q = a * bits_f((unsigned)(127 + F::M - e) << 23);  // exact: a * 2^(M - e)
+  const unsigned n = f_bits(q + 12582912.0f) - 0x4B400000u;    // rne, q <= 16
+  return (sign << (2 + F::M)) | (unsigned)((e << F::M) + (int)n);
+}
+
+// ------------------------------------------------------------------ quantization
+
+// One wave per row (grid-stride over rows); a lane owns 16 elements, so a lane pair
+// owns one 32-element block.
+template <int DT, int FMT>
+__global__ __launch_bounds__(256) void k_mxquant(const void* x, int64_t ldx, int64_t rows, int k, int64_t rows8,
+                                                 uint8_t* codes, uint8_t* scales) {
+  using F = MxFmt<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int64_t row_bytes = (int64_t)k * F::W / 8;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4) {
+    const char* xr = reinterpret_cast<const char*>(x) + row * ldx * 2;
+    uint8_t* cr = codes + row * row_bytes;
+    for (int c = lane; c < k / 16; c += 64) {  // k / 16 is even: both lanes of a pair take part
+      float v[16];
+      load16<DT>(xr + (int64_t)c * 32, v);
+      float amax = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[t]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      const int ex = (int)((f_bits(amax) >> 23) & 0xFF);
+      int e = ex == 0 ? -127 : ex - 127 - 2;  // emax = 2 for both formats
+      e = e < -127 ? -127 : e;
+      const int blk = c >> 1;
+      if ((c & 1) == 0) scales[((int64_t)(blk >> 1) * rows8 + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
+      const float inv = bits_f((unsigned)(127 - e) << 23);  // 2^-e, e in [-127, 125]
+      unsigned u[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) u[t] = mx_code<FMT>(v[t] * inv);
+      if constexpr (FMT == MX_FP4) {
+        u2v w{0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w.x |= u[t] << (4 * t);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w.y |= u[8 + t] << (4 * t);
+        *reinterpret_cast<u2v*>(cr + (int64_t)c * 8) = w;
+      } else {
+        const unsigned d0 = u[0] | u[1] << 6 | u[2] << 12 | u[3] << 18 | u[4] << 24 | u[5] << 30;
+        const unsigned d1 = u[5] >> 2 | u[6] << 4 | u[7] << 10 | u[8] << 16 | u[9] << 22 | u[10] << 28;
+        const unsigned d2 = u[10] >> 4 | u[11] << 2 | u[12] << 8 | u[13] << 14 | u[14] << 20 | u[15] << 26;
+        unsigned* p = reinterpret_cast<unsigned*>(cr + (int64_t)c * 12);
+        p[0] = d0;
+        p[1] = d1;
+        p[2] = d2;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+
+constexpr int MX_BM = 256, MX_BN = 256, MX_BK = 64;
+constexpr int MX_NT = 512;
+constexpr int MX_WTM = 128, MX_WTN = 64;
+constexpr int MX_MBLK = MX_WTM / 32, MX_NBLK = MX_WTN / 32;
+
+template <int FA>
+struct MxCfg {
+  static constexpr int A_ROW = MxFmt<FA>::STEP_BYTES;  // 32 (FP4) or 48 (FP6)
+  static constexpr int A_BYTES = MX_BM * A_ROW;
+  static constexpr int B_BYTES = MX_BN * 32;
+  static constexpr int SA_OFF = A_BYTES + B_BYTES;      // 256 x 2 scale bytes of A, then of B
+  static constexpr int STAGE = SA_OFF + 1024;
+  static constexpr int NST = 6;
+  // Direct loads per wave and step: A slots, one B slot, one scale slot (8 lanes each).
+  static constexpr int LA = FA == MX_FP4 ? 1 : 2;
+  static constexpr int L = LA + 2;
+};
+
+struct MxArgs {
+  const uint8_t* a;   // activations: codes [m x row bytes], scales [k/64][m8][2]
+  const uint8_t* sa;
+  const uint8_t* b;   // weights: FP4 codes [n x k/2], scales [k/64][n8][2]
+  const uint8_t* sb;
+  void* y;
+  int m, n, k;
+  int64_t m8, n8;
+  int64_t ldy;
+  int vec_store;
+  int tiles_m, tiles_n;
+};
+
+template <int FA, int OUT_DT>
+__global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mxgemm(MxArgs g) {
+  using C = MxCfg<FA>;
+  constexpr bool HALF_OUT = OUT_DT != DT_F32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // wave grid 2 (M) x 4 (N)
+  const int T = g.tiles_m * g.tiles_n;
+  const int nk = g.k / MX_BK;
+  const int64_t a_rowb = (int64_t)g.k * MxFmt<FA>::W / 8;
+  const int64_t b_rowb = g.k / 2;
+
+  // ---- direct-load assignment (per lane, per step).
+  // A, FP4: one 1 KB slot per wave = 32 rows x 32 B, lane -> row 32w + lane/2, chunk
+  //   (lane & 1) ^ swz32(row).  A, FP6: two 768 B slots per wave (lanes 0-47) = 16 rows
+  //   x 48 B each, dense rows, lane -> row, 16-byte third lane % 3.
+  // B: one 1 KB slot per wave, as A in FP4.  Scales: 128 B per wave (lanes 0-7): waves
+  //   0-3 carry the A scales of rows 64w .. 64w+63, waves 4-7 the B scales.
+  int ra[C::LA], ca[C::LA], la_off[C::LA];
+  bool a_on[C::LA];
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) {
+    if constexpr (FA == MX_FP4) {
+      ra[i] = 32 * wave + (lane >> 1);
+      ca[i] = 16 * ((lane & 1) ^ swz32(ra[i]));
+      la_off[i] = wave * 1024;
+      a_on[i] = true;
+    } else {
+      const int slot = 2 * wave + i;  // 16 slots of 768 B
+      ra[i] = 16 * slot + lane / 3;
+      ca[i] = 16 * (lane % 3);
+      la_off[i] = slot * 768;
+      a_on[i] = lane < 48;
+    }
+  }
+  const int rb = 32 * wave + (lane >> 1);
+  const int cb = 16 * ((lane & 1) ^ swz32(rb));
+  const int lb_off = C::A_BYTES + wave * 1024;
+  const bool s_on = lane < 8;
+  const bool s_is_a = wave < 4;
+  const int s_row0 = 64 * (wave & 3) + 8 * lane;  // first tile row of this lane's 16 scale bytes
+  const int ls_off = C::SA_OFF + wave * 128;
+
+  const uint8_t* ga[C::LA];
+  const uint8_t* gb;
+  const uint8_t* gs;
+  int64_t s_pitch = 0;  // bytes between the scale slabs of consecutive steps
+  int m0 = 0, n0 = 0;
+  auto set_tile = [&](int vt) {
+    int tm, tn;
+    tile_of(vt, g.tiles_m, g.tiles_n, tm, tn);
+    m0 = tm * MX_BM;
+    n0 = tn * MX_BN;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) ga[i] = g.a + (int64_t)min(m0 + ra[i], g.m - 1) * a_rowb + ca[i];
+    gb = g.b + (int64_t)min(n0 + rb, g.n - 1) * b_rowb + cb;
+    // Scale chunk of 8 rows: clamped to the last whole chunk of the (8-padded) slab.
+    if (s_is_a) {
+      const int64_t r = min((int64_t)m0 + s_row0, g.m8 - 8);
+      gs = g.sa + r * 2;
+      s_pitch = g.m8 * 2;
+    } else {
+      const int64_t r = min((int64_t)n0 + s_row0, g.n8 - 8);
+      gs = g.sb + r * 2;
+      s_pitch = g.n8 * 2;
+    }
+  };
+  auto issue = [&](int kt, int slot) {
+    uint8_t* base = lds + slot * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i)
+      if (a_on[i]) dma16(ga[i] + (int64_t)kt * MxFmt<FA>::STEP_BYTES, base + la_off[i]);
+    dma16(gb + (int64_t)kt * 32, base + lb_off);
+    if (s_on) dma16(gs + (int64_t)kt * s_pitch, base + ls_off);
+  };
+  auto issue_prologue = [&]() {
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+      if (s < nk) issue(s, s);
+  };
+
+  // ---- fragment offsets: rows 32*blk + (lane & 31), K half lane >> 5.
+  const int rl = lane & 31;
+  const int kh = lane >> 5;
+  int fa_off;
+  if constexpr (FA == MX_FP4) {
+    fa_off = (wm * MX_WTM + rl) * 32 + 16 * (kh ^ swz32(rl));
+  } else {
+    fa_off = (wm * MX_WTM + rl) * 48 + 24 * kh;
+  }
+  const int fb_off = C::A_BYTES + (wn * MX_WTN + rl) * 32 + 16 * (kh ^ swz32(rl));
+  const int fsa_off = C::SA_OFF + (wm * MX_WTM + rl) * 2 + kh;
+  const int fsb_off = C::SA_OFF + 512 + (wn * MX_WTN + rl) * 2 + kh;
+
+  // Operands of one step: A fragments (4 or 6 dwords), B fragments, scale bytes.
+  struct Frag {
+    v8i a[MX_MBLK];
+    v8i b[MX_NBLK];
+    int sa[MX_MBLK];
+    int sb[MX_NBLK];
+  };
+  auto load_step = [&](int slot, Frag& f) {
+    const uint8_t* st = lds + slot * C::STAGE;
+#pragma unroll
+    for (int nb = 0; nb < MX_NBLK; ++nb) {
+      const v4i w = *reinterpret_cast<const v4i*>(st + fb_off + nb * 32 * 32);
+      f.b[nb] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
+      f.sb[nb] = st[fsb_off + nb * 32 * 2];
+    }
+#pragma unroll
+    for (int mb = 0; mb < MX_MBLK; ++mb) {
+      if constexpr (FA == MX_FP4) {
+        const v4i w = *reinterpret_cast<const v4i*>(st + fa_off + mb * 32 * 32);
+        f.a[mb] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
+      } else {
+        const uint8_t* p = st + fa_off + mb * 32 * 48;
+        const u2v w0 = *reinterpret_cast<const u2v*>(p);
+        const u2v w1 = *reinterpret_cast<const u2v*>(p + 8);
+        const u2v w2 = *reinterpret_cast<const u2v*>(p + 16);
+        f.a[mb] = v8i{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
+      }
+      f.sa[mb] = st[fsa_off + mb * 32 * 2];
+    }
+  };
+
+  v16f acc[MX_MBLK][MX_NBLK];
+  // Weights are the MFMA's A operand (FP4), activations its B operand (FA).
+  auto mma_nb = [&](const Frag& f, int nb) {
+#pragma unroll
+    for (int mb = 0; mb < MX_MBLK; ++mb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[nb], f.a[mb], acc[mb][nb], MX_FP4, FA, 0,
+                                                                    f.sb[nb], 0, f.sa[mb]);
+  };
+  auto wait_loads = [&](int later) {  // at most `later` load groups may stay in flight
+    if (later >= 4) {
+      wait_vmcnt<4 * C::L>();
+    } else if (later == 3) {
+      wait_vmcnt<3 * C::L>();
+    } else if (later == 2) {
+      wait_vmcnt<2 * C::L>();
+    } else if (later == 1) {
+      wait_vmcnt<C::L>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+
+  int vt = blockIdx.x;
+  if (vt >= T) return;
+  set_tile(vt);
+  issue_prologue();
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < MX_MBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < MX_NBLK; ++j) acc[i][j] = v16f{};
+
+    // Step kt: the MFMAs of weight block 0 run on operands read during step kt-1; then
+    // every wave waits for its loads of step kt+1 and meets the others at a barrier,
+    // which publishes stage kt+1 and certifies that stage kt-1 is no longer read; that
+    // stage receives step kt+NST-1 and the operands of step kt+1 are read while the
+    // MFMAs of weight block 1 run.
+    Frag f0, f1;
+    wait_loads(min(C::NST - 2, nk - 1));
+    barrier_nofence();
+    load_step(0, f0);
+    int kt = 0, slot = 0;
+    for (; kt < nk - (C::NST - 1); ++kt) {
+      const int next = slot + 1 == C::NST ? 0 : slot + 1;
+      const int refill = slot == 0 ? C::NST - 1 : slot - 1;
+      mma_nb(f0, 0);
+      wait_vmcnt<(C::NST - 3) * C::L>();
+      barrier_nofence();
+      issue(kt + C::NST - 1, refill);
+      load_step(next, f1);
+      mma_nb(f0, 1);
+      f0 = f1;
+      slot = next;
+    }
+    for (; kt < nk; ++kt) {
+      const int next = slot + 1 == C::NST ? 0 : slot + 1;
+      mma_nb(f0, 0);
+      if (kt + 1 < nk) {
+        wait_loads(nk - 2 - kt);
+        barrier_nofence();
+        load_step(next, f1);
+      }
+      mma_nb(f0, 1);
+      f0 = f1;
+      slot = next;
+    }
+
+    // ------------------------------------------------------------ epilogue
+    const int nvt = vt + (int)gridDim.x;
+    const bool has_next = nvt < T;
+    const int cm0 = m0, cn0 = n0;
+    barrier_nofence();  // every wave is done with the ring
+    if (has_next) {
+      set_tile(nvt);
+      issue_prologue();
+    }
+    // Output layout of a 32 x 32 block: lane holds column m = lane & 31 (activation row)
+    // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows); the
+    // block scales are already applied by the matrix cores.
+    const int mrow = wm * MX_WTM + (lane & 31);
+    const int ncol = wn * MX_WTN + 4 * (lane >> 5);
+    typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+#pragma unroll
+    for (int mb = 0; mb < MX_MBLK; ++mb) {
+      const int m = cm0 + mrow + mb * 32;
+#pragma unroll
+      for (int nb = 0; nb < MX_NBLK; ++nb) {
+        u2v hw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = cn0 + ncol + nb * 32 + 8 * q;
+          float out[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) out[r] = acc[mb][nb][4 * q + r];
+          if constexpr (HALF_OUT) {
+            h_t hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = (h_t)f32_fence(out[r]);
+            hw[q] = u2v{(unsigned)__builtin_bit_cast(unsigned short, hv[0]) |
+                            ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
+                        (unsigned)__builtin_bit_cast(unsigned short, hv[2]) |
+                            ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
+          } else {
+            if (m < g.m && n < g.n) store4_f32(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
+          }
+        }
+        if constexpr (HALF_OUT) {
+          // Lanes l and l+32 exchange column groups so that each holds eight consecutive
+          // outputs of its row (one 16-byte store).
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const u2v X = hw[2 * pr], Y = hw[2 * pr + 1];
+            const auto s0 = __builtin_amdgcn_permlane32_swap(X.x, Y.x, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(X.y, Y.y, false, false);
+            const u4v w = {s0[0], s1[0], s0[1], s1[1]};
+            const int no = cn0 + wn * MX_WTN + nb * 32 + 16 * pr + 8 * (lane >> 5);
+            if (m < g.m && no < g.n) {
+              h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + no;
+              if (g.vec_store && no + 8 <= g.n) {
+                *reinterpret_cast<u4v*>(dst) = w;
+              } else {
+                for (int e = 0; e < 8 && no + e < g.n; ++e) {
+                  const unsigned d = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+                  dst[e] = __builtin_bit_cast(h_t, (unsigned short)(d >> (16 * (e & 1))));
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    if (!has_next) break;
+    vt = nvt;
+  }
+}
+
+}  // namespace vqk
+
+namespace vq_internal {
+
+using namespace vqk;
+
+int64_t mx_rows8(int64_t rows) { return (rows + 7) / 8 * 8; }
+
+hipError_t launch_mx_quant(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int fmt, uint8_t* codes,
+                           uint8_t* scales, hipStream_t st) {
+  const int64_t blocks64 = (rows + 3) / 4;
+  const unsigned grid = (unsigned)(blocks64 < 8192 ? blocks64 : 8192);
+  const int64_t r8 = mx_rows8(rows);
+#define MXQ(DTV, FV) hipLaunchKernelGGL((k_mxquant<DTV, FV>), dim3(grid), dim3(256), 0, st, x, ldx, rows, (int)k, r8, codes, scales)
+  if (dtype == DT_F16) {
+    if (fmt == MX_FP4) MXQ(DT_F16, MX_FP4); else MXQ(DT_F16, MX_FP6);
+  } else {
+    if (fmt == MX_FP4) MXQ(DT_BF16, MX_FP4); else MXQ(DT_BF16, MX_FP6);
+  }
+#undef MXQ
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uint8_t* b, const uint8_t* sb, int64_t m,
+                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, hipStream_t st) {
+  MxArgs g{};
+  g.a = a;
+  g.sa = sa;
+  g.b = b;
+  g.sb = sb;
+  g.y = y;
+  g.m = (int)m;
+  g.n = (int)n;
+  g.k = (int)k;
+  g.m8 = mx_rows8(m);
+  g.n8 = mx_rows8(n);
+  g.ldy = ldy;
+  const int64_t esize = out_dt == DT_F32 ? 4 : 2;
+  g.vec_store = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * esize) % 16 == 0) ? 1 : 0;
+  g.tiles_m = (int)((m + MX_BM - 1) / MX_BM);
+  g.tiles_n = (int)((n + MX_BN - 1) / MX_BN);
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int grid = tiles < persistent_blocks() ? tiles : persistent_blocks();
+#define MXG(F, O) hipLaunchKernelGGL((k_mxgemm<F, O>), dim3(grid), dim3(MX_NT), 0, st, g)
+  if (fa == MX_FP4) {
+    if (out_dt == DT_F16) MXG(MX_FP4, DT_F16); else if (out_dt == DT_BF16) MXG(MX_FP4, DT_BF16); else MXG(MX_FP4, DT_F32);
+  } else {
+    if (out_dt == DT_F16) MXG(MX_FP6, DT_F16); else if (out_dt == DT_BF16) MXG(MX_FP6, DT_BF16); else MXG(MX_FP6, DT_F32);
+  }
+#undef MXG
+  return hipGetLastError();
+}
+
+}  // namespace vq_internal

@@ -308,6 +308,47 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
   return hip_status(vq_internal::launch_residual_merge(y12, n_rows, n, rows_dev, m, y, (int)out_dt, ldy, stream));
 }
 
+// ------------------------------------------------------------------ MX formats
+
+namespace {
+bool mx_fmt_ok(vq_mx_fmt f) { return f == VQ_MXFP4 || f == VQ_MXFP6; }
+int mx_bits(vq_mx_fmt f) { return f == VQ_MXFP4 ? 4 : 6; }
+}  // namespace
+
+int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt) {
+  if (rows < 1 || k < 1 || k % VQ_K_ALIGN || !mx_fmt_ok(fmt)) return 0;
+  return rows * (k * mx_bits(fmt) / 8);
+}
+
+int64_t vq_mx_scale_bytes(int64_t rows, int64_t k) {
+  if (rows < 1 || k < 1 || k % VQ_K_ALIGN) return 0;
+  return (k / 64) * vq_internal::mx_rows8(rows) * 2;
+}
+
+vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt, uint8_t* codes,
+                      uint8_t* scales, hipStream_t stream) {
+  if (!x || !codes || !scales) return VQ_ERR_INVALID_ARG;
+  if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
+  if (rows < 1 || k < 1 || rows >= kMaxDim || k >= kMaxDim || ldx < k) return VQ_ERR_INVALID_ARG;
+  if (!mx_fmt_ok(fmt)) return VQ_ERR_UNSUPPORTED;
+  if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
+  if (!aligned16(x) || ldx % 8 || reinterpret_cast<uintptr_t>(codes) % 8) return VQ_ERR_SHAPE;
+  return hip_status(vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream));
+}
+
+vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const uint8_t* b, const uint8_t* sb,
+                     vq_mx_fmt fb, int64_t m, int64_t n, int64_t k, void* y, vq_dtype out_dt, int64_t ldy,
+                     hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !y) return VQ_ERR_INVALID_ARG;
+  if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
+  if (m < 1 || n < 1 || k < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return VQ_ERR_INVALID_ARG;
+  if (!mx_fmt_ok(fa) || fb != VQ_MXFP4) return VQ_ERR_UNSUPPORTED;
+  if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(sa) || !aligned16(sb)) return VQ_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
+  return hip_status(vq_internal::launch_mx_gemm(a, sa, (int)fa, b, sb, m, n, k, y, (int)out_dt, ldy, stream));
+}
+
 // ------------------------------------------------------------------ routing
 
 int64_t vq_route_workspace_elems(int64_t n) { return n < 1 ? 0 : 2 * (int64_t)vq_internal::route_blocks(); }

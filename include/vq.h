@@ -32,7 +32,8 @@
  * diffusion models"), sections Methodology and Technical details; 6Bit-Diffusion
  * (gist.science summary of arXiv 2603.18742), Key Insights 1 and Methodology B.1 (DMPQ);
  * S2Q-VDiT (gist.science summary of arXiv 2508.04016), the W4A6 setting; SemanticDialect
- * (gist.science summary of arXiv 2603.02883), Methodology 2.2 (activation decomposition).
+ * (gist.science summary of arXiv 2603.02883), Methodology 2.2 (activation decomposition);
+ * the OCP Microscaling (MX) v1.0 format definition for the MX block formats.
  */
 #ifndef VQ_H
 #define VQ_H
@@ -59,6 +60,12 @@ typedef enum vq_gran {
   VQ_PER_TOKEN = 1,        /* one dynamic scale per row (token) and partition */
   VQ_PER_TENSOR_STATIC = 2 /* caller-given scale per partition: r = fl32(1 / s) */
 } vq_gran;
+
+/* MX element formats: the codes of the scaled MFMA's operand formats. */
+typedef enum vq_mx_fmt {
+  VQ_MXFP6 = 2, /* FP6 E2M3: sign, 2 exponent bits (bias 1), 3 mantissa bits; largest 7.5 */
+  VQ_MXFP4 = 4  /* FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; largest 6 */
+} vq_mx_fmt;
 
 #define VQ_K_ALIGN 64        /* K and each K partition are multiples of this */
 #define VQ_HAD_BLOCK 128     /* the only Hadamard block size */
@@ -218,6 +225,40 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
                                     const float* sb, int64_t m, int64_t n, int64_t kp, const int8_t* a2,
                                     const float* sa2, const int32_t* rows_dev, int64_t n_rows, void* y,
                                     vq_dtype out_dt, int64_t ldy, void* ws, hipStream_t stream);
+
+/*
+ * MX block formats (6Bit-Diffusion, Introduction and Methodology B.1: GPUs that dropped
+ * INT4 offer a 4-bit floating-point block format, and DMPQ routes activations between
+ * INT8 and it, with the weights in it offline).  The gfx950 form is OCP MX: per row,
+ * blocks of 32 consecutive K elements share a scale 2^e stored as an E8M0 byte
+ * (e + 127), e = floor(log2(max|v|)) - 2 clamped to [-127, 127] (a zero block gets
+ * e = -127); each element is v / 2^e rounded to nearest even and clamped to +-6 (FP4)
+ * or +-7.5 (FP6); a negative value that rounds to zero keeps its sign bit.
+ *   codes   row-major [rows x k*w/8] bytes, w = 4 or 6; element p of a row at bits
+ *           [w*p, w*p+w) of the row's little-endian bit string
+ *   scales  E8M0 bytes in step-major order [k/64][rows8][2], rows8 = rows rounded up to a
+ *           multiple of 8 (byte (t * rows8 + r) * 2 + h = block 2t + h of row r); bytes
+ *           of the padding rows are not written
+ * vq_mx_code_bytes / vq_mx_scale_bytes give the buffer sizes (0 for invalid sizes).
+ *
+ * vq_mx_quant: x device, dt in {F16, BF16}, [rows x k], stride ldx; 16-byte aligned,
+ *   ldx % 8 == 0, k % 64 == 0, codes 8-byte aligned.  Finite inputs.
+ *   Errors: INVALID_ARG, SHAPE, UNSUPPORTED (fmt).
+ * vq_mx_gemm: y[i,j] = sum_k dec(a[i,k]) * dec(b[j,k]) on the matrix cores (block scales
+ *   applied there, float32 accumulation), then RNE to out_dt.  a: activations [m x k]
+ *   in fa (MXFP4 or MXFP6); b: weights [n x k], MXFP4 only (fb); codes and scales
+ *   16-byte aligned; y as for vq_qgemm_dequant.  The sums are accumulated in float32 by
+ *   the hardware, so y equals the exact sum rounded to float32 only up to the
+ *   accumulation's rounding.  Errors: INVALID_ARG, SHAPE (k % 64, alignment),
+ *   UNSUPPORTED (fa, fb other than MXFP4).
+ */
+int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt);
+int64_t vq_mx_scale_bytes(int64_t rows, int64_t k);
+vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt,
+                      uint8_t* codes, uint8_t* scales, hipStream_t stream);
+vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const uint8_t* b,
+                     const uint8_t* sb, vq_mx_fmt fb, int64_t m, int64_t n, int64_t k, void* y,
+                     vq_dtype out_dt, int64_t ldy, hipStream_t stream);
 
 /*
  * DMPQ routing on the device (6Bit-Diffusion, Key Insights 1 and Methodology B.1):

@@ -261,3 +261,59 @@ def gemm_res(lib, **kw):
 ])
 def test_qgemm_residual_validation(lib, kw, want):
     assert gemm_res(lib, **kw) == want
+
+
+MXFP6, MXFP4 = 2, 4
+
+
+def test_mx_size_helpers(lib):
+    assert lib.vq_mx_code_bytes(17776, 12288, MXFP4) == 17776 * 6144
+    assert lib.vq_mx_code_bytes(10, 128, MXFP6) == 10 * 96
+    assert lib.vq_mx_code_bytes(10, 100, MXFP4) == 0
+    assert lib.vq_mx_code_bytes(10, 128, 3) == 0
+    # step-major E8M0 scales: [k/64][rows rounded up to 8][2]
+    assert lib.vq_mx_scale_bytes(17776, 12288) == 192 * 17776 * 2
+    assert lib.vq_mx_scale_bytes(3, 128) == 2 * 8 * 2
+    assert lib.vq_mx_scale_bytes(0, 128) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=NULL), INVALID),
+    (dict(codes=NULL), INVALID),
+    (dict(scales=NULL), INVALID),
+    (dict(dt=F32), INVALID),
+    (dict(rows=0), INVALID),
+    (dict(ldx=100), INVALID),
+    (dict(fmt=3), UNSUP),
+    (dict(k=96, ldx=96), SHAPE),
+    (dict(ldx=132), SHAPE),
+    (dict(x=ctypes.c_void_p(0x10008)), SHAPE),
+    (dict(codes=ctypes.c_void_p(0x10004)), SHAPE),
+])
+def test_mx_quant_validation(lib, kw, want):
+    a = dict(x=FAKE, dt=BF16, rows=64, k=128, ldx=128, fmt=MXFP4, codes=FAKE, scales=FAKE, stream=NULL)
+    a.update(kw)
+    assert lib.vq_mx_quant(a["x"], a["dt"], a["rows"], a["k"], a["ldx"], a["fmt"], a["codes"], a["scales"],
+                           a["stream"]) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(a=NULL), INVALID),
+    (dict(sb=NULL), INVALID),
+    (dict(y=NULL), INVALID),
+    (dict(out=5), INVALID),
+    (dict(m=0), INVALID),
+    (dict(ldy=10), INVALID),
+    (dict(fa=3), UNSUP),
+    (dict(fb=MXFP6), UNSUP),
+    (dict(k=96), SHAPE),
+    (dict(sa=ctypes.c_void_p(0x10008)), SHAPE),
+    (dict(b=ctypes.c_void_p(0x10004)), SHAPE),
+    (dict(y=ctypes.c_void_p(0x10001)), SHAPE),
+])
+def test_mx_gemm_validation(lib, kw, want):
+    a = dict(a=FAKE, sa=FAKE, fa=MXFP4, b=FAKE, sb=FAKE, fb=MXFP4, m=64, n=64, k=128, y=FAKE, out=BF16, ldy=64,
+             stream=NULL)
+    a.update(kw)
+    assert lib.vq_mx_gemm(a["a"], a["sa"], a["fa"], a["b"], a["sb"], a["fb"], a["m"], a["n"], a["k"], a["y"],
+                          a["out"], a["ldy"], a["stream"]) == want
