@@ -111,17 +111,22 @@ constexpr int MX_NT = 512;
 constexpr int MX_WTM = 128, MX_WTN = 64;
 constexpr int MX_MBLK = MX_WTM / 32, MX_NBLK = MX_WTN / 32;
 
-template <int FA>
+// A ring stage holds S consecutive 64-deep MFMA steps ("sub-steps") of both operands and
+// their scales; one barrier per stage, so S = 2 halves the synchronization per MFMA.
+template <int FA, int S>
 struct MxCfg {
-  static constexpr int A_ROW = MxFmt<FA>::STEP_BYTES;  // 32 (FP4) or 48 (FP6)
+  static constexpr int A_ROW = MxFmt<FA>::STEP_BYTES * S;  // 32/64 (FP4) or 48/96 (FP6) bytes
+  static constexpr int B_ROW = 32 * S;
   static constexpr int A_BYTES = MX_BM * A_ROW;
-  static constexpr int B_BYTES = MX_BN * 32;
-  static constexpr int SA_OFF = A_BYTES + B_BYTES;      // 256 x 2 scale bytes of A, then of B
-  static constexpr int STAGE = SA_OFF + 1024;
-  static constexpr int NST = 6;
-  // Direct loads per wave and step: A slots, one B slot, one scale slot (8 lanes each).
-  static constexpr int LA = FA == MX_FP4 ? 1 : 2;
-  static constexpr int L = LA + 2;
+  static constexpr int B_BYTES = MX_BN * B_ROW;
+  static constexpr int SA_OFF = A_BYTES + B_BYTES;  // per sub-step: 256 x 2 scale bytes of A, then of B
+  static constexpr int STAGE = SA_OFF + 1024 * S;
+  static constexpr int NST = (160 * 1024) / STAGE > 6 ? 6 : (160 * 1024) / STAGE;
+  // Direct loads per wave and stage: A slots (1 KB, or 768 B of dense FP6 rows), B slots,
+  // and one 8-lane scale slot per sub-step.
+  static constexpr int LA = FA == MX_FP4 ? A_BYTES / 8192 : A_BYTES / (8 * 768);
+  static constexpr int LB = B_BYTES / 8192;
+  static constexpr int L = LA + LB + S;
 };
 
 struct MxArgs {
@@ -137,9 +142,9 @@ struct MxArgs {
   int tiles_m, tiles_n;
 };
 
-template <int FA, int OUT_DT>
+template <int FA, int S, int OUT_DT>
 __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mxgemm(MxArgs g) {
-  using C = MxCfg<FA>;
+  using C = MxCfg<FA, S>;
   constexpr bool HALF_OUT = OUT_DT != DT_F32;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
 
@@ -148,43 +153,58 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // wave grid 2 (M) x 4 (N)
   const int T = g.tiles_m * g.tiles_n;
-  const int nk = g.k / MX_BK;
+  const int nk = g.k / (MX_BK * S);  // ring stages along K
   const int64_t a_rowb = (int64_t)g.k * MxFmt<FA>::W / 8;
   const int64_t b_rowb = g.k / 2;
 
-  // ---- direct-load assignment (per lane, per step).
-  // A, FP4: one 1 KB slot per wave = 32 rows x 32 B, lane -> row 32w + lane/2, chunk
-  //   (lane & 1) ^ swz32(row).  A, FP6: two 768 B slots per wave (lanes 0-47) = 16 rows
-  //   x 48 B each, dense rows, lane -> row, 16-byte third lane % 3.
-  // B: one 1 KB slot per wave, as A in FP4.  Scales: 128 B per wave (lanes 0-7): waves
-  //   0-3 carry the A scales of rows 64w .. 64w+63, waves 4-7 the B scales.
+  // ---- direct-load assignment (per lane, per stage).
+  // 64-byte rows (FP4, S = 2): 1 KB slot = 16 rows, lane -> row lane/4, chunk (lane & 3)
+  //   ^ swz64(row), as in the integer kernel.  32-byte rows (FP4, S = 1): 1 KB = 32 rows,
+  //   lane -> row lane/2, chunk (lane & 1) ^ swz32(row).  Dense FP6 rows of 48 or 96 B:
+  //   768 B slots (lanes 0-47), lane -> row and 16-byte piece in row order.
+  // Scales: per sub-step 128 B per wave (lanes 0-7): waves 0-3 carry the A scales of rows
+  //   64w .. 64w+63, waves 4-7 the B scales.
+  auto assign64 = [&](int q, int& r, int& c) {
+    if constexpr (S == 2) {
+      r = 16 * q + (lane >> 2);
+      c = 16 * ((lane & 3) ^ swz64(r));
+    } else {
+      r = 32 * q + (lane >> 1);
+      c = 16 * ((lane & 1) ^ swz32(r));
+    }
+  };
   int ra[C::LA], ca[C::LA], la_off[C::LA];
   bool a_on[C::LA];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
+    const int q = wave * C::LA + i;
     if constexpr (FA == MX_FP4) {
-      ra[i] = 32 * wave + (lane >> 1);
-      ca[i] = 16 * ((lane & 1) ^ swz32(ra[i]));
-      la_off[i] = wave * 1024;
+      assign64(q, ra[i], ca[i]);
+      la_off[i] = q * 1024;
       a_on[i] = true;
     } else {
-      const int slot = 2 * wave + i;  // 16 slots of 768 B
-      ra[i] = 16 * slot + lane / 3;
-      ca[i] = 16 * (lane % 3);
-      la_off[i] = slot * 768;
+      constexpr int PIECES = C::A_ROW / 16;  // 3 or 6 pieces per row
+      constexpr int ROWS = 48 / PIECES;      // rows per 768 B slot
+      ra[i] = ROWS * q + lane / PIECES;
+      ca[i] = 16 * (lane % PIECES);
+      la_off[i] = q * 768;
       a_on[i] = lane < 48;
     }
   }
-  const int rb = 32 * wave + (lane >> 1);
-  const int cb = 16 * ((lane & 1) ^ swz32(rb));
-  const int lb_off = C::A_BYTES + wave * 1024;
+  int rb[C::LB], cb[C::LB], lb_off[C::LB];
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) {
+    const int q = wave * C::LB + i;
+    assign64(q, rb[i], cb[i]);
+    lb_off[i] = C::A_BYTES + q * 1024;
+  }
   const bool s_on = lane < 8;
   const bool s_is_a = wave < 4;
   const int s_row0 = 64 * (wave & 3) + 8 * lane;  // first tile row of this lane's 16 scale bytes
   const int ls_off = C::SA_OFF + wave * 128;
 
   const uint8_t* ga[C::LA];
-  const uint8_t* gb;
+  const uint8_t* gb[C::LB];
   const uint8_t* gs;
   int64_t s_pitch = 0;  // bytes between the scale slabs of consecutive steps
   int m0 = 0, n0 = 0;
@@ -195,7 +215,8 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     n0 = tn * MX_BN;
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) ga[i] = g.a + (int64_t)min(m0 + ra[i], g.m - 1) * a_rowb + ca[i];
-    gb = g.b + (int64_t)min(n0 + rb, g.n - 1) * b_rowb + cb;
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * b_rowb + cb[i];
     // Scale chunk of 8 rows: clamped to the last whole chunk of the (8-padded) slab.
     if (s_is_a) {
       const int64_t r = min((int64_t)m0 + s_row0, g.m8 - 8);
@@ -211,9 +232,12 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     uint8_t* base = lds + slot * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::LA; ++i)
-      if (a_on[i]) dma16(ga[i] + (int64_t)kt * MxFmt<FA>::STEP_BYTES, base + la_off[i]);
-    dma16(gb + (int64_t)kt * 32, base + lb_off);
-    if (s_on) dma16(gs + (int64_t)kt * s_pitch, base + ls_off);
+      if (a_on[i]) dma16(ga[i] + (int64_t)kt * C::A_ROW, base + la_off[i]);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) dma16(gb[i] + (int64_t)kt * C::B_ROW, base + lb_off[i]);
+#pragma unroll
+    for (int sub = 0; sub < S; ++sub)
+      if (s_on) dma16(gs + (int64_t)(kt * S + sub) * s_pitch, base + ls_off + sub * 1024);
   };
   auto issue_prologue = [&]() {
 #pragma unroll
@@ -221,47 +245,52 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       if (s < nk) issue(s, s);
   };
 
-  // ---- fragment offsets: rows 32*blk + (lane & 31), K half lane >> 5.
+  // ---- fragment offsets: rows 32*blk + (lane & 31); sub-step u, K half lane >> 5.
   const int rl = lane & 31;
   const int kh = lane >> 5;
-  int fa_off;
-  if constexpr (FA == MX_FP4) {
-    fa_off = (wm * MX_WTM + rl) * 32 + 16 * (kh ^ swz32(rl));
-  } else {
-    fa_off = (wm * MX_WTM + rl) * 48 + 24 * kh;
+  int fa_off[S], fb_off[S];
+#pragma unroll
+  for (int u = 0; u < S; ++u) {
+    if constexpr (FA == MX_FP4) {
+      fa_off[u] = (wm * MX_WTM + rl) * C::A_ROW +
+                  16 * (S == 2 ? ((2 * u + kh) ^ swz64(rl)) : (kh ^ swz32(rl)));
+    } else {
+      fa_off[u] = (wm * MX_WTM + rl) * C::A_ROW + 48 * u + 24 * kh;
+    }
+    fb_off[u] = C::A_BYTES + (wn * MX_WTN + rl) * C::B_ROW +
+                16 * (S == 2 ? ((2 * u + kh) ^ swz64(rl)) : (kh ^ swz32(rl)));
   }
-  const int fb_off = C::A_BYTES + (wn * MX_WTN + rl) * 32 + 16 * (kh ^ swz32(rl));
   const int fsa_off = C::SA_OFF + (wm * MX_WTM + rl) * 2 + kh;
   const int fsb_off = C::SA_OFF + 512 + (wn * MX_WTN + rl) * 2 + kh;
 
-  // Operands of one step: A fragments (4 or 6 dwords), B fragments, scale bytes.
+  // Operands of one sub-step: A fragments (4 or 6 dwords), B fragments, scale bytes.
   struct Frag {
     v8i a[MX_MBLK];
     v8i b[MX_NBLK];
     int sa[MX_MBLK];
     int sb[MX_NBLK];
   };
-  auto load_step = [&](int slot, Frag& f) {
+  auto load_sub = [&](int slot, int u, Frag& f) {
     const uint8_t* st = lds + slot * C::STAGE;
 #pragma unroll
     for (int nb = 0; nb < MX_NBLK; ++nb) {
-      const v4i w = *reinterpret_cast<const v4i*>(st + fb_off + nb * 32 * 32);
+      const v4i w = *reinterpret_cast<const v4i*>(st + fb_off[u] + nb * 32 * C::B_ROW);
       f.b[nb] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
-      f.sb[nb] = st[fsb_off + nb * 32 * 2];
+      f.sb[nb] = st[fsb_off + u * 1024 + nb * 32 * 2];
     }
 #pragma unroll
     for (int mb = 0; mb < MX_MBLK; ++mb) {
       if constexpr (FA == MX_FP4) {
-        const v4i w = *reinterpret_cast<const v4i*>(st + fa_off + mb * 32 * 32);
+        const v4i w = *reinterpret_cast<const v4i*>(st + fa_off[u] + mb * 32 * C::A_ROW);
         f.a[mb] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
       } else {
-        const uint8_t* p = st + fa_off + mb * 32 * 48;
+        const uint8_t* p = st + fa_off[u] + mb * 32 * C::A_ROW;
         const u2v w0 = *reinterpret_cast<const u2v*>(p);
         const u2v w1 = *reinterpret_cast<const u2v*>(p + 8);
         const u2v w2 = *reinterpret_cast<const u2v*>(p + 16);
         f.a[mb] = v8i{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
       }
-      f.sa[mb] = st[fsa_off + mb * 32 * 2];
+      f.sa[mb] = st[fsa_off + u * 1024 + mb * 32 * 2];
     }
   };
 
@@ -272,6 +301,10 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int mb = 0; mb < MX_MBLK; ++mb)
       acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[nb], f.a[mb], acc[mb][nb], MX_FP4, FA, 0,
                                                                     f.sb[nb], 0, f.sa[mb]);
+  };
+  auto mma_sub = [&](const Frag& f) {
+#pragma unroll
+    for (int nb = 0; nb < MX_NBLK; ++nb) mma_nb(f, nb);
   };
   auto wait_loads = [&](int later) {  // at most `later` load groups may stay in flight
     if (later >= 4) {
@@ -297,39 +330,69 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
       for (int j = 0; j < MX_NBLK; ++j) acc[i][j] = v16f{};
 
-    // Step kt: the MFMAs of weight block 0 run on operands read during step kt-1; then
-    // every wave waits for its loads of step kt+1 and meets the others at a barrier,
-    // which publishes stage kt+1 and certifies that stage kt-1 is no longer read; that
-    // stage receives step kt+NST-1 and the operands of step kt+1 are read while the
-    // MFMAs of weight block 1 run.
     Frag f0, f1;
     wait_loads(min(C::NST - 2, nk - 1));
     barrier_nofence();
-    load_step(0, f0);
+    load_sub(0, 0, f0);
     int kt = 0, slot = 0;
-    for (; kt < nk - (C::NST - 1); ++kt) {
-      const int next = slot + 1 == C::NST ? 0 : slot + 1;
-      const int refill = slot == 0 ? C::NST - 1 : slot - 1;
-      mma_nb(f0, 0);
-      wait_vmcnt<(C::NST - 3) * C::L>();
-      barrier_nofence();
-      issue(kt + C::NST - 1, refill);
-      load_step(next, f1);
-      mma_nb(f0, 1);
-      f0 = f1;
-      slot = next;
-    }
-    for (; kt < nk; ++kt) {
-      const int next = slot + 1 == C::NST ? 0 : slot + 1;
-      mma_nb(f0, 0);
-      if (kt + 1 < nk) {
-        wait_loads(nk - 2 - kt);
+    if constexpr (S == 2) {
+      // Stage kt holds two sub-steps.  The second sub-step's operands are read while the
+      // first one's MFMAs run; in the middle of the stage every wave waits for its loads
+      // of stage kt+1 and meets the others at a barrier, which publishes stage kt+1 and
+      // certifies that stage kt-1 is no longer read; that stage receives stage kt+NST-1,
+      // and the first sub-step of stage kt+1 is read while the second one's MFMAs run.
+      for (; kt < nk - (C::NST - 1); ++kt) {
+        const int next = slot + 1 == C::NST ? 0 : slot + 1;
+        const int refill = slot == 0 ? C::NST - 1 : slot - 1;
+        load_sub(slot, 1, f1);
+        mma_sub(f0);
+        wait_vmcnt<(C::NST - 3) * C::L>();
         barrier_nofence();
-        load_step(next, f1);
+        issue(kt + C::NST - 1, refill);
+        load_sub(next, 0, f0);
+        mma_sub(f1);
+        slot = next;
       }
-      mma_nb(f0, 1);
-      f0 = f1;
-      slot = next;
+      for (; kt < nk; ++kt) {
+        const int next = slot + 1 == C::NST ? 0 : slot + 1;
+        load_sub(slot, 1, f1);
+        mma_sub(f0);
+        if (kt + 1 < nk) {
+          wait_loads(nk - 2 - kt);
+          barrier_nofence();
+          load_sub(next, 0, f0);
+        }
+        mma_sub(f1);
+        slot = next;
+      }
+    } else {
+      // One sub-step per stage: the MFMAs of weight block 0 run on operands read during
+      // stage kt-1, then the barrier as above, then the operands of stage kt+1 are read
+      // while the MFMAs of weight block 1 run.
+      for (; kt < nk - (C::NST - 1); ++kt) {
+        const int next = slot + 1 == C::NST ? 0 : slot + 1;
+        const int refill = slot == 0 ? C::NST - 1 : slot - 1;
+        mma_nb(f0, 0);
+        wait_vmcnt<(C::NST - 3) * C::L>();
+        barrier_nofence();
+        issue(kt + C::NST - 1, refill);
+        load_sub(next, 0, f1);
+        mma_nb(f0, 1);
+        f0 = f1;
+        slot = next;
+      }
+      for (; kt < nk; ++kt) {
+        const int next = slot + 1 == C::NST ? 0 : slot + 1;
+        mma_nb(f0, 0);
+        if (kt + 1 < nk) {
+          wait_loads(nk - 2 - kt);
+          barrier_nofence();
+          load_sub(next, 0, f1);
+        }
+        mma_nb(f0, 1);
+        f0 = f1;
+        slot = next;
+      }
     }
 
     // ------------------------------------------------------------ epilogue
@@ -444,12 +507,23 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uin
   g.tiles_n = (int)((n + MX_BN - 1) / MX_BN);
   const int tiles = g.tiles_m * g.tiles_n;
   const int grid = tiles < persistent_blocks() ? tiles : persistent_blocks();
-#define MXG(F, O) hipLaunchKernelGGL((k_mxgemm<F, O>), dim3(grid), dim3(MX_NT), 0, st, g)
+  // Two 64-deep sub-steps per ring stage for FP4 activations when K allows it (with FP6
+  // the doubled operand registers do not fit).
+  const bool two = fa == MX_FP4 && k % 128 == 0;
+#define MXG(F, SS, O) hipLaunchKernelGGL((k_mxgemm<F, SS, O>), dim3(grid), dim3(MX_NT), 0, st, g)
+#define MXO(F, SS)                \
+  if (out_dt == DT_F16)           \
+    MXG(F, SS, DT_F16);           \
+  else if (out_dt == DT_BF16)     \
+    MXG(F, SS, DT_BF16);          \
+  else                            \
+    MXG(F, SS, DT_F32)
   if (fa == MX_FP4) {
-    if (out_dt == DT_F16) MXG(MX_FP4, DT_F16); else if (out_dt == DT_BF16) MXG(MX_FP4, DT_BF16); else MXG(MX_FP4, DT_F32);
+    if (two) { MXO(MX_FP4, 2); } else { MXO(MX_FP4, 1); }
   } else {
-    if (out_dt == DT_F16) MXG(MX_FP6, DT_F16); else if (out_dt == DT_BF16) MXG(MX_FP6, DT_BF16); else MXG(MX_FP6, DT_F32);
+    MXO(MX_FP6, 1);
   }
+#undef MXO
 #undef MXG
   return hipGetLastError();
 }
