@@ -37,22 +37,43 @@
 
 namespace vqk {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
 constexpr int NT = 512;           // threads per workgroup
 constexpr int WTM = 128, WTN = 64;  // wave tile
 constexpr int MBLK = WTM / 32, NBLK = WTN / 32;
 
-template <int BBITS>
+// A ring stage holds H k-halves of 32 codes (BK = 32 H codes); one barrier per stage.
+template <int BBITS, int H>
 struct GCfg {
-  static constexpr int A_BYTES = BM * 64;
-  static constexpr int B_ROW = BBITS == 8 ? 64 : 32;
+  static constexpr int BK = 32 * H;
+  static constexpr int A_ROW = BK;                            // int8 codes
+  static constexpr int B_ROW = BBITS == 8 ? BK : BK / 2;      // int8 codes or packed nibbles
+  static constexpr int A_BYTES = BM * A_ROW;
   static constexpr int B_BYTES = BN * B_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NST = BBITS == 8 ? 4 : 5;
-  static constexpr int LA = A_BYTES / (NT * 16);  // 16-byte loads per thread per step
+  static constexpr int NST = H == 4 ? 3 : (BBITS == 8 ? 4 : 5);
+  static constexpr int LA = A_BYTES / (NT * 16);  // 16-byte loads per thread per stage
   static constexpr int LB = B_BYTES / (NT * 16);
   static constexpr int L = LA + LB;
 };
+
+// Swizzle and direct-load lane mapping of a row width: a 1 KB load covers 1024/W rows,
+// lane -> (row, 16-byte position), the position holding chunk position ^ swz(row).
+// A 16-lane group of 16-byte fragment reads covers the 64 banks once when the chunks of
+// its 16 rows land on distinct 16-byte bank groups: with 128-byte rows, rows r and r+1
+// start half a bank line apart, so the eight chunk positions are spread over r >> 1.
+template <int W>
+__device__ __forceinline__ int swz_row(int r) {
+  if constexpr (W == 32) return swz32(r);
+  else if constexpr (W == 64) return swz64(r);
+  else return (r >> 1) & 7;
+}
+template <int W>
+__device__ __forceinline__ void dma_lane(int q, int lane, int& row, int& col) {
+  constexpr int LPR = W / 16;  // lanes per row
+  row = (1024 / W) * q + lane / LPR;
+  col = 16 * ((lane % LPR) ^ swz_row<W>(row));
+}
 
 struct GArgs {
   const int8_t* a;
@@ -79,9 +100,11 @@ __device__ __forceinline__ v4i unpack_int4x16(u2v w) {
   return r;
 }
 
-template <int BBITS, int OUT_DT, bool DUAL>
+template <int BBITS, int OUT_DT, bool DUAL, int H>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm(GArgs g) {
-  using C = GCfg<BBITS>;
+  static_assert(!DUAL || H == 2, "the outlier partition is staged in 64-code stages");
+  using C = GCfg<BBITS, H>;
+  constexpr int BK = C::BK;
   constexpr int P = DUAL ? 2 : 1;
   constexpr bool HALF_OUT = OUT_DT != DT_F32;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
@@ -96,26 +119,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int nk = g.k0 / BK;
 
   // ---- direct-load assignment: instruction q of this wave fills 1 KB of a stage.
-  // A: 16 rows x 64 B per instruction, lane -> (row, position) = (lane >> 2, lane & 3).
   int ra[C::LA], rb[C::LB];  // tile-local rows loaded by this lane
   int la_off[C::LA], lb_off[C::LB], ca[C::LA], cb[C::LB];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
     const int q = wave * C::LA + i;
-    ra[i] = 16 * q + (lane >> 2);
-    ca[i] = 16 * ((lane & 3) ^ swz64(ra[i]));
+    dma_lane<C::A_ROW>(q, lane, ra[i], ca[i]);
     la_off[i] = q * 1024;
   }
 #pragma unroll
   for (int i = 0; i < C::LB; ++i) {
     const int q = wave * C::LB + i;
-    if constexpr (BBITS == 8) {
-      rb[i] = 16 * q + (lane >> 2);
-      cb[i] = 16 * ((lane & 3) ^ swz64(rb[i]));
-    } else {
-      rb[i] = 32 * q + (lane >> 1);
-      cb[i] = 16 * ((lane & 1) ^ swz32(rb[i]));
-    }
+    dma_lane<C::B_ROW>(q, lane, rb[i], cb[i]);
     lb_off[i] = C::A_BYTES + q * 1024;
   }
   const int64_t ldb = BBITS == 8 ? g.kp : g.kp / 2;
@@ -168,28 +183,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // ---- fragment offsets (per lane, constant): rows 32*blk + (lane & 31), k-half h:
-  // 16-byte chunk 2h + (lane >> 5) of the 64-code row.
+  // 16-byte chunk 2h + (lane >> 5) of the int8 row; 8 bytes (lane >> 5) of chunk h of a
+  // packed 4-bit row.
   const int rl = lane & 31;
   const int kc = lane >> 5;
-  int fa[2], fb[2];
+  int fa[H], fb[H];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    fa[h] = (wm * WTM + rl) * 64 + 16 * ((2 * h + kc) ^ swz64(rl));
+  for (int h = 0; h < H; ++h) {
+    fa[h] = (wm * WTM + rl) * C::A_ROW + 16 * ((2 * h + kc) ^ swz_row<C::A_ROW>(rl));
     if constexpr (BBITS == 8) {
-      fb[h] = C::A_BYTES + (wn * WTN + rl) * 64 + 16 * ((2 * h + kc) ^ swz64(rl));
+      fb[h] = C::A_BYTES + (wn * WTN + rl) * C::B_ROW + 16 * ((2 * h + kc) ^ swz_row<C::B_ROW>(rl));
     } else {
-      fb[h] = C::A_BYTES + (wn * WTN + rl) * 32 + 16 * (h ^ swz32(rl)) + 8 * kc;
+      fb[h] = C::A_BYTES + (wn * WTN + rl) * C::B_ROW + 16 * (h ^ swz_row<C::B_ROW>(rl)) + 8 * kc;
     }
   }
   auto afrag = [&](int slot, int h, int mb) -> v4i {
-    return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fa[h] + mb * 32 * 64);
+    return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fa[h] + mb * 32 * C::A_ROW);
   };
   // B fragment as stored (int8 codes, or the 8 packed bytes in .xy for 4-bit weights).
   auto braw = [&](int slot, int h, int nb) -> v4i {
     if constexpr (BBITS == 8) {
-      return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 64);
+      return *reinterpret_cast<const v4i*>(lds + slot * C::STAGE + fb[h] + nb * 32 * C::B_ROW);
     } else {
-      const u2v w = *reinterpret_cast<const u2v*>(lds + slot * C::STAGE + fb[h] + nb * 32 * 32);
+      const u2v w = *reinterpret_cast<const u2v*>(lds + slot * C::STAGE + fb[h] + nb * 32 * C::B_ROW);
       return v4i{(int)w.x, (int)w.y, 0, 0};
     }
   };
@@ -252,57 +268,59 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
 
-    // Half-step software pipeline.  Step kt uses stage kt % NST; its second half's
-    // fragments are read while the first half's MFMAs run.  In the middle of the step
-    // every wave waits for its loads of step kt+1 and meets the others at a barrier,
-    // which publishes stage kt+1 and certifies that stage kt-1 is no longer read; that
-    // stage then receives step kt+NST-1, and the first half of step kt+1 is read while
-    // the second half of step kt runs.
-    Frag f0, f1;
+    // Software pipeline over k-halves.  Stage kt holds H k-halves; each half's MFMAs run
+    // while the next half's fragments are read.  Before the last half every wave waits for
+    // its loads of stage kt+1 and meets the others at a barrier, which publishes stage
+    // kt+1 and certifies that stage kt-1 is no longer read; that stage then receives stage
+    // kt+NST-1, and the first half of stage kt+1 is read while the last half of stage kt
+    // runs.  (H is even, so the next stage's first half lands in F[0].)
+    Frag F[2];
     wait_loads(min(C::NST - 2, nk - 1));
     barrier_nofence();
-    load_half(0, 0, f0);
+    load_half(0, 0, F[0]);
     int kt = 0, slot = 0;
-    // Steady state: every step refills a stage and keeps NST-3 load groups in flight.
-    // The body has no branch, so the waits the compiler inserts for the fragments stay
-    // partial (lgkmcnt of the reads issued later) instead of draining all LDS reads.
-    for (; kt < nk - (C::NST - 1); ++kt) {
-      const int next = slot + 1 == C::NST ? 0 : slot + 1;
-      const int refill = slot == 0 ? C::NST - 1 : slot - 1;
-      // First half: MFMAs on f0 with the reads of f1 interleaved between them.
-      load_half(slot, 1, f1);
-      mma_half(f0);
+    auto interleave = [&]() {
 #pragma unroll
       for (int i = 0; i < MBLK + NBLK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
       __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
+    };
+    // Steady state: every stage refills a stage and keeps NST-3 load groups in flight.
+    // The body has no branch, so the waits the compiler inserts for the fragments stay
+    // partial (lgkmcnt of the reads issued later) instead of draining all LDS reads.
+    for (; kt < nk - (C::NST - 1); ++kt) {
+      const int next = slot + 1 == C::NST ? 0 : slot + 1;
+      const int refill = slot == 0 ? C::NST - 1 : slot - 1;
+#pragma unroll
+      for (int h = 0; h < H - 1; ++h) {
+        load_half(slot, h + 1, F[(h + 1) & 1]);
+        mma_half(F[h & 1]);
+        interleave();
+      }
       wait_vmcnt<(C::NST - 3) * C::L>();
       barrier_nofence();
       issue((kt + C::NST - 1) * BK, refill);
-      // Second half: MFMAs on f1 with the reads of the next step's f0 interleaved.
-      load_half(next, 0, f0);
-      mma_half(f1);
-#pragma unroll
-      for (int i = 0; i < MBLK + NBLK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, MBLK * NBLK - (MBLK + NBLK), 0);
+      load_half(next, 0, F[0]);
+      mma_half(F[(H - 1) & 1]);
+      interleave();
       slot = next;
     }
-    // Last NST-1 steps: nothing left to load; fewer groups in flight each step.
+    // Last NST-1 stages: nothing left to load; fewer groups in flight each stage.
     for (; kt < nk; ++kt) {
       const int next = slot + 1 == C::NST ? 0 : slot + 1;
-      load_half(slot, 1, f1);
-      mma_half(f0);
+#pragma unroll
+      for (int h = 0; h < H - 1; ++h) {
+        load_half(slot, h + 1, F[(h + 1) & 1]);
+        mma_half(F[h & 1]);
+      }
       if (kt + 1 < nk) {
         wait_loads(nk - 2 - kt);
         barrier_nofence();
-        load_half(next, 0, f0);
+        load_half(next, 0, F[0]);
       }
-      mma_half(f1);
+      mma_half(F[(H - 1) & 1]);
       slot = next;
     }
 
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       // Outlier partition [k0, kp): at most two 64-code steps, staged in stages 0-1.
       steps1 = (g.kp - g.k0) / BK;
       issue(g.k0, 0);
-      if (steps1 > 1) issue(g.k0 + BK, 1);
+      if (steps1 > 1) issue(g.k0 + BK, 1);  // (H == 2 here: BK = 64)
       wait_vmcnt<0>();
       barrier_nofence();
     } else {
@@ -436,9 +454,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 template <int BBITS, int OUT_DT>
 static hipError_t launch_dual(const GArgs& a, bool dual, int grid, hipStream_t st) {
   if (dual)
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, 2>), dim3(grid), dim3(NT), 0, st, a);
+  else if (BBITS == 4 && a.k0 % 128 == 0)  // 4-bit weights: 128-code stages
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, BBITS == 4 ? 4 : 2>), dim3(grid), dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, 2>), dim3(grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
