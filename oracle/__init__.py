@@ -24,8 +24,10 @@ Steps and the passages they follow:
 * ``linear``    the whole layer, chaining the steps above.
 * ``decompose`` residual re-quantization of selected tokens, added back through a
                 second accumulator (SemanticDialect page, Methodology 2.2).
+* ``calib``     static per-tensor activation scale by clipping-percentile search
+                (Q-ARVD page, Technical details: learned clipping percentile and scale).
 * ``mx``        MX block formats (FP4 E2M1, FP6 E2M3, E8M0 block scales of 32) and their
                 exact GEMM: the 4-bit floating-point route of the 6Bit-Diffusion page
                 (Methodology B.1) in the form gfx950's scaled MFMA consumes.
 """
-from . import numerics, detect, quantizer, fwht, gemm, route, linear, decompose, mx  # noqa: F401
+from . import numerics, detect, quantizer, fwht, gemm, route, linear, decompose, mx, calib  # noqa: F401
