@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--mx", choices=["fp4", "fp6"], default=None,
                    help="route the activations through the MX block formats (MXFP4 weights) on the scaled "
                         "MFMA; with --config 5 the layers routed to 4 bits take MXFP4, the others INT8")
+    p.add_argument("--calibrate", action="store_true",
+                   help="only time the static-scale calibration (clipping-percentile search) on the "
+                        "workload's activations and exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times) and exit; "
                         "rocprofv3 counters of that copy scale FETCH_SIZE/WRITE_SIZE to bytes")
@@ -238,6 +241,32 @@ def cpu_baseline(cfg, budget_s):
                       f"steps: activation quantization, exact integer GEMM (float64 BLAS), float32 epilogue"}
 
 
+def calibrate(args, vq, gen, torch, dev):
+    """Time the clipping-percentile search on the workload's activations (whole call, wall clock).
+
+    The call runs the |x| histogram kernel, copies the histogram back and scores every
+    candidate on the host; rocprofv3 gives the kernel's own duration.
+    """
+    x = gen.make_x(args.config).to(dev)
+    hist = torch.empty(int(vq._lib.vq_calib_hist_bins()), dtype=torch.int32, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        r = vq.vq_calib_static_scale(x, 8, scale=scale, hist=hist)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r = vq.vq_calib_static_scale(x, 8, scale=scale, hist=hist)
+    call_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    nbytes = x.numel() * x.element_size()
+    print(json.dumps({
+        "metric": "static-scale calibration call time", "value": round(call_ms, 4), "unit": "ms",
+        "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": gen.CONFIGS[args.config]["name"] + "_activations", "rows": x.shape[0],
+                   "cols": x.shape[1], "bits": 8, "candidates": len(r["mse"])},
+        "best_percentile": vq.CALIB_GRID[r["best"]], "scale": r["scales"][r["best"]],
+        "input_bytes": nbytes, "call_gbs": round(nbytes / (call_ms * 1e-3) / 1e9, 1)}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -260,6 +289,9 @@ def main():
     import gen
 
     dev = torch.device("cuda:0")
+    if args.calibrate:
+        calibrate(args, vq, gen, torch, dev)
+        return
     L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx)
     stream = torch.cuda.current_stream(dev)
 

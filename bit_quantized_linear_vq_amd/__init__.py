@@ -29,8 +29,9 @@ EXPORTS = (
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
     "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
-    "vq_status_string", "vq_last_hip_error", "vq_version",
+    "vq_calib_hist_bins", "vq_calib_static_scale", "vq_status_string", "vq_last_hip_error", "vq_version",
 )
+CALIB_GRID = (100.0, 99.999, 99.99, 99.9, 99.8, 99.5, 99.0, 98.0, 97.0, 95.0, 90.0)
 
 _DT = {torch.float16: VQ_F16, torch.bfloat16: VQ_BF16, torch.float32: VQ_F32}
 _GRAN = {"tensor": VQ_PER_TENSOR, "token": VQ_PER_TOKEN, "static": VQ_PER_TENSOR_STATIC}
@@ -69,6 +70,8 @@ def _load():
         "vq_mx_scale_bytes": (I64, [I64, I64]),
         "vq_mx_quant": (I, [P, I, I64, I64, I64, I, P, P, P]),
         "vq_mx_gemm": (I, [P, P, I, P, P, I, I64, I64, I64, P, I, I64, P]),
+        "vq_calib_hist_bins": (I64, []),
+        "vq_calib_static_scale": (I, [P, I, I64, I64, I64, I, P, I32, P, P, P, P, P, P, P]),
         "vq_status_string": (ctypes.c_char_p, [I]),
         "vq_last_hip_error": (I, []),
         "vq_version": (ctypes.c_char_p, []),
@@ -288,3 +291,28 @@ def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: 
         _ptr(a), _ptr(sa), _MX.get(fa, -1), _ptr(b), _ptr(sb), _MX.get(fb, -1), m, n, k,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _stream(a)))
     return y
+
+
+def vq_calib_static_scale(x: torch.Tensor, bits: int, percentiles=CALIB_GRID, scale=None, hist=None):
+    """Clipping-percentile search of a static per-tensor scale for x.
+
+    Returns dict(clips, scales, mse, best, scale): host arrays over the candidates and the
+    chosen scale as a device float [1] ready for vq_quant_act(..., "static", static_scale=...).
+    """
+    _dev(x, "x")
+    rows, cols = x.shape
+    n = len(percentiles)
+    pct = (ctypes.c_double * n)(*percentiles)
+    clips = (ctypes.c_float * n)()
+    scales = (ctypes.c_float * n)()
+    mse = (ctypes.c_double * n)()
+    best = ctypes.c_int32(0)
+    if hist is None:
+        hist = torch.empty(int(_lib.vq_calib_hist_bins()), dtype=torch.int32, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check("vq_calib_static_scale", _lib.vq_calib_static_scale(
+        _ptr(x), _DT.get(x.dtype, -1), rows, cols, x.stride(0), bits, pct, n, _ptr(hist),
+        clips, scales, mse, ctypes.byref(best), _ptr(scale), _stream(x)))
+    return {"clips": list(clips), "scales": list(scales), "mse": list(mse), "best": best.value, "scale": scale,
+            "hist": hist}

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvq.so")
 
-SOURCES = ["k_quant.hip", "k_hadamard.hip", "k_qgemm.hip", "k_detect_route.hip", "k_decompose.hip", "k_mx.hip", "vq_api.cpp"]
+SOURCES = ["k_quant.hip", "k_hadamard.hip", "k_qgemm.hip", "k_detect_route.hip", "k_decompose.hip", "k_mx.hip", "k_calib.hip", "vq_api.cpp"]
 
 ARCH = os.environ.get("VQ_OFFLOAD_ARCH", "gfx950")
 

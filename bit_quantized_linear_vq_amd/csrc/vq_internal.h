@@ -64,6 +64,9 @@ hipError_t launch_mx_quant(const void* x, int dtype, int64_t ldx, int64_t rows, 
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uint8_t* b, const uint8_t* sb, int64_t m,
                           int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, hipStream_t st);
 
+int calib_hist_bins();
+hipError_t launch_abs_hist(const void* x, int64_t rows, int64_t cols, int64_t ldx, unsigned* hist, hipStream_t st);
+
 int detect_row_chunks(int64_t rows);
 hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, double* ws,
                            hipStream_t st);

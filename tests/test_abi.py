@@ -317,3 +317,26 @@ def test_mx_gemm_validation(lib, kw, want):
     a.update(kw)
     assert lib.vq_mx_gemm(a["a"], a["sa"], a["fa"], a["b"], a["sb"], a["fb"], a["m"], a["n"], a["k"], a["y"],
                           a["out"], a["ldy"], a["stream"]) == want
+
+
+def test_calib_validation(lib):
+    assert lib.vq_calib_hist_bins() == 32768
+    pct = (ctypes.c_double * 2)(100.0, 99.9)
+    bad_pct = (ctypes.c_double * 2)(100.0, 0.0)
+    f = (ctypes.c_float * 2)()
+    d = (ctypes.c_double * 2)()
+    best = ctypes.c_int32(0)
+
+    def call(x=FAKE, dt=BF16, rows=64, cols=128, ldx=128, bits=8, p=pct, n=2, hist=FAKE):
+        return lib.vq_calib_static_scale(x, dt, rows, cols, ldx, bits, p, n, hist, f, f, d, ctypes.byref(best),
+                                         NULL, NULL)
+    assert call(x=NULL) == INVALID
+    assert call(hist=NULL) == INVALID
+    assert call(dt=F32) == INVALID
+    assert call(n=0) == INVALID
+    assert call(p=bad_pct) == INVALID
+    assert call(ldx=100) == INVALID
+    assert call(bits=5) == UNSUP
+    assert call(rows=70000, cols=65536, ldx=65536) == UNSUP
+    assert call(cols=100, ldx=100) == SHAPE
+    assert call(x=ctypes.c_void_p(0x10008)) == SHAPE
