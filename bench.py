@@ -242,10 +242,11 @@ def cpu_baseline(cfg, budget_s):
 
 
 def calibrate(args, vq, gen, torch, dev):
-    """Time the clipping-percentile search on the workload's activations (whole call, wall clock).
+    """Time the clipping-percentile search on the workload's activations.
 
-    The call runs the |x| histogram kernel, copies the histogram back and scores every
-    candidate on the host; rocprofv3 gives the kernel's own duration.
+    One call = a fill of the histogram, the |x| histogram kernel (one HBM pass), the
+    per-candidate search kernel and the pick; the time is taken between synchronizations
+    around `steps` calls, and rocprofv3 gives each kernel's duration.
     """
     x = gen.make_x(args.config).to(dev)
     hist = torch.empty(int(vq._lib.vq_calib_hist_bins()), dtype=torch.int32, device=dev)
@@ -256,14 +257,15 @@ def calibrate(args, vq, gen, torch, dev):
     t0 = time.perf_counter()
     for _ in range(args.steps):
         r = vq.vq_calib_static_scale(x, 8, scale=scale, hist=hist)
+    torch.cuda.synchronize()
     call_ms = (time.perf_counter() - t0) / args.steps * 1e3
     nbytes = x.numel() * x.element_size()
     print(json.dumps({
         "metric": "static-scale calibration call time", "value": round(call_ms, 4), "unit": "ms",
         "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
         "config": {"workload": gen.CONFIGS[args.config]["name"] + "_activations", "rows": x.shape[0],
-                   "cols": x.shape[1], "bits": 8, "candidates": len(r["mse"])},
-        "best_percentile": vq.CALIB_GRID[r["best"]], "scale": r["scales"][r["best"]],
+                   "cols": x.shape[1], "bits": 8, "candidates": r["mse"].numel()},
+        "best_percentile": vq.CALIB_GRID[int(r["best"].item())], "scale": r["scale"].item(),
         "input_bytes": nbytes, "call_gbs": round(nbytes / (call_ms * 1e-3) / 1e9, 1)}))
 
 

@@ -100,8 +100,31 @@ def _ptr(t):
 
 
 def _dev(t, name):
+    """A device tensor whose last dimension is dense (the library takes a row pitch only)."""
     if not (isinstance(t, torch.Tensor) and t.is_cuda):
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() > 2 or (t.dim() >= 1 and t.size(-1) > 1 and t.stride(-1) != 1):
+        raise ValueError(f"{name} must be 1-D or 2-D with unit stride along its last dimension")
+    return t
+
+
+def _buf(t, name, nbytes, device):
+    """A caller-given output or scratch buffer: a contiguous device tensor of at least nbytes bytes."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.device == device):
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} are needed")
+    return t
+
+
+def _out2d(t, name, rows, cols, device):
+    """A caller-given [rows x cols] output with unit stride along its rows (any row pitch >= cols)."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.device == device):
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor on {device}")
+    if tuple(t.shape) != (rows, cols) or (cols > 1 and t.stride(1) != 1) or (rows > 1 and t.stride(0) < cols):
+        raise ValueError(f"{name} must be [{rows} x {cols}] with unit stride along its rows")
     return t
 
 
@@ -119,6 +142,7 @@ def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kf
     rows, cols = x.shape
     if ws is None:
         ws = torch.empty(int(_lib.vq_detect_workspace_elems(rows, cols)), dtype=torch.float64, device=x.device)
+    _buf(ws, "ws", 8 * int(_lib.vq_detect_workspace_elems(rows, cols)), x.device)
     norms = torch.empty(cols, dtype=torch.float64)
     mask = torch.empty(cols, dtype=torch.uint8)
     idx = torch.empty(cols, dtype=torch.int32)
@@ -141,6 +165,8 @@ def vq_pack_weights(w: torch.Tensor, bits: int, idx: torch.Tensor | None = None,
                  else torch.empty((n, kp // 2), dtype=torch.uint8, device=w.device))
     if scales is None:
         scales = torch.empty((n, 2) if n_out else (n,), dtype=torch.float32, device=w.device)
+    _buf(codes, "codes", n * (kp if bits == 8 else kp // 2), w.device)
+    _buf(scales, "scales", 4 * n * (2 if n_out else 1), w.device)
     _check("vq_pack_weights", _lib.vq_pack_weights(
         _ptr(w), _DT.get(w.dtype, -1), n, k, w.stride(0), bits, _ptr(idx), n_out, had_block,
         _ptr(codes), _ptr(scales), _stream(w)))
@@ -162,6 +188,8 @@ def vq_quant_act(x: torch.Tensor, bits: int, gran: str = "token", had_block: int
         parts = 2 if n_out else 1
         shape = ((m, 2) if n_out else (m,)) if g == VQ_PER_TOKEN else (parts,)
         scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _buf(codes, "codes", m * kp, x.device)
+    _buf(scales, "scales", 4 * (m if g == VQ_PER_TOKEN else 1) * (2 if n_out else 1), x.device)
     _check("vq_quant_act", _lib.vq_quant_act(
         _ptr(x), _DT.get(x.dtype, -1), m, k, x.stride(0), bits, _ptr(bits_dev), g, had_block,
         _ptr(idx), n_out, _ptr(static_scale), _ptr(codes), _ptr(scales), _stream(x)))
@@ -174,6 +202,7 @@ def vq_hadamard_block(x: torch.Tensor, out_dtype=None, normalize: bool = True, b
     rows, cols = x.shape
     if y is None:
         y = torch.empty((rows, cols), dtype=out_dtype or x.dtype, device=x.device)
+    _out2d(y, "y", rows, cols, x.device)
     _check("vq_hadamard_block", _lib.vq_hadamard_block(
         _ptr(x), _DT.get(x.dtype, -1), x.stride(0), _ptr(y), _DT.get(y.dtype, -1), y.stride(0), rows, cols,
         block, int(bool(normalize)), _stream(x)))
@@ -192,6 +221,9 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if acc_debug and acc is None:
         acc = torch.empty((2 if k0 < kp else 1, m, n), dtype=torch.int32, device=a.device)
+    _out2d(y, "y", m, n, a.device)
+    if acc_debug:
+        _buf(acc, "acc", 4 * (2 if k0 < kp else 1) * m * n, a.device)
     _check("vq_qgemm_dequant", _lib.vq_qgemm_dequant(
         _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None), _stream(a)))
@@ -209,6 +241,9 @@ def vq_route_rel_l1(x: torch.Tensor, y: torch.Tensor, threshold: float = 0.1, bi
         gamma = torch.empty(1, dtype=torch.float64, device=x.device)
     if bits is None:
         bits = torch.empty(1, dtype=torch.int32, device=x.device)
+    _buf(ws, "ws", 8 * int(_lib.vq_route_workspace_elems(n)), x.device)
+    _buf(gamma, "gamma", 8, x.device)
+    _buf(bits, "bits", 4, x.device)
     _check("vq_route_rel_l1", _lib.vq_route_rel_l1(
         _ptr(x), _ptr(y), _DT.get(x.dtype, -1), n, threshold, bits_hi, bits_lo, _ptr(ws), _ptr(gamma),
         _ptr(bits), _stream(x)))
@@ -229,6 +264,9 @@ def vq_quant_residual(x: torch.Tensor, rows: torch.Tensor, bits1: int, bits2: in
         codes = torch.empty((2 * n_rows, k), dtype=torch.int8, device=x.device)
     if scales is None:
         scales = torch.empty((2 * n_rows,), dtype=torch.float32, device=x.device)
+    _dev(rows, "rows")
+    _buf(codes, "codes", 2 * n_rows * k, x.device)
+    _buf(scales, "scales", 8 * n_rows, x.device)
     _check("vq_quant_residual", _lib.vq_quant_residual(
         _ptr(x), _DT.get(x.dtype, -1), m, k, x.stride(0), bits1, bits2, _ptr(rows), n_rows,
         _ptr(codes), _ptr(scales), _stream(x)))
@@ -251,6 +289,10 @@ def vq_qgemm_dequant_residual(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if ws is None and n_rows:
         ws = torch.empty(vq_residual_workspace_bytes(m, n_rows, n), dtype=torch.uint8, device=a.device)
+    _out2d(y, "y", m, n, a.device)
+    if n_rows:
+        _dev(rows, "rows")
+        _buf(ws, "ws", vq_residual_workspace_bytes(m, n_rows, n), a.device)
     _check("vq_qgemm_dequant_residual", _lib.vq_qgemm_dequant_residual(
         _ptr(a), _ptr(sa), _ptr(b), b_bits, _ptr(sb), m, n, kp, _ptr(a2), _ptr(sa2), _ptr(rows), n_rows,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(ws), _stream(a)))
@@ -273,6 +315,9 @@ def vq_mx_quant(x: torch.Tensor, fmt: str = "fp4", codes=None, scales=None):
         codes = torch.empty((rows, k * _MX_BITS[fmt] // 8), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(max(vq_mx_scale_bytes(rows, k), 1), dtype=torch.uint8, device=x.device)
+    if fmt in _MX:
+        _buf(codes, "codes", vq_mx_code_bytes(rows, k, fmt), x.device)
+        _buf(scales, "scales", vq_mx_scale_bytes(rows, k), x.device)
     _check("vq_mx_quant", _lib.vq_mx_quant(
         _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), _MX.get(fmt, -1), _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales
@@ -287,6 +332,7 @@ def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: 
     k = a.shape[1] * 8 // _MX_BITS[fa]
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _out2d(y, "y", m, n, a.device)
     _check("vq_mx_gemm", _lib.vq_mx_gemm(
         _ptr(a), _ptr(sa), _MX.get(fa, -1), _ptr(b), _ptr(sb), _MX.get(fb, -1), m, n, k,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _stream(a)))
@@ -294,25 +340,28 @@ def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: 
 
 
 def vq_calib_static_scale(x: torch.Tensor, bits: int, percentiles=CALIB_GRID, scale=None, hist=None):
-    """Clipping-percentile search of a static per-tensor scale for x.
+    """Clipping-percentile search of a static per-tensor scale for x (asynchronous).
 
-    Returns dict(clips, scales, mse, best, scale): host arrays over the candidates and the
-    chosen scale as a device float [1] ready for vq_quant_act(..., "static", static_scale=...).
+    Returns dict of device tensors: clips, scales (float32 [n]), mse (float64 [n]), best
+    (int32 [1]), scale (float32 [1], ready for vq_quant_act(..., "static",
+    static_scale=...)) and hist (the |x| histogram).
     """
     _dev(x, "x")
     rows, cols = x.shape
     n = len(percentiles)
     pct = (ctypes.c_double * n)(*percentiles)
-    clips = (ctypes.c_float * n)()
-    scales = (ctypes.c_float * n)()
-    mse = (ctypes.c_double * n)()
-    best = ctypes.c_int32(0)
+    kw = dict(device=x.device)
+    clips = torch.empty(n, dtype=torch.float32, **kw)
+    scales = torch.empty(n, dtype=torch.float32, **kw)
+    mse = torch.empty(n, dtype=torch.float64, **kw)
+    best = torch.empty(1, dtype=torch.int32, **kw)
     if hist is None:
-        hist = torch.empty(int(_lib.vq_calib_hist_bins()), dtype=torch.int32, device=x.device)
+        hist = torch.empty(int(_lib.vq_calib_hist_bins()), dtype=torch.int32, **kw)
     if scale is None:
-        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+        scale = torch.empty(1, dtype=torch.float32, **kw)
+    _buf(hist, "hist", 4 * int(_lib.vq_calib_hist_bins()), x.device)
+    _buf(scale, "scale", 4, x.device)
     _check("vq_calib_static_scale", _lib.vq_calib_static_scale(
         _ptr(x), _DT.get(x.dtype, -1), rows, cols, x.stride(0), bits, pct, n, _ptr(hist),
-        clips, scales, mse, ctypes.byref(best), _ptr(scale), _stream(x)))
-    return {"clips": list(clips), "scales": list(scales), "mse": list(mse), "best": best.value, "scale": scale,
-            "hist": hist}
+        _ptr(clips), _ptr(scales), _ptr(mse), _ptr(best), _ptr(scale), _stream(x)))
+    return {"clips": clips, "scales": scales, "mse": mse, "best": best, "scale": scale, "hist": hist}

@@ -351,92 +351,25 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
 
 // ------------------------------------------------------------------ calibration
 
-namespace {
-// float32 value of a 15-bit magnitude pattern of a 16-bit float.
-float mag_value(unsigned pat, vq_dtype dt) {
-  if (dt == VQ_BF16) {
-    uint32_t u = pat << 16;
-    float f;
-    std::memcpy(&f, &u, 4);
-    return f;
-  }
-  const unsigned e = (pat >> 10) & 0x1F, m = pat & 0x3FF;
-  if (e == 0) return std::ldexp((float)m, -24);  // subnormal: m * 2^-24
-  if (e == 31) return m ? NAN : INFINITY;
-  return std::ldexp((float)(1024 + m), (int)e - 25);
-}
-}  // namespace
-
 int64_t vq_calib_hist_bins(void) { return vq_internal::calib_hist_bins(); }
 
 vq_status vq_calib_static_scale(const void* x, vq_dtype dt, int64_t rows, int64_t cols, int64_t ldx, int bits,
                                 const double* percentiles_host, int32_t n_cand, uint32_t* hist_dev,
-                                float* clips_host, float* scales_host, double* mse_host, int32_t* best_host,
+                                float* clips_dev, float* scales_dev, double* mse_dev, int32_t* best_dev,
                                 float* scale_dev, hipStream_t stream) {
-  if (!x || !percentiles_host || !hist_dev || !clips_host || !scales_host || !mse_host || !best_host)
+  if (!x || !percentiles_host || !hist_dev || !clips_dev || !scales_dev || !mse_dev || !best_dev)
     return VQ_ERR_INVALID_ARG;
   if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
-  if (rows < 1 || cols < 1 || ldx < cols || rows >= kMaxDim || cols >= kMaxDim || n_cand < 1) return VQ_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1 || ldx < cols || rows >= kMaxDim || cols >= kMaxDim) return VQ_ERR_INVALID_ARG;
+  if (n_cand < 1 || n_cand > vq_internal::CALIB_MAX_CAND) return VQ_ERR_INVALID_ARG;
   if ((double)rows * (double)cols >= 4294967296.0) return VQ_ERR_UNSUPPORTED;  // 32-bit bin counts
   if (!ok_bits(bits)) return VQ_ERR_UNSUPPORTED;
   for (int i = 0; i < n_cand; ++i)
     if (!(percentiles_host[i] > 0.0 && percentiles_host[i] <= 100.0)) return VQ_ERR_INVALID_ARG;
   if (cols % 8 || ldx % 8 || !aligned16(x)) return VQ_ERR_SHAPE;
-
-  const int nb = vq_internal::calib_hist_bins();
-  hipError_t e = vq_internal::launch_abs_hist(x, rows, cols, ldx, hist_dev, stream);
-  if (e != hipSuccess) return hip_status(e);
-  std::vector<uint32_t> h(nb);
-  e = hipMemcpyAsync(h.data(), hist_dev, nb * sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) return hip_status(e);
-
-  const double n = (double)rows * (double)cols;
-  const float Q = (float)((1 << (bits - 1)) - 1);
-  for (int c = 0; c < n_cand; ++c) {
-    // Clip: the order statistic of |x| at rank ceil(p/100 * N).
-    double rk = std::ceil(percentiles_host[c] / 100.0 * n);
-    rk = std::min(std::max(rk, 1.0), n);
-    double cum = 0.0;
-    int bin = nb - 1;
-    for (int i = 0; i < nb; ++i) {
-      cum += h[i];
-      if (cum >= rk) {
-        bin = i;
-        break;
-      }
-    }
-    const float clip = mag_value((unsigned)bin, dt);
-    const float s = clip / Q;
-    float r = 1.0f / s;
-    if (!(s != 0.0f) || std::isinf(r)) r = 0.0f;
-    // Reconstruction error of the static quantizer, summed over the bins (|x| and -|x|
-    // have the same error).
-    double se = 0.0;
-    for (int i = 0; i < nb; ++i) {
-      if (!h[i]) continue;
-      const float v = mag_value((unsigned)i, dt);
-      float t = v * r;
-      t = std::min(std::max(t, -Q), Q);
-      const float q = std::nearbyint(t);
-      const float deq = q * s;
-      const double d = (double)v - (double)deq;
-      se += (double)h[i] * d * d;
-    }
-    clips_host[c] = clip;
-    scales_host[c] = s;
-    mse_host[c] = se / n;
-  }
-  int best = 0;
-  for (int c = 1; c < n_cand; ++c)
-    if (mse_host[c] < mse_host[best]) best = c;
-  *best_host = best;
-  if (scale_dev) {
-    e = hipMemcpyAsync(scale_dev, &scales_host[best], sizeof(float), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return VQ_OK;
+  return hip_status(vq_internal::launch_calib(x, dt == VQ_BF16 ? 1 : 0, rows, cols, ldx, bits, percentiles_host,
+                                              n_cand, hist_dev, clips_dev, scales_dev, mse_dev, best_dev,
+                                              scale_dev, stream));
 }
 
 // ------------------------------------------------------------------ routing

@@ -65,7 +65,10 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uin
                           int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, hipStream_t st);
 
 int calib_hist_bins();
-hipError_t launch_abs_hist(const void* x, int64_t rows, int64_t cols, int64_t ldx, unsigned* hist, hipStream_t st);
+constexpr int CALIB_MAX_CAND = 64;
+hipError_t launch_calib(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int bits,
+                        const double* pct, int n_cand, unsigned* hist, float* clips, float* scales, double* mse,
+                        int32_t* best, float* scale_out, hipStream_t st);
 
 int detect_row_chunks(int64_t rows);
 hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, double* ws,

@@ -264,7 +264,7 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
  * Static per-tensor activation scale by clipping-percentile search (Q-ARVD, Technical
  * details: per-tensor activations with a clipping percentile and a scale learned during
  * reconstruction).  One pass builds the histogram of |x| over its 32768 16-bit magnitude
- * patterns on the device; on the host, for each candidate percentile p:
+ * patterns; then, on the device, for each candidate percentile p:
  *   clip  = the order statistic of |x| at rank ceil(p/100 * N) (1-based, N = rows*cols)
  *   s     = fl32(clip / Q),  r = fl32(1 / s)   (Q = 2^(bits-1) - 1)
  *   mse   = sum over x of (x - fl32(clamp(rne(fl32(x * r)), -Q, Q) * s))^2 / N  (float64)
@@ -273,19 +273,20 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
  * a model); the result feeds vq_quant_act's VQ_PER_TENSOR_STATIC.
  *   x              device, dt in {F16, BF16}, [rows x cols], stride ldx; finite values;
  *                  16-byte aligned, cols % 8 == 0, ldx % 8 == 0, rows * cols < 2^32
- *   percentiles_host  host double [n_cand], each in (0, 100]
+ *   percentiles_host  host double [n_cand], each in (0, 100], 1 <= n_cand <= 64
+ *                  (read during the call; kernel arguments carry them)
  *   hist_dev       device uint32 [vq_calib_hist_bins()] scratch: receives the histogram
- *   clips_host, scales_host (float), mse_host (double): host [n_cand]
- *   best_host      host int32: index of the chosen candidate
- *   scale_dev      device float [1] or NULL: receives scales_host[best]
- * Waits on `stream` (the histogram is read back).  Errors: INVALID_ARG, SHAPE,
+ *   clips_dev, scales_dev (float), mse_dev (double): device [n_cand]
+ *   best_dev       device int32 [1]: index of the chosen candidate
+ *   scale_dev      device float [1] or NULL: receives scales_dev[best]
+ * Asynchronous on `stream` (no host synchronization).  Errors: INVALID_ARG, SHAPE,
  * UNSUPPORTED (bits not 4/6/8, too many elements).
  */
 int64_t vq_calib_hist_bins(void);
 vq_status vq_calib_static_scale(const void* x, vq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                                 int bits, const double* percentiles_host, int32_t n_cand,
-                                uint32_t* hist_dev, float* clips_host, float* scales_host,
-                                double* mse_host, int32_t* best_host, float* scale_dev,
+                                uint32_t* hist_dev, float* clips_dev, float* scales_dev,
+                                double* mse_dev, int32_t* best_dev, float* scale_dev,
                                 hipStream_t stream);
 
 /*

@@ -323,17 +323,18 @@ def test_calib_validation(lib):
     assert lib.vq_calib_hist_bins() == 32768
     pct = (ctypes.c_double * 2)(100.0, 99.9)
     bad_pct = (ctypes.c_double * 2)(100.0, 0.0)
-    f = (ctypes.c_float * 2)()
-    d = (ctypes.c_double * 2)()
-    best = ctypes.c_int32(0)
+    many = (ctypes.c_double * 65)(*([99.0] * 65))
 
-    def call(x=FAKE, dt=BF16, rows=64, cols=128, ldx=128, bits=8, p=pct, n=2, hist=FAKE):
-        return lib.vq_calib_static_scale(x, dt, rows, cols, ldx, bits, p, n, hist, f, f, d, ctypes.byref(best),
+    def call(x=FAKE, dt=BF16, rows=64, cols=128, ldx=128, bits=8, p=pct, n=2, hist=FAKE, out=FAKE):
+        # Every call here fails validation, so no device pointer is touched.
+        return lib.vq_calib_static_scale(x, dt, rows, cols, ldx, bits, p, n, hist, out, FAKE, FAKE, FAKE,
                                          NULL, NULL)
     assert call(x=NULL) == INVALID
     assert call(hist=NULL) == INVALID
+    assert call(out=NULL) == INVALID
     assert call(dt=F32) == INVALID
     assert call(n=0) == INVALID
+    assert call(p=many, n=65) == INVALID
     assert call(p=bad_pct) == INVALID
     assert call(ldx=100) == INVALID
     assert call(bits=5) == UNSUP
