@@ -56,7 +56,7 @@ def _load():
         "vq_outlier_part_len": (I64, [I32]),
         "vq_packed_k": (I64, [I64, I32]),
         "vq_detect_workspace_elems": (I64, [I64, I64]),
-        "vq_detect_outliers": (I, [P, I, I64, I64, I64, D, D, D, P, P, P, P, P, P]),
+        "vq_detect_outliers": (I, [P, I, I64, I64, I64, D, D, D, P, P, P, P, P, P, P]),
         "vq_pack_weights": (I, [P, I, I64, I64, I64, I, P, I32, I, P, P, P]),
         "vq_quant_act": (I, [P, I, I64, I64, I64, I, P, I, I, P, I32, P, P, P, P]),
         "vq_hadamard_block": (I, [P, I, I64, P, I, I64, I64, I64, I, I, P]),
@@ -136,8 +136,10 @@ def vq_packed_k(k: int, n_out: int) -> int:
     return int(_lib.vq_packed_k(k, n_out))
 
 
-def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kfac: float = 1.0, ws=None):
-    """Outlier input channels (columns) of x.  Returns (mask uint8 [K], idx int32 [n_out], norms f64 [K]) on the host."""
+def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kfac: float = 1.0, ws=None,
+                       n_out_dev=None):
+    """Outlier input channels (columns) of x.  Returns (mask uint8 [K], idx int32 [n_out], norms f64 [K]) on the host;
+    n_out_dev (device int32 [1]), if given, receives the count for vq_step_control."""
     _dev(x, "x")
     rows, cols = x.shape
     if ws is None:
@@ -149,7 +151,7 @@ def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kf
     n_out = ctypes.c_int32(0)
     _check("vq_detect_outliers", _lib.vq_detect_outliers(
         _ptr(x), _DT.get(x.dtype, -1), rows, cols, x.stride(0), tau, alpha, kfac, _ptr(ws),
-        _ptr(norms), _ptr(mask), _ptr(idx), ctypes.byref(n_out), _stream(x)))
+        _ptr(norms), _ptr(mask), _ptr(idx), ctypes.byref(n_out), _ptr(n_out_dev), _stream(x)))
     return mask, idx[: n_out.value].clone(), norms
 
 

@@ -62,6 +62,142 @@ __global__ __launch_bounds__(256) void k_colsumsq_final(double* ws, int64_t cols
   ws[(int64_t)chunks * cols + c] = s;
 }
 
+// ---- outlier statistics and flags (one workgroup): norms, median, MAD, the flag rule and
+// the outlier-first index list.  The median and MAD are exact order statistics, found by
+// radix selection over the float64 bit patterns (non-negative doubles order like their
+// bits), so they equal any correct sort of the same norms.
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_LDS_VALUES = 16384;  // norms kept in LDS when cols <= this
+
+struct DetectOut {
+  double* norms;  // [cols]
+  double* stats;  // [2]: median, MAD
+  int32_t* n_out; // [1]
+  int32_t* idx;   // [cols]
+  uint8_t* mask;  // [cols]
+};
+
+// The rank-th smallest (0-based) of val(0..n-1), all non-negative and finite.
+template <class F>
+__device__ double select_rank(F val, int n, int rank, unsigned* hist, int* s_sel, int* s_rem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t prefix = 0;
+  int rem = rank;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0u;
+    __syncthreads();
+    const uint64_t hi = shift == 56 ? 0ull : (~0ull << (shift + 8));
+    for (int i = tid; i < n; i += SEL_THREADS) {
+      const uint64_t b = (uint64_t)__double_as_longlong(val(i));
+      if ((b & hi) == prefix) atomicAdd(&hist[(b >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {  // the digit whose cumulative count passes rem: lane l holds digits 4l..4l+3
+      unsigned c[4], own = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[4 * lane + j];
+        own += c[j];
+      }
+      unsigned incl = own;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const unsigned v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      const unsigned excl = incl - own;
+      if (excl <= (unsigned)rem && (unsigned)rem < incl) {
+        unsigned cum = excl;
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] > (unsigned)rem) {
+            *s_sel = 4 * lane + j;
+            *s_rem = rem - (int)cum;
+            break;
+          }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)*s_sel << shift;
+    rem = *s_rem;
+    __syncthreads();
+  }
+  return __longlong_as_double((long long)prefix);
+}
+
+template <class F>
+__device__ double median_of(F val, int n, unsigned* hist, int* s_sel, int* s_rem) {
+  if (n & 1) return select_rank(val, n, n / 2, hist, s_sel, s_rem);
+  const double a = select_rank(val, n, n / 2 - 1, hist, s_sel, s_rem);
+  const double b = select_rank(val, n, n / 2, hist, s_sel, s_rem);
+  return 0.5 * (a + b);
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void k_detect_flags(const double* sums, int cols, double tau, double alpha,
+                                                              double kfac, DetectOut o) {
+  __shared__ double sv[SEL_LDS_VALUES];
+  __shared__ unsigned hist[256];
+  __shared__ int s_sel, s_rem;
+  __shared__ int s_wcnt[SEL_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool in_lds = cols <= SEL_LDS_VALUES;
+  for (int i = tid; i < cols; i += SEL_THREADS) {
+    const double v = sqrt(sums[i]);
+    o.norms[i] = v;
+    if (in_lds) sv[i] = v;
+  }
+  __syncthreads();
+  const double* vg = o.norms;
+  auto V = [&](int i) { return in_lds ? sv[i] : vg[i]; };
+  const double med = median_of(V, cols, hist, &s_sel, &s_rem);
+  auto D = [&](int i) { return fabs(V(i) - med); };
+  const double mad = median_of(D, cols, hist, &s_sel, &s_rem);
+  const double amin = alpha * med;
+
+  // Outliers in ascending order, then the normal channels in ascending order.
+  int base = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int c0 = 0; c0 < cols; c0 += SEL_THREADS) {
+      const int i = c0 + tid;
+      bool f = false;
+      if (i < cols) {
+        bool out;
+        if (pass == 0) {
+          const double v = V(i);
+          double z;
+          if (mad == 0.0)
+            z = v > med ? __builtin_inf() : 0.0;
+          else
+            z = kfac * (v - med) / mad;
+          out = z > tau && v > amin;
+          o.mask[i] = out ? 1 : 0;
+        } else {
+          out = o.mask[i] != 0;  // written by this thread in the first pass
+        }
+        f = pass == 0 ? out : !out;
+      }
+      const uint64_t bal = __ballot(f);
+      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) s_wcnt[wave] = __popcll(bal);
+      __syncthreads();
+      int off = 0, tot = 0;
+      for (int w = 0; w < SEL_THREADS / 64; ++w) {
+        if (w < wave) off += s_wcnt[w];
+        tot += s_wcnt[w];
+      }
+      if (f) o.idx[base + off + pre] = i;
+      base += tot;
+      __syncthreads();
+    }
+    if (pass == 0 && tid == 0) *o.n_out = base;
+  }
+  if (tid == 0) {
+    o.stats[0] = med;
+    o.stats[1] = mad;
+  }
+}
+
 constexpr int ROUTE_BLOCKS = 512;
 
 template <int DT>
@@ -134,6 +270,22 @@ hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_colsumsq_final, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st, ws, cols, chunks);
+  return hipGetLastError();
+}
+
+int64_t detect_result_bytes(int64_t cols) { return 13 * cols + 32; }
+
+hipError_t launch_detect_flags(double* ws, int64_t cols, int chunks, double tau, double alpha, double kfac,
+                               hipStream_t st) {
+  const double* sums = ws + (int64_t)chunks * cols;
+  uint8_t* r = reinterpret_cast<uint8_t*>(ws + (int64_t)(chunks + 1) * cols);
+  DetectOut o;
+  o.norms = reinterpret_cast<double*>(r);
+  o.stats = reinterpret_cast<double*>(r + 8 * cols);
+  o.n_out = reinterpret_cast<int32_t*>(r + 8 * cols + 16);
+  o.idx = reinterpret_cast<int32_t*>(r + 8 * cols + 32);
+  o.mask = r + 12 * cols + 32;
+  hipLaunchKernelGGL(k_detect_flags, dim3(1), dim3(SEL_THREADS), 0, st, sums, (int)cols, tau, alpha, kfac, o);
   return hipGetLastError();
 }
 

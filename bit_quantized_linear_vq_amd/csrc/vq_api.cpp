@@ -77,54 +77,39 @@ const char* vq_version(void) { return "vq 0.1 gfx950"; }
 
 int64_t vq_detect_workspace_elems(int64_t rows, int64_t cols) {
   if (rows < 1 || cols < 1) return 0;
-  return ((int64_t)vq_internal::detect_row_chunks(rows) + 1) * cols;
+  return ((int64_t)vq_internal::detect_row_chunks(rows) + 1) * cols +
+         (vq_internal::detect_result_bytes(cols) + 7) / 8;
 }
 
 vq_status vq_detect_outliers(const void* x, vq_dtype dt, int64_t rows, int64_t cols, int64_t ldx, double tau,
                              double alpha, double kfac, double* ws_dev, double* norms_host, uint8_t* mask_host,
-                             int32_t* idx_host, int32_t* n_out, hipStream_t stream) {
+                             int32_t* idx_host, int32_t* n_out, int32_t* n_out_dev, hipStream_t stream) {
   if (!x || !ws_dev || !mask_host || !idx_host || !n_out) return VQ_ERR_INVALID_ARG;
   if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
   if (rows < 1 || cols < 1 || ldx < cols || rows >= kMaxDim || cols >= kMaxDim) return VQ_ERR_INVALID_ARG;
   if (!std::isfinite(tau) || !std::isfinite(alpha) || !std::isfinite(kfac)) return VQ_ERR_INVALID_ARG;
   if (!aligned16(x) || ldx % 8) return VQ_ERR_SHAPE;
 
+  // Every step runs on the device; the host only receives the results, because the
+  // outlier count fixes the packed layout that the caller allocates next.
   hipError_t e = vq_internal::launch_colsumsq(x, (int)dt, rows, cols, ldx, ws_dev, stream);
   if (e != hipSuccess) return hip_status(e);
-  std::vector<double> v((size_t)cols);
   const int chunks = vq_internal::detect_row_chunks(rows);
-  e = hipMemcpyAsync(v.data(), ws_dev + (int64_t)chunks * cols, sizeof(double) * (size_t)cols,
-                     hipMemcpyDeviceToHost, stream);
+  e = vq_internal::launch_detect_flags(ws_dev, cols, chunks, tau, alpha, kfac, stream);
   if (e != hipSuccess) return hip_status(e);
-  e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) return hip_status(e);
-
-  for (auto& s : v) s = std::sqrt(s);
-  auto median = [](std::vector<double> a) {
-    const size_t n = a.size();
-    std::sort(a.begin(), a.end());
-    return n % 2 ? a[n / 2] : 0.5 * (a[n / 2 - 1] + a[n / 2]);
-  };
-  const double med = median(v);
-  std::vector<double> dev(v.size());
-  for (size_t i = 0; i < v.size(); ++i) dev[i] = std::fabs(v[i] - med);
-  const double mad = median(dev);
-  int32_t cnt = 0;
-  for (int64_t i = 0; i < cols; ++i) {
-    double z;
-    if (mad == 0.0)
-      z = v[(size_t)i] > med ? INFINITY : 0.0;
-    else
-      z = kfac * (v[(size_t)i] - med) / mad;
-    const bool out = z > tau && v[(size_t)i] > alpha * med;
-    mask_host[i] = out ? 1 : 0;
-    if (out) idx_host[cnt++] = (int32_t)i;
+  const uint8_t* res = reinterpret_cast<const uint8_t*>(ws_dev + (int64_t)(chunks + 1) * cols);
+  if (n_out_dev) {
+    e = hipMemcpyAsync(n_out_dev, res + 8 * cols + 16, sizeof(int32_t), hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_status(e);
   }
-  int32_t j = cnt;
-  for (int64_t i = 0; i < cols; ++i)
-    if (!mask_host[i]) idx_host[j++] = (int32_t)i;
-  *n_out = cnt;
-  if (norms_host) std::memcpy(norms_host, v.data(), sizeof(double) * (size_t)cols);
+  std::vector<uint8_t> h((size_t)vq_internal::detect_result_bytes(cols));
+  e = hipMemcpyAsync(h.data(), res, h.size(), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (norms_host) std::memcpy(norms_host, h.data(), sizeof(double) * (size_t)cols);
+  std::memcpy(n_out, h.data() + 8 * cols + 16, sizeof(int32_t));
+  std::memcpy(idx_host, h.data() + 8 * cols + 32, sizeof(int32_t) * (size_t)cols);
+  std::memcpy(mask_host, h.data() + 12 * cols + 32, (size_t)cols);
   return VQ_OK;
 }
 

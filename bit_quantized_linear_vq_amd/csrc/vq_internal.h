@@ -71,6 +71,12 @@ hipError_t launch_calib(const void* x, int dtype, int64_t rows, int64_t cols, in
                         int32_t* best, float* scale_out, hipStream_t st);
 
 int detect_row_chunks(int64_t rows);
+// Result block of the detection, after the (chunks + 1) * cols partial and total sums in
+// the workspace: norms f64 [cols], median and MAD f64, n_out i32 (+12 pad), idx i32 [cols],
+// mask u8 [cols].
+int64_t detect_result_bytes(int64_t cols);
+hipError_t launch_detect_flags(double* ws, int64_t cols, int chunks, double tau, double alpha, double kfac,
+                               hipStream_t st);
 hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, double* ws,
                            hipStream_t st);
 

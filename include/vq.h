@@ -90,16 +90,20 @@ int64_t vq_packed_k(int64_t k, int32_t n_out);
  *   ws_dev     device scratch of vq_detect_workspace_elems(rows, cols) doubles
  *   norms_host host [cols] or NULL: receives v
  *   mask_host  host [cols]: 1 for an outlier channel, else 0
- *   idx_host   host [cols]: first *n_out entries = outlier channels, ascending
+ *   idx_host   host [cols]: first *n_out entries = outlier channels, ascending, then
+ *              the other channels, ascending
  *   n_out      host: number of outlier channels
- * Waits on `stream` (the sums are copied to the host and the median is taken there).
+ *   n_out_dev  device int32 [1] or NULL: receives the same count (for vq_step_control)
+ * The norms, the median and MAD (exact order statistics of the norms) and the flags are
+ * computed on the device; the call then copies the results to the host and waits on
+ * `stream`, since the count fixes the packed layout the caller allocates next.
  * Errors: INVALID_ARG for null pointers / rows or cols < 1 / ldx < cols / bad dtype.
  */
 int64_t vq_detect_workspace_elems(int64_t rows, int64_t cols);
 vq_status vq_detect_outliers(const void* x, vq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                              double tau, double alpha, double kfac, double* ws_dev,
                              double* norms_host, uint8_t* mask_host, int32_t* idx_host,
-                             int32_t* n_out, hipStream_t stream);
+                             int32_t* n_out, int32_t* n_out_dev, hipStream_t stream);
 
 /*
  * Offline per-output-channel weight quantization (Q-ARVD, Methodology and Technical

@@ -54,8 +54,9 @@ def test_layout_helpers(lib):
     assert lib.vq_outlier_part_len(65) == 128
     assert lib.vq_packed_k(3072, 30) == 3136
     assert lib.vq_packed_k(1920, 0) == 1920
-    assert lib.vq_detect_workspace_elems(12288, 3072) == (256 + 1) * 3072
-    assert lib.vq_detect_workspace_elems(10, 7) == 11 * 7
+    # Partial and total column sums, then the result block (13 bytes per column + 32).
+    assert lib.vq_detect_workspace_elems(12288, 3072) == (256 + 1) * 3072 + (13 * 3072 + 32 + 7) // 8
+    assert lib.vq_detect_workspace_elems(10, 7) == 11 * 7 + (13 * 7 + 32 + 7) // 8
     assert lib.vq_route_workspace_elems(65536) == 1024
     assert lib.vq_detect_workspace_elems(0, 5) == 0
 
@@ -174,13 +175,13 @@ def test_detect_and_route_validation(lib):
     buf = (ctypes.c_uint8 * 16)()
     idx = (ctypes.c_int32 * 16)()
     assert lib.vq_detect_outliers(NULL, BF16, 8, 16, 16, 3.5, 2.0, 1.0, FAKE, NULL, buf, idx,
-                                  ctypes.byref(n_out), NULL) == INVALID
+                                  ctypes.byref(n_out), NULL, NULL) == INVALID
     assert lib.vq_detect_outliers(FAKE, F32, 8, 16, 16, 3.5, 2.0, 1.0, FAKE, NULL, buf, idx,
-                                  ctypes.byref(n_out), NULL) == INVALID
+                                  ctypes.byref(n_out), NULL, NULL) == INVALID
     assert lib.vq_detect_outliers(FAKE, BF16, 8, 16, 8, 3.5, 2.0, 1.0, FAKE, NULL, buf, idx,
-                                  ctypes.byref(n_out), NULL) == INVALID
+                                  ctypes.byref(n_out), NULL, NULL) == INVALID
     assert lib.vq_detect_outliers(FAKE, BF16, 8, 16, 16, float("nan"), 2.0, 1.0, FAKE, NULL, buf, idx,
-                                  ctypes.byref(n_out), NULL) == INVALID
+                                  ctypes.byref(n_out), NULL, NULL) == INVALID
     assert lib.vq_route_rel_l1(FAKE, FAKE, BF16, 0, 0.1, 8, 4, FAKE, NULL, FAKE, NULL) == INVALID
     assert lib.vq_route_rel_l1(FAKE, FAKE, BF16, 16, 0.1, 5, 4, FAKE, NULL, FAKE, NULL) == INVALID
     assert lib.vq_route_rel_l1(FAKE, FAKE, BF16, 16, 0.1, 8, 4, FAKE, NULL, NULL, NULL) == INVALID

@@ -348,6 +348,53 @@ def test_detect_worked_example(vq):
     assert_same(idx.numpy(), r["idx"], "indices")
 
 
+@pytest.mark.parametrize("cols", [1, 2, 7, 1000, 1001, 16384, 20008])
+def test_detect_order_statistics_exact(vq, cols):
+    """Median and MAD are exact order statistics of the device norms: the flag rule applied
+    by the oracle to those same norms gives the same mask and index order, for even and odd
+    counts, ties, and counts beyond the LDS-resident case."""
+    g = np.random.default_rng(cols)
+    rows = 24
+    x = g.standard_normal((rows, cols)).astype(np.float32)
+    x[:, : cols // 3] = x[:, :1]  # a third of the columns share one norm (ties)
+    x[:, g.integers(0, cols, max(1, cols // 50))] *= 8.0
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    if cols % 8:  # rows must start on 16-byte boundaries: use a padded pitch
+        pad = torch.zeros((rows, (cols + 7) // 8 * 8), dtype=torch.bfloat16)
+        pad[:, :cols] = t
+        xd = pad.to(DEV)[:, :cols]
+    else:
+        xd = t.to(DEV)
+    for kfac in (1.0, 0.6745):
+        mask, idx, norms = vq.vq_detect_outliers(xd, 3.5, 2.0, kfac)
+        fm, fidx, _, _, _ = odetect.flag_outliers(norms.numpy(), 3.5, 2.0, kfac)
+        assert_same(mask.numpy().astype(bool), fm, "mask")
+        assert_same(idx.numpy(), fidx, "indices")
+    r = oracle.linear.detect_on(npb(t), "bf16")
+    np.testing.assert_allclose(norms.numpy(), r["norms"], rtol=1e-12)
+
+
+def test_detect_zero_mad(vq):
+    """More than half of the norms equal: MAD = 0, so every larger norm above alpha * median is flagged."""
+    x = torch.ones((4, 64), dtype=torch.float32)
+    x[:, 5] = 3.0
+    x[:, 9] = 1.5   # above the median but not above 2 * median
+    x[:, 40] = 0.5
+    mask, idx, norms = vq.vq_detect_outliers(x.to(torch.float16).to(DEV))
+    fm, fidx, _, med, mad = odetect.flag_outliers(norms.numpy())
+    assert mad == 0.0
+    assert_same(idx.numpy(), np.array([5], np.int32), "indices")
+    assert_same(mask.numpy().astype(bool), fm, "mask")
+
+
+def test_detect_count_on_device(vq):
+    w = gen.make_w(3)
+    cnt = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    _, idx, _ = vq.vq_detect_outliers(w.to(DEV), n_out_dev=cnt)
+    torch.cuda.synchronize()
+    assert cnt.item() == idx.numel()
+
+
 def test_route_pairs_and_tie(vq):
     got_bits = []
     for layer in range(42):
