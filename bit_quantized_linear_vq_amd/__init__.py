@@ -29,7 +29,7 @@ EXPORTS = (
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
     "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
-    "vq_calib_hist_bins", "vq_calib_static_scale", "vq_status_string", "vq_last_hip_error", "vq_version",
+    "vq_calib_hist_bins", "vq_calib_static_scale", "vq_control_workspace_elems", "vq_step_control", "vq_status_string", "vq_last_hip_error", "vq_version",
 )
 CALIB_GRID = (100.0, 99.999, 99.99, 99.9, 99.8, 99.5, 99.0, 98.0, 97.0, 95.0, 90.0)
 
@@ -57,6 +57,8 @@ def _load():
         "vq_packed_k": (I64, [I64, I32]),
         "vq_detect_workspace_elems": (I64, [I64, I64]),
         "vq_detect_outliers": (I, [P, I, I64, I64, I64, D, D, D, P, P, P, P, P, P, P]),
+        "vq_control_workspace_elems": (I64, []),
+        "vq_step_control": (I, [P, P, I, I64, P, P, I, I64, P, I64, P, P, P, P, P, P, P, P]),
         "vq_pack_weights": (I, [P, I, I64, I64, I64, I, P, I32, I, P, P, P]),
         "vq_quant_act": (I, [P, I, I64, I64, I64, I, P, I, I, P, I32, P, P, P, P]),
         "vq_hadamard_block": (I, [P, I, I64, P, I, I64, I64, I64, I, I, P]),
@@ -367,3 +369,57 @@ def vq_calib_static_scale(x: torch.Tensor, bits: int, percentiles=CALIB_GRID, sc
         _ptr(x), _DT.get(x.dtype, -1), rows, cols, x.stride(0), bits, pct, n, _ptr(hist),
         _ptr(clips), _ptr(scales), _ptr(mse), _ptr(best), _ptr(scale), _stream(x)))
     return {"clips": clips, "scales": scales, "mse": mse, "best": best, "scale": scale, "hist": hist}
+
+
+class ControlParams(ctypes.Structure):
+    """vq_control_params: TDC skip and drift thresholds, skip limit, DMPQ widths and
+    threshold, PDR outlier-ratio limit."""
+    _fields_ = [("skip_threshold", ctypes.c_double), ("drift_threshold", ctypes.c_double),
+                ("max_skips", ctypes.c_int32), ("bits_hi", ctypes.c_int32), ("bits_lo", ctypes.c_int32),
+                ("route_threshold", ctypes.c_double), ("outlier_ratio_max", ctypes.c_double)]
+
+
+CONTROL_STATE_BYTES = 16
+
+
+def vq_control_state(device) -> torch.Tensor:
+    """Zeroed per-block control state (consecutive skips, accumulated error)."""
+    return torch.zeros(CONTROL_STATE_BYTES // 8, dtype=torch.float64, device=device)
+
+
+def vq_step_control(state: torch.Tensor, params: ControlParams, delta_new=None, delta_old=None, x_prev=None,
+                    y_prev=None, n_out_dev=None, channels: int = 0, ws=None, skip=None, bits=None, e=None,
+                    gamma=None):
+    """One block's decision at a step, on the device.  Returns (skip int32 [1], bits int32 [1],
+    E float64 [1], Gamma float64 [1]); the state tensor is updated in place."""
+    _buf(state, "state", CONTROL_STATE_BYTES, state.device)
+    dev = state.device
+    for t, name in ((delta_new, "delta_new"), (delta_old, "delta_old"), (x_prev, "x_prev"), (y_prev, "y_prev")):
+        if t is not None:
+            _dev(t, name)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    if (delta_new is None) != (delta_old is None) or (x_prev is None) != (y_prev is None):
+        raise ValueError("deltas and the previous input/output come in pairs")
+    for a, b, what in ((delta_new, delta_old, "deltas"), (x_prev, y_prev, "previous input/output")):
+        if a is not None and (a.numel() != b.numel() or a.dtype != b.dtype):
+            raise ValueError(f"the {what} must have the same size and dtype")
+    nw = int(_lib.vq_control_workspace_elems())
+    ws = torch.empty(nw, dtype=torch.float64, device=dev) if ws is None else ws
+    _buf(ws, "ws", 8 * nw, dev)
+    skip = torch.empty(1, dtype=torch.int32, device=dev) if skip is None else skip
+    bits = torch.empty(1, dtype=torch.int32, device=dev) if bits is None else bits
+    e = torch.empty(1, dtype=torch.float64, device=dev) if e is None else e
+    gamma = torch.empty(1, dtype=torch.float64, device=dev) if gamma is None else gamma
+    for t, name, nb in ((skip, "skip", 4), (bits, "bits", 4), (e, "e", 8), (gamma, "gamma", 8)):
+        _buf(t, name, nb, dev)
+    if n_out_dev is not None:
+        _buf(n_out_dev, "n_out_dev", 4, dev)
+    dnew_dt = _DT.get(delta_new.dtype, -1) if delta_new is not None else 0
+    xy_dt = _DT.get(x_prev.dtype, -1) if x_prev is not None else 0
+    _check("vq_step_control", _lib.vq_step_control(
+        _ptr(delta_new), _ptr(delta_old), dnew_dt, delta_new.numel() if delta_new is not None else 0,
+        _ptr(x_prev), _ptr(y_prev), xy_dt, x_prev.numel() if x_prev is not None else 0,
+        _ptr(n_out_dev), channels, ctypes.byref(params), _ptr(state), _ptr(ws), _ptr(skip), _ptr(bits), _ptr(e),
+        _ptr(gamma), _stream(state)))
+    return skip, bits, e, gamma

@@ -249,6 +249,66 @@ __global__ void k_route_final(const double* ws, int blocks, double threshold, in
   *bits = g > threshold ? hi : lo;
 }
 
+// ---- per-block step control (TDC skip test, PDR overrides, DMPQ route).
+struct ControlParams {
+  double skip_threshold, drift_threshold, route_threshold, outlier_ratio_max;
+  int max_skips, bits_hi, bits_lo;
+};
+
+__device__ __forceinline__ void sum_pairs(const double* ws, int blocks, double& a, double& b) {
+  a = 0.0;
+  b = 0.0;
+  for (int i = 0; i < blocks; ++i) {
+    a += ws[2 * i];
+    b += ws[2 * i + 1];
+  }
+}
+
+// ws_e / ws_g: partial sums of the two relative-L1 statistics (blocks_e / blocks_g = 0 when
+// absent).  state[0] = consecutive skips (int32), state + 8 = accumulated error (double).
+__global__ void k_control_final(const double* ws_e, int blocks_e, const double* ws_g, int blocks_g,
+                                const int32_t* n_out, int64_t channels, ControlParams p, uint8_t* state,
+                                int32_t* skip, int32_t* bits, double* e_out, double* g_out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int32_t* skips = reinterpret_cast<int32_t*>(state);
+  double* drift = reinterpret_cast<double*>(state + 8);
+  double e = __builtin_nan(""), g = __builtin_nan("");
+  if (blocks_e) {
+    double num, den;
+    sum_pairs(ws_e, blocks_e, num, den);
+    e = num == 0.0 ? 0.0 : (den > 0.0 ? num / den : __builtin_inf());
+  }
+  if (blocks_g) {
+    double num, den;
+    sum_pairs(ws_g, blocks_g, num, den);
+    g = den > 0.0 ? num / den : __builtin_inf();
+  }
+  if (e_out) *e_out = e;
+  if (g_out) *g_out = g;
+  const int s = *skips;
+  const double d = *drift;
+  if (blocks_e && s < p.max_skips && e <= p.skip_threshold && d + e <= p.drift_threshold) {
+    *skips = s + 1;
+    *drift = d + e;
+    *skip = 1;
+    *bits = 0;
+    return;
+  }
+  int b;
+  if (n_out && channels > 0 && (double)*n_out / (double)channels > p.outlier_ratio_max)
+    b = 16;
+  else if (s > 0)
+    b = 8;
+  else if (!blocks_g)
+    b = p.bits_hi;
+  else
+    b = g > p.route_threshold ? p.bits_hi : p.bits_lo;
+  *skips = 0;
+  *drift = 0.0;
+  *skip = 0;
+  *bits = b;
+}
+
 }  // namespace vqk
 
 namespace vq_internal {
@@ -291,15 +351,42 @@ hipError_t launch_detect_flags(double* ws, int64_t cols, int chunks, double tau,
 
 int route_blocks() { return ROUTE_BLOCKS; }
 
-hipError_t launch_route(const void* x, const void* y, int dt, int64_t n, double threshold, int hi, int lo,
-                        double* ws, double* gamma, int32_t* bits, hipStream_t st) {
-  int64_t want = (n + 2047) / 2048;
-  const int blocks = (int)(want < ROUTE_BLOCKS ? (want < 1 ? 1 : want) : ROUTE_BLOCKS);
+static int route_grid(int64_t n) {
+  const int64_t want = (n + 2047) / 2048;
+  return (int)(want < ROUTE_BLOCKS ? (want < 1 ? 1 : want) : ROUTE_BLOCKS);
+}
+
+static void launch_route_partial(const void* x, const void* y, int dt, int64_t n, int blocks, double* ws,
+                                 hipStream_t st) {
   switch (dt) {
     case DT_F16: hipLaunchKernelGGL(k_route_partial<DT_F16>, dim3(blocks), dim3(256), 0, st, x, y, n, ws); break;
     case DT_BF16: hipLaunchKernelGGL(k_route_partial<DT_BF16>, dim3(blocks), dim3(256), 0, st, x, y, n, ws); break;
     default: hipLaunchKernelGGL(k_route_partial<DT_F32>, dim3(blocks), dim3(256), 0, st, x, y, n, ws); break;
   }
+}
+
+hipError_t launch_control(const void* d1, const void* d2, int d_dt, int64_t n_d, const void* x, const void* y,
+                          int xy_dt, int64_t n_xy, const int32_t* n_out, int64_t channels, double skip_thr,
+                          double drift_thr, int max_skips, double route_thr, int hi, int lo, double ratio_max,
+                          uint8_t* state, double* ws, int32_t* skip, int32_t* bits, double* e, double* g,
+                          hipStream_t st) {
+  // E = sum|d1 - d2| / sum|d2| is the relative-L1 form with x = d2 (older), y = d1 (newer).
+  const int be = d1 ? route_grid(n_d) : 0;
+  const int bg = x ? route_grid(n_xy) : 0;
+  double* ws_e = ws;
+  double* ws_g = ws + 2 * ROUTE_BLOCKS;
+  if (be) launch_route_partial(d2, d1, d_dt, n_d, be, ws_e, st);
+  if (bg) launch_route_partial(x, y, xy_dt, n_xy, bg, ws_g, st);
+  ControlParams p{skip_thr, drift_thr, route_thr, ratio_max, max_skips, hi, lo};
+  hipLaunchKernelGGL(k_control_final, dim3(1), dim3(64), 0, st, ws_e, be, ws_g, bg, n_out, channels, p, state, skip,
+                     bits, e, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const void* x, const void* y, int dt, int64_t n, double threshold, int hi, int lo,
+                        double* ws, double* gamma, int32_t* bits, hipStream_t st) {
+  const int blocks = route_grid(n);
+  launch_route_partial(x, y, dt, n, blocks, ws, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_route_final, dim3(1), dim3(64), 0, st, ws, blocks, threshold, hi, lo, gamma, bits);

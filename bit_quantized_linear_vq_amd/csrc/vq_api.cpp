@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -369,6 +370,33 @@ vq_status vq_route_rel_l1(const void* x, const void* y, vq_dtype dt, int64_t n, 
   if (!ok_bits(bits_hi) || !ok_bits(bits_lo) || !std::isfinite(threshold)) return VQ_ERR_INVALID_ARG;
   return hip_status(vq_internal::launch_route(x, y, (int)dt, n, threshold, bits_hi, bits_lo, ws_dev, gamma_dev,
                                               bits_dev, stream));
+}
+
+static_assert(sizeof(vq_control_params) == 48 && offsetof(vq_control_params, max_skips) == 16 &&
+                  offsetof(vq_control_params, route_threshold) == 32,
+              "vq_control_params layout is part of the ABI");
+
+int64_t vq_control_workspace_elems(void) { return 4 * (int64_t)vq_internal::route_blocks(); }
+
+vq_status vq_step_control(const void* delta_new, const void* delta_old, vq_dtype delta_dt, int64_t n_delta,
+                          const void* x_prev, const void* y_prev, vq_dtype xy_dt, int64_t n_xy,
+                          const int32_t* n_out_dev, int64_t channels, const vq_control_params* params,
+                          void* state_dev, double* ws_dev, int32_t* skip_dev, int32_t* bits_dev, double* e_dev,
+                          double* gamma_dev, hipStream_t stream) {
+  if (!params || !state_dev || !ws_dev || !skip_dev || !bits_dev) return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(state_dev) % 8) return VQ_ERR_INVALID_ARG;
+  if (!delta_new != !delta_old || !x_prev != !y_prev) return VQ_ERR_INVALID_ARG;
+  if (delta_new && (!valid_dt(delta_dt) || n_delta < 1)) return VQ_ERR_INVALID_ARG;
+  if (x_prev && (!valid_dt(xy_dt) || n_xy < 1)) return VQ_ERR_INVALID_ARG;
+  if (n_out_dev && channels < 1) return VQ_ERR_INVALID_ARG;
+  const vq_control_params& p = *params;
+  if (std::isnan(p.skip_threshold) || std::isnan(p.drift_threshold) || std::isnan(p.route_threshold) ||
+      std::isnan(p.outlier_ratio_max) || p.max_skips < 0 || !ok_bits(p.bits_hi) || !ok_bits(p.bits_lo))
+    return VQ_ERR_INVALID_ARG;
+  return hip_status(vq_internal::launch_control(
+      delta_new, delta_old, (int)delta_dt, n_delta, x_prev, y_prev, (int)xy_dt, n_xy, n_out_dev, channels,
+      p.skip_threshold, p.drift_threshold, p.max_skips, p.route_threshold, p.bits_hi, p.bits_lo,
+      p.outlier_ratio_max, static_cast<uint8_t*>(state_dev), ws_dev, skip_dev, bits_dev, e_dev, gamma_dev, stream));
 }
 
 }  // extern "C"

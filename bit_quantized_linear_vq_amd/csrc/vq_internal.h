@@ -81,6 +81,11 @@ hipError_t launch_colsumsq(const void* x, int dt, int64_t rows, int64_t cols, in
                            hipStream_t st);
 
 int route_blocks();
+hipError_t launch_control(const void* d1, const void* d2, int d_dt, int64_t n_d, const void* x, const void* y,
+                          int xy_dt, int64_t n_xy, const int32_t* n_out, int64_t channels, double skip_thr,
+                          double drift_thr, int max_skips, double route_thr, int hi, int lo, double ratio_max,
+                          uint8_t* state, double* ws, int32_t* skip, int32_t* bits, double* e, double* g,
+                          hipStream_t st);
 hipError_t launch_route(const void* x, const void* y, int dt, int64_t n, double threshold, int hi, int lo,
                         double* ws, double* gamma, int32_t* bits, hipStream_t st);
 

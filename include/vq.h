@@ -310,6 +310,55 @@ vq_status vq_route_rel_l1(const void* x, const void* y, vq_dtype dt, int64_t n, 
                           int bits_hi, int bits_lo, double* ws_dev, double* gamma_dev,
                           int32_t* bits_dev, hipStream_t stream);
 
+/*
+ * One block's runtime decision at a denoising step (6Bit-Diffusion, Methodology B.1-B.3:
+ * DMPQ route, TDC skip with drift control, PDR precision overrides).  On the device:
+ *   E     = sum|delta_new - delta_old| / sum|delta_old|  (float64; 0 when the numerator
+ *           is 0, +inf when only the denominator is 0), from the block's two cached
+ *           residual deltas (output minus input at the two previous computed steps);
+ *   Gamma = sum|y_prev - x_prev| / sum|x_prev|  (as vq_route_rel_l1);
+ *   skip  <=>  deltas given, skips < max_skips, E <= skip_threshold and
+ *              drift + E <= drift_threshold; then skips += 1, drift += E, bits = 0;
+ *   else compute, skips = drift = 0, and bits =
+ *     16       if n_out / channels > outlier_ratio_max (unquantized layer),
+ *     8        else if the previous step was skipped (no routing information),
+ *     bits_hi  else if Gamma is unknown (no x_prev/y_prev) or Gamma > route_threshold,
+ *     bits_lo  otherwise.
+ * The readings (delta definition, the form of E, the accumulated error, the precedence)
+ * are this library's: the page states the rules without formulas.  bits_dev feeds
+ * vq_quant_act's bits_dev directly (it quantizes a 16 as 8: a caller that honours the
+ * flag runs the layer unquantized instead).
+ *   delta_new, delta_old  device [n_delta] of delta_dt (F16/BF16/F32), or both NULL
+ *   x_prev, y_prev        device [n_xy] of xy_dt, or both NULL
+ *   n_out_dev             device int32 [1] (e.g. vq_detect_outliers' n_out_dev) or NULL;
+ *                         channels >= 1 when given
+ *   state_dev             device, VQ_CONTROL_STATE_BYTES, 8-byte aligned, zero for a
+ *                         fresh block: consecutive skips (int32) and the accumulated
+ *                         error (double at byte 8); updated in place
+ *   ws_dev                device scratch of vq_control_workspace_elems() doubles
+ *   skip_dev, bits_dev    device int32 [1]: 1 to skip the block; the precision code
+ *   e_dev, gamma_dev      device double [1] or NULL (NaN when not computed)
+ * Asynchronous.  Calls for one block must be ordered (they share its state).
+ * Errors: INVALID_ARG (null state/ws/outputs/params, an unpaired input, n < 1, a NaN
+ * threshold, max_skips < 0, widths not 4/6/8, channels < 1 with n_out_dev).
+ */
+typedef struct vq_control_params {
+  double skip_threshold;
+  double drift_threshold;
+  int32_t max_skips;
+  int32_t bits_hi;
+  int32_t bits_lo;
+  double route_threshold;
+  double outlier_ratio_max;
+} vq_control_params;
+#define VQ_CONTROL_STATE_BYTES 16
+int64_t vq_control_workspace_elems(void);
+vq_status vq_step_control(const void* delta_new, const void* delta_old, vq_dtype delta_dt, int64_t n_delta,
+                          const void* x_prev, const void* y_prev, vq_dtype xy_dt, int64_t n_xy,
+                          const int32_t* n_out_dev, int64_t channels, const vq_control_params* params,
+                          void* state_dev, double* ws_dev, int32_t* skip_dev, int32_t* bits_dev,
+                          double* e_dev, double* gamma_dev, hipStream_t stream);
+
 /* Text of a status code (static storage). */
 const char* vq_status_string(vq_status s);
 

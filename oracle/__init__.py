@@ -22,6 +22,9 @@ Steps and the passages they follow:
 * ``route``     relative-L1 routing statistic Gamma and the INT8-vs-4-bit decision
                 (6Bit-Diffusion page, Key Insights 1 and Methodology B.1, DMPQ).
 * ``linear``    the whole layer, chaining the steps above.
+* ``control``   one block's runtime decision at a timestep: TDC skip test on the cached
+                residual deltas, PDR precision overrides, then the DMPQ route
+                (6Bit-Diffusion page, Methodology B.1-B.3).
 * ``decompose`` residual re-quantization of selected tokens, added back through a
                 second accumulator (SemanticDialect page, Methodology 2.2).
 * ``calib``     static per-tensor activation scale by clipping-percentile search
@@ -30,4 +33,4 @@ Steps and the passages they follow:
                 exact GEMM: the 4-bit floating-point route of the 6Bit-Diffusion page
                 (Methodology B.1) in the form gfx950's scaled MFMA consumes.
 """
-from . import numerics, detect, quantizer, fwht, gemm, route, linear, decompose, mx, calib  # noqa: F401
+from . import numerics, detect, quantizer, fwht, gemm, route, linear, decompose, mx, calib, control  # noqa: F401

@@ -342,3 +342,30 @@ def test_calib_validation(lib):
     assert call(rows=70000, cols=65536, ldx=65536) == UNSUP
     assert call(cols=100, ldx=100) == SHAPE
     assert call(x=ctypes.c_void_p(0x10008)) == SHAPE
+
+
+def test_step_control_validation(lib):
+    import bit_quantized_linear_vq_amd as vq
+    assert ctypes.sizeof(vq.ControlParams) == 48 and vq.ControlParams.route_threshold.offset == 32
+    assert lib.vq_control_workspace_elems() == 2048
+    ok = vq.ControlParams(0.05, 0.15, 3, 8, 4, 0.1, 0.01)
+
+    def call(dn=FAKE, do=FAKE, ddt=BF16, nd=64, x=FAKE, y=FAKE, xdt=BF16, nx=64, nout=NULL, ch=0, p=ok,
+             state=FAKE, ws=FAKE, skip=FAKE, bits=FAKE):
+        # Every call here fails validation, so no device pointer is touched.
+        return lib.vq_step_control(dn, do, ddt, nd, x, y, xdt, nx, nout, ch,
+                                   ctypes.byref(p) if p is not None else NULL, state, ws, skip, bits, NULL, NULL,
+                                   NULL)
+    assert call(p=None) == INVALID
+    assert call(state=NULL) == INVALID
+    assert call(state=ctypes.c_void_p(0x10004)) == INVALID
+    assert call(ws=NULL) == INVALID
+    assert call(bits=NULL) == INVALID
+    assert call(do=NULL) == INVALID
+    assert call(y=NULL) == INVALID
+    assert call(nd=0) == INVALID
+    assert call(xdt=7) == INVALID
+    assert call(nout=FAKE, ch=0) == INVALID
+    for bad in (vq.ControlParams(float("nan"), 0.15, 3, 8, 4, 0.1, 0.01), vq.ControlParams(0.05, 0.15, -1, 8, 4, 0.1, 0.01),
+                vq.ControlParams(0.05, 0.15, 3, 5, 4, 0.1, 0.01), vq.ControlParams(0.05, 0.15, 3, 8, 4, 0.1, float("nan"))):
+        assert call(p=bad) == INVALID
