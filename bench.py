@@ -159,8 +159,9 @@ class Layer:
             import numpy as np
             rows = np.sort(np.random.default_rng(1000 * cfg + 20).choice(self.M, self.R, replace=False))
             self.rows = torch.from_numpy(rows.astype(np.int32)).to(dev)
-            self.codes2 = torch.empty((self.R, self.K), dtype=torch.int8, device=dev)
-            self.scales2 = torch.empty((self.R,), dtype=torch.float32, device=dev)
+            # Stacked operand: first-quantizer codes of the R listed rows, then their residual codes.
+            self.codes2 = torch.empty((2 * self.R, self.K), dtype=torch.int8, device=dev)
+            self.scales2 = torch.empty((2 * self.R,), dtype=torch.float32, device=dev)
             self.ws = torch.empty(vq.vq_residual_workspace_bytes(self.M, self.R, self.N), dtype=torch.uint8,
                                   device=dev)
         torch.cuda.synchronize()
