@@ -26,10 +26,11 @@ VQ_MAX_OUTLIERS = 128
 
 EXPORTS = (
     "vq_outlier_part_len", "vq_packed_k", "vq_detect_workspace_elems", "vq_detect_outliers",
-    "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant",
+    "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant", "vq_qgemm_workspace_bytes",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
     "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
-    "vq_calib_hist_bins", "vq_calib_static_scale", "vq_control_workspace_elems", "vq_step_control", "vq_status_string", "vq_last_hip_error", "vq_version",
+    "vq_calib_hist_bins", "vq_calib_static_scale", "vq_control_workspace_elems", "vq_step_control",
+    "vq_status_string", "vq_last_hip_error", "vq_version",
 )
 CALIB_GRID = (100.0, 99.999, 99.99, 99.9, 99.8, 99.5, 99.0, 98.0, 97.0, 95.0, 90.0)
 
@@ -62,7 +63,8 @@ def _load():
         "vq_pack_weights": (I, [P, I, I64, I64, I64, I, P, I32, I, P, P, P]),
         "vq_quant_act": (I, [P, I, I64, I64, I64, I, P, I, I, P, I32, P, P, P, P]),
         "vq_hadamard_block": (I, [P, I, I64, P, I, I64, I64, I64, I, I, P]),
-        "vq_qgemm_dequant": (I, [P, P, I, P, I, P, I64, I64, I64, I64, P, I, I64, P, P]),
+        "vq_qgemm_dequant": (I, [P, P, I, P, I, P, I64, I64, I64, I64, P, I, I64, P, P, P]),
+        "vq_qgemm_workspace_bytes": (I64, [I64, I64, I64]),
         "vq_route_workspace_elems": (I64, [I64]),
         "vq_route_rel_l1": (I, [P, P, I, I64, D, I, I, P, P, P, P]),
         "vq_quant_residual": (I, [P, I, I64, I64, I64, I, I, P, I64, P, P, P]),
@@ -215,8 +217,12 @@ def vq_hadamard_block(x: torch.Tensor, out_dtype=None, normalize: bool = True, b
 
 def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor, b_bits: int,
                      k0: int | None = None, out_dtype=torch.bfloat16, sa_per_token: bool = True,
-                     acc_debug: bool = False, y=None, acc=None):
-    """Y = dequant(A_codes . B_codes^T).  Returns y, or (y, acc int32 [P x M x N]) with acc_debug."""
+                     acc_debug: bool = False, y=None, acc=None, ws=None):
+    """Y = dequant(A_codes . B_codes^T).  Returns y, or (y, acc int32 [P x M x N]) with acc_debug.
+
+    ws: None uses a zero-filled workspace kept per device and stream (the library leaves it
+    zeroed after every call), a tensor of vq_qgemm_workspace_bytes() bytes is used as
+    given, False runs without the remainder split."""
     _dev(a, "a")
     m, kp = a.shape
     n = b.shape[0]
@@ -228,10 +234,31 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
     _out2d(y, "y", m, n, a.device)
     if acc_debug:
         _buf(acc, "acc", 4 * (2 if k0 < kp else 1) * m * n, a.device)
+    ws = _gemm_workspace(m, n, k0, a.device) if ws is None else ws
+    if ws is not False:
+        _buf(ws, "ws", int(_lib.vq_qgemm_workspace_bytes(m, n, k0)), a.device)
     _check("vq_qgemm_dequant", _lib.vq_qgemm_dequant(
         _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
-        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None), _stream(a)))
+        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None),
+        None if ws is False else _ptr(ws), _stream(a)))
     return (y, acc) if acc_debug else y
+
+
+_GEMM_WS = {}
+
+
+def _gemm_workspace(m, n, k0, device):
+    """The remainder-split workspace for this shape: one zero-filled buffer per device and
+    stream, grown on demand (calls on one stream never overlap, and each leaves it zeroed)."""
+    need = int(_lib.vq_qgemm_workspace_bytes(m, n, k0))
+    if need == 0:
+        return False
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    t = _GEMM_WS.get(key)
+    if t is None or t.numel() < need:
+        t = torch.zeros(need, dtype=torch.uint8, device=device)
+        _GEMM_WS[key] = t
+    return t
 
 
 def vq_route_rel_l1(x: torch.Tensor, y: torch.Tensor, threshold: float = 0.1, bits_hi: int = 8, bits_lo: int = 4,

@@ -29,6 +29,15 @@
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2; block b is mapped so that every XCD walks a contiguous range of tiles in a grouped
 // order (8 M-tiles per sweep over N), keeping the A and B slices it reuses in its L2.
+//
+// Remainder split: the tiles fill whole rounds of the persistent grid except the last
+// round, which would leave most CUs idle.  With a workspace, each remaining tile is split
+// into S ranges of K stages handled by different workgroups; each stores its int32
+// partial tile (device-coherent stores), then bumps an atomic count, and the workgroup
+// that arrives last adds the other partials and runs the epilogue.  Integer
+// sums are exact in any order, so the result is bit-identical to the unsplit tile, and
+// no workgroup ever waits for another.  The last arrival resets the tile's counter, so
+// the workspace is left zeroed for the next call.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -38,6 +47,7 @@
 namespace vqk {
 
 constexpr int BM = 256, BN = 256;
+constexpr int64_t QGEMM_WS_COUNTERS = 4096;  // arrival counters of up to 1024 remaining tiles
 constexpr int NT = 512;           // threads per workgroup
 constexpr int WTM = 128, WTN = 64;  // wave tile
 constexpr int MBLK = WTM / 32, NBLK = WTN / 32;
@@ -87,6 +97,11 @@ struct GArgs {
   int sa_tok;
   int vec_store;  // 16-byte stores are aligned (y 16-byte aligned, row pitch a multiple of 16 B)
   int tiles_m, tiles_n;
+  int dp_items;      // whole tiles: items [0, dp_items) are tiles [0, dp_items)
+  int split;         // K ranges per remaining tile (1: no split)
+  int items;         // dp_items + (tiles - dp_items) * split
+  int32_t* ws_cnt;   // [tiles - dp_items] arrival counters (zero between calls)
+  uint64_t* ws_part;  // [(tiles - dp_items) * split][64][NT] partial accumulators (int32 pairs)
 };
 
 __device__ __forceinline__ v4i unpack_int4x16(u2v w) {
@@ -115,8 +130,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // wave grid 2 (M) x 4 (N)
-  const int T = g.tiles_m * g.tiles_n;
   const int nk = g.k0 / BK;
+  __shared__ int s_last;
 
   // ---- direct-load assignment: instruction q of this wave fills 1 KB of a stage.
   int ra[C::LA], rb[C::LB];  // tile-local rows loaded by this lane
@@ -137,9 +152,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int8_t* ga[C::LA];
   const uint8_t* gb[C::LB];
   int m0 = 0, n0 = 0;
-  auto set_tile = [&](int vt) {
+  int kb0 = 0, nks = nk;    // the item's first stage and stage count
+  int part = -1, rslot = 0;  // K range of a split tile (-1: whole tile) and its remainder index
+  auto set_tile = [&](int w) {
+    int ti = w;
+    if (w < g.dp_items) {
+      kb0 = 0;
+      nks = nk;
+      part = -1;
+    } else {
+      const int j = w - g.dp_items;
+      rslot = j / g.split;
+      part = j - rslot * g.split;
+      ti = g.dp_items + rslot;
+      kb0 = part * nk / g.split;
+      nks = (part + 1) * nk / g.split - kb0;
+    }
     int tm, tn;
-    tile_of(vt, g.tiles_m, g.tiles_n, tm, tn);
+    tile_of(ti, g.tiles_m, g.tiles_n, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
 #pragma unroll
@@ -158,7 +188,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto issue_prologue = [&]() {
 #pragma unroll
     for (int s = 0; s < C::NST - 1; ++s)
-      if (s < nk) issue(s * BK, s);
+      if (s < nks) issue((kb0 + s) * BK, s);
   };
   // Scales of a tile's rows and columns: loaded into registers early, written to LDS late.
   float sc_a[P], sc_b[P];
@@ -256,7 +286,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // and first NST-1 stages are requested before the current tile's epilogue, so its
   // load latency and this tile's output stores overlap.
   int vt = blockIdx.x;
-  if (vt >= T) return;
+  if (vt >= g.items) return;
   set_tile(vt);
   issue_prologue();
   load_scales();
@@ -275,7 +305,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // kt+NST-1, and the first half of stage kt+1 is read while the last half of stage kt
     // runs.  (H is even, so the next stage's first half lands in F[0].)
     Frag F[2];
-    wait_loads(min(C::NST - 2, nk - 1));
+    wait_loads(min(C::NST - 2, nks - 1));
     barrier_nofence();
     load_half(0, 0, F[0]);
     int kt = 0, slot = 0;
@@ -290,7 +320,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // Steady state: every stage refills a stage and keeps NST-3 load groups in flight.
     // The body has no branch, so the waits the compiler inserts for the fragments stay
     // partial (lgkmcnt of the reads issued later) instead of draining all LDS reads.
-    for (; kt < nk - (C::NST - 1); ++kt) {
+    for (; kt < nks - (C::NST - 1); ++kt) {
       const int next = slot + 1 == C::NST ? 0 : slot + 1;
       const int refill = slot == 0 ? C::NST - 1 : slot - 1;
 #pragma unroll
@@ -301,22 +331,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
       wait_vmcnt<(C::NST - 3) * C::L>();
       barrier_nofence();
-      issue((kt + C::NST - 1) * BK, refill);
+      issue((kb0 + kt + C::NST - 1) * BK, refill);
       load_half(next, 0, F[0]);
       mma_half(F[(H - 1) & 1]);
       interleave();
       slot = next;
     }
     // Last NST-1 stages: nothing left to load; fewer groups in flight each stage.
-    for (; kt < nk; ++kt) {
+    for (; kt < nks; ++kt) {
       const int next = slot + 1 == C::NST ? 0 : slot + 1;
 #pragma unroll
       for (int h = 0; h < H - 1; ++h) {
         load_half(slot, h + 1, F[(h + 1) & 1]);
         mma_half(F[h & 1]);
       }
-      if (kt + 1 < nk) {
-        wait_loads(nk - 2 - kt);
+      if (kt + 1 < nks) {
+        wait_loads(nks - 2 - kt);
         barrier_nofence();
         load_half(next, 0, F[0]);
       }
@@ -324,9 +354,54 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       slot = next;
     }
 
+    // ------------------------------------------------------------ remainder split
+    if (part >= 0) {
+      // Every item after a split one is split too and belongs to another workgroup, so
+      // this is the block's last item and nothing is in flight.  The partials move with
+      // device-scope relaxed atomic stores and loads, which write through and bypass the
+      // per-XCD L2: a device-scope fence would instead write back and invalidate the whole
+      // L2 under every other workgroup of the XCD.  A store is performed device-wide once
+      // vmcnt reaches 0, and the count is bumped only after that; the last arrival loads
+      // the other partials only after it has read the count.
+      uint64_t* mine = g.ws_part + (int64_t)(rslot * g.split + part) * (64 * NT) + tid;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint64_t v = (uint64_t)(uint32_t)acc[mb][nb][2 * i] | ((uint64_t)(uint32_t)acc[mb][nb][2 * i + 1] << 32);
+            __hip_atomic_store(mine + (int64_t)((mb * NBLK + nb) * 8 + i) * NT, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(&g.ws_cnt[rslot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 g.split - 1;
+      __syncthreads();
+      if (!s_last) break;
+      for (int p2 = 0; p2 < g.split; ++p2) {
+        if (p2 == part) continue;
+        const uint64_t* src = g.ws_part + (int64_t)(rslot * g.split + p2) * (64 * NT) + tid;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const uint64_t v = __hip_atomic_load(src + (int64_t)((mb * NBLK + nb) * 8 + i) * NT, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+              acc[mb][nb][2 * i] += (int)(uint32_t)v;
+              acc[mb][nb][2 * i + 1] += (int)(uint32_t)(v >> 32);
+            }
+      }
+      if (tid == 0) __hip_atomic_store(&g.ws_cnt[rslot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // ------------------------------------------------------------ epilogue
     const int nvt = vt + (int)gridDim.x;
-    const bool has_next = nvt < T;
+    const bool has_next = nvt < g.items;
     const int cm0 = m0, cn0 = n0;  // this tile
     barrier_nofence();             // every wave is done with the ring
     int steps1 = 0;
@@ -477,6 +552,26 @@ namespace vq_internal {
 
 using namespace vqk;
 
+// Remainder split of a tile grid: K ranges per remaining tile (1: none).  A range's
+// partial (256 KB of int32) is stored and reloaded through one CU, which costs about
+// as much as 15-20 stages of its MFMA work: measured at the workload shapes, two ranges
+// pay off once K has at least 96 stages of 64 codes (17776 x 12288 x 3072: 5-6%
+// faster), while at 30 or 48 stages any split is slower or even.
+static int split_of(int tiles, int grid, int nk) {
+  const int rem = tiles % grid;
+  if (rem == 0 || nk < 96 || grid > QGEMM_WS_COUNTERS / 4) return 1;
+  return grid / rem >= 2 ? 2 : 1;
+}
+
+int64_t qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0) {
+  const int tiles = (int)(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+  const int grid = persistent_blocks();
+  const int s = split_of(tiles, grid, (int)(k0 / 64));
+  if (s == 1) return 0;
+  const int64_t rem = tiles % grid;
+  return QGEMM_WS_COUNTERS + rem * s * (int64_t)(32 * NT * 16);
+}
+
 hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   GArgs a{};
   a.a = p.a;
@@ -496,7 +591,16 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.tiles_m = (int)((p.m + BM - 1) / BM);
   a.tiles_n = (int)((p.n + BN - 1) / BN);
   const int tiles = a.tiles_m * a.tiles_n;
-  const int grid = tiles < persistent_blocks() ? tiles : persistent_blocks();
+  const int pb = persistent_blocks();
+  // The split is chosen on 64-code stages; a kernel with 128-code stages still gets at
+  // least two stages per range.
+  const int split = p.ws ? split_of(tiles, pb, (int)(p.k0 / 64)) : 1;
+  a.split = split;
+  a.dp_items = split > 1 ? tiles - tiles % pb : tiles;
+  a.items = a.dp_items + (tiles - a.dp_items) * split;
+  a.ws_cnt = split > 1 ? reinterpret_cast<int32_t*>(p.ws) : nullptr;
+  a.ws_part = split > 1 ? reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(p.ws) + QGEMM_WS_COUNTERS) : nullptr;
+  const int grid = a.items < pb ? a.items : pb;
   const bool dual = p.k0 < p.kp;
   if (p.b_bits == 8) return launch_out<8>(a, p.out_dt, dual, grid, st);
   return launch_out<4>(a, p.out_dt, dual, grid, st);

@@ -217,9 +217,14 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
 
 // ------------------------------------------------------------------ GEMM
 
+int64_t vq_qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0) {
+  if (m < 1 || n < 1 || k0 < 1 || m >= kMaxDim || n >= kMaxDim || k0 >= kMaxDim) return 0;
+  return vq_internal::qgemm_workspace_bytes(m, n, k0);
+}
+
 vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits,
                            const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0, void* y, vq_dtype out_dt,
-                           int64_t ldy, int32_t* acc_debug, hipStream_t stream) {
+                           int64_t ldy, int32_t* acc_debug, void* ws, hipStream_t stream) {
   if (!a || !sa || !b || !sb || !y) return VQ_ERR_INVALID_ARG;
   if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
   if (sa_per_token != 0 && sa_per_token != 1) return VQ_ERR_INVALID_ARG;
@@ -229,6 +234,7 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
   if (kp % VQ_K_ALIGN || k0 % VQ_K_ALIGN || k0 > kp || kp - k0 > VQ_MAX_OUTLIERS) return VQ_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b)) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
+  if (ws && !aligned16(ws)) return VQ_ERR_SHAPE;
   vq_internal::GemmParams p{};
   p.a = a;
   p.sa = sa;
@@ -244,6 +250,7 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
   p.out_dt = (int)out_dt;
   p.ldy = ldy;
   p.acc_debug = acc_debug;
+  p.ws = ws;
   return hip_status(vq_internal::launch_qgemm(p, stream));
 }
 
@@ -284,12 +291,13 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
     return VQ_ERR_UNSUPPORTED;
   if (n_rows > 0 && (!aligned16(a2) || !aligned16(ws))) return VQ_ERR_SHAPE;
   // Every row as without decomposition (this also validates a, sa, b, sb, y and the sizes).
-  vq_status st = vq_qgemm_dequant(a, sa, 1, b, b_bits, sb, m, n, kp, kp, y, out_dt, ldy, nullptr, stream);
+  vq_status st = vq_qgemm_dequant(a, sa, 1, b, b_bits, sb, m, n, kp, kp, y, out_dt, ldy, nullptr, nullptr, stream);
   if (st != VQ_OK || n_rows == 0) return st;
   // Both terms of every listed row in float32: y12 = fl32(acc * fl32(s * sw)) over the
   // stacked operand [q1 rows; q2 rows].
   float* y12 = reinterpret_cast<float*>(ws);
-  st = vq_qgemm_dequant(a2, sa2, 1, b, b_bits, sb, 2 * n_rows, n, kp, kp, y12, VQ_F32, n, nullptr, stream);
+  st = vq_qgemm_dequant(a2, sa2, 1, b, b_bits, sb, 2 * n_rows, n, kp, kp, y12, VQ_F32, n, nullptr, nullptr,
+                        stream);
   if (st != VQ_OK) return st;
   return hip_status(vq_internal::launch_residual_merge(y12, n_rows, n, rows_dev, m, y, (int)out_dt, ldy, stream));
 }

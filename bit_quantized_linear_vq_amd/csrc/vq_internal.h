@@ -49,7 +49,9 @@ struct GemmParams {
   int out_dt;
   int64_t ldy;
   int32_t* acc_debug;
+  void* ws;  // remainder-split workspace or nullptr
 };
+int64_t qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0);
 hipError_t launch_qgemm(const GemmParams& g, hipStream_t st);
 
 hipError_t launch_residual_quant(const void* x, int dtype, int64_t ldx, int64_t m, int64_t k, const int32_t* rows,

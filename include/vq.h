@@ -177,11 +177,20 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
  *            a 16-byte aligned y whose row pitch is a multiple of 16 bytes takes the
  *            vector-store path)
  *   acc_debug device int32 [P x m x n] or NULL: receives the raw accumulators
+ *   ws       device workspace of vq_qgemm_workspace_bytes(m, n, k0) bytes (16-byte
+ *            aligned, zero-filled before its first use), or NULL.  With it, the 256 x 256
+ *            tiles that do not fill a whole round of the persistent grid are split into
+ *            ranges of K handled by different workgroups; each range's int32 partial goes
+ *            through the workspace and the last one to finish adds them, so the result is
+ *            bit-identical to the unsplit GEMM.  Every call leaves the workspace
+ *            zero-filled; calls that share one must not overlap.  A size of 0 means the
+ *            shape gains nothing from the split (ws is then not used).
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8, out_dt).
  */
+int64_t vq_qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0);
 vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b,
                            int b_bits, const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0,
-                           void* y, vq_dtype out_dt, int64_t ldy, int32_t* acc_debug,
+                           void* y, vq_dtype out_dt, int64_t ldy, int32_t* acc_debug, void* ws,
                            hipStream_t stream);
 
 /*

@@ -121,14 +121,15 @@ def test_pack_weights_validation(lib, kw, want):
 
 def gemm(lib, **kw):
     a = dict(a=FAKE, sa=FAKE, tok=1, b=FAKE, bb=8, sb=FAKE, m=100, n=64, kp=1920, k0=1920, y=FAKE, odt=BF16,
-             ldy=64, acc=NULL, stream=NULL)
+             ldy=64, acc=NULL, ws=NULL, stream=NULL)
     a.update(kw)
     return lib.vq_qgemm_dequant(a["a"], a["sa"], a["tok"], a["b"], a["bb"], a["sb"], a["m"], a["n"], a["kp"],
-                                a["k0"], a["y"], a["odt"], a["ldy"], a["acc"], a["stream"])
+                                a["k0"], a["y"], a["odt"], a["ldy"], a["acc"], a["ws"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(a=NULL), INVALID),
+    (dict(ws=ctypes.c_void_p(0x10008)), SHAPE),  # workspace not 16-byte aligned
     (dict(sb=NULL), INVALID),
     (dict(y=NULL), INVALID),
     (dict(odt=5), INVALID),
@@ -369,3 +370,19 @@ def test_step_control_validation(lib):
     for bad in (vq.ControlParams(float("nan"), 0.15, 3, 8, 4, 0.1, 0.01), vq.ControlParams(0.05, 0.15, -1, 8, 4, 0.1, 0.01),
                 vq.ControlParams(0.05, 0.15, 3, 5, 4, 0.1, 0.01), vq.ControlParams(0.05, 0.15, 3, 8, 4, 0.1, float("nan"))):
         assert call(p=bad) == INVALID
+
+
+def test_gemm_workspace_sizes(lib):
+    """Remainder-split workspace (256 persistent workgroups when no GPU is visible): 4 KB of
+    counters plus a 256 KB int32 partial per K range of every tile past the last whole
+    round, two ranges per tile, only when K has at least 96 stages of 64 codes."""
+    part = 256 * 256 * 4
+    assert lib.vq_qgemm_workspace_bytes(17776, 3072, 12288) == 4096 + 72 * 2 * part  # 840 tiles
+    assert lib.vq_qgemm_workspace_bytes(300, 320, 6144) == 4096 + 4 * 2 * part         # 4 tiles
+    assert lib.vq_qgemm_workspace_bytes(17776, 5760, 1920) == 0   # 30 stages: the split does not pay
+    assert lib.vq_qgemm_workspace_bytes(17776, 12288, 3072) == 0  # 48 stages
+    assert lib.vq_qgemm_workspace_bytes(35552, 3072, 3072) == 0
+    assert lib.vq_qgemm_workspace_bytes(4096, 4096, 12288) == 0   # exactly one round
+    assert lib.vq_qgemm_workspace_bytes(512, 33280, 8192) == 4096 + 4 * 2 * part   # 260 tiles: 4 left over
+    assert lib.vq_qgemm_workspace_bytes(4864, 6144, 8192) == 0    # 456 tiles: 200 left, no room for two ranges
+    assert lib.vq_qgemm_workspace_bytes(0, 64, 12288) == 0
