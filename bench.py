@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--calibrate", action="store_true",
                    help="only time the static-scale calibration (clipping-percentile search) on the "
                         "workload's activations and exit")
+    p.add_argument("--hadamard", action="store_true",
+                   help="only time the standalone 128-point block Hadamard rotation on the 17776 x 12288 "
+                        "activations (bf16 in and out) beside a device copy of the same bytes, and exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times) and exit; "
                         "rocprofv3 counters of that copy scale FETCH_SIZE/WRITE_SIZE to bytes")
@@ -296,6 +299,44 @@ def calibrate(args, vq, gen, torch, dev):
         "input_bytes": nbytes, "call_gbs": round(nbytes / (call_ms * 1e-3) / 1e9, 1)}))
 
 
+def hadamard(args, vq, gen, torch, dev):
+    """Time vq_hadamard_block (standalone rotation, normalized, bf16 -> bf16) on the c4
+    activations, and a device copy moving the same bytes (2 B read, 2 B written per
+    element), both with HIP events around each launch on the launch stream."""
+    x = gen.make_x(4).to(dev)  # 17776 x 12288 bf16: 437 MB, beyond the Infinity Cache
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+
+    had_us = timed(lambda: vq.vq_hadamard_block(x, y=y))
+    copy_us = timed(lambda: y.copy_(x))
+    nbytes = 4 * x.numel()
+    gbs = nbytes / (had_us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "block Hadamard rotation GB/s", "value": round(gbs, 1), "unit": "GB/s",
+        "higher_is_better": True, "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": "c4_activations_hadamard128", "rows": x.shape[0], "cols": x.shape[1],
+                   "in_dtype": "bf16", "out_dtype": "bf16", "normalize": True},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes, "avg_us": round(had_us, 2),
+                     "kernel": "k_hadamard"},
+        "stream_ref": {"op": "device copy of the same tensor (2 B read, 2 B written per element)",
+                       "avg_us": round(copy_us, 2), "achieved": round(nbytes / (copy_us * 1e-6) / 1e9, 1),
+                       "unit": "GB/s"}}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -320,6 +361,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate:
         calibrate(args, vq, gen, torch, dev)
+        return
+    if args.hadamard:
+        hadamard(args, vq, gen, torch, dev)
         return
     L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx)
     stream = torch.cuda.current_stream(dev)
