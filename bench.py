@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--hadamard", action="store_true",
                    help="only time the standalone 128-point block Hadamard rotation on the 17776 x 12288 "
                         "activations (bf16 in and out) beside a device copy of the same bytes, and exit")
+    p.add_argument("--control", action="store_true",
+                   help="only time the per-block step control (TDC skip test, PDR overrides, DMPQ route) "
+                        "over the 42 routed blocks' statistics and exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times) and exit; "
                         "rocprofv3 counters of that copy scale FETCH_SIZE/WRITE_SIZE to bytes")
@@ -337,6 +340,50 @@ def hadamard(args, vq, gen, torch, dev):
                        "unit": "GB/s"}}))
 
 
+def control(args, vq, gen, torch, dev):
+    """Time vq_step_control for the 42 routed blocks of one denoising step: each decision
+    reduces the block's two cached residual deltas (E) and its previous input/output
+    (Gamma), 65536 bf16 values each as in the routing workload, then applies the rules."""
+    c = gen.CONFIGS[5]
+    blocks = []
+    for l in range(c["layers"]):
+        x, y, _ = gen.make_route_pair(5, l)
+        d_old, d_new, _ = gen.make_route_pair(5, l + 100)
+        blocks.append([t.to(dev) for t in (d_new, d_old, x, y)] + [vq.vq_control_state(dev)])
+    params = vq.ControlParams(0.05, 0.15, 3, c["route_hi_bits"], c["route_lo_bits"], c["route_threshold"], 0.01)
+    nw = int(vq._lib.vq_control_workspace_elems())
+    ws = torch.empty(nw, dtype=torch.float64, device=dev)
+    outs = [torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.float64, device=dev), torch.empty(1, dtype=torch.float64, device=dev)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        for dn, do, x, y, st in blocks:
+            vq.vq_step_control(st, params, delta_new=dn, delta_old=do, x_prev=x, y_prev=y, ws=ws, skip=outs[0],
+                               bits=outs[1], e=outs[2], gamma=outs[3])
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (args.steps * len(blocks))
+    nbytes = 4 * c["route_n"] * 2
+    print(json.dumps({
+        "metric": "step-control decision time", "value": round(us, 3), "unit": "us per block decision",
+        "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": "c5_dmpq_42_blocks_control", "blocks": len(blocks), "elements_per_tensor": c["route_n"],
+                   "dtype": "bf16"},
+        "roofline": {"bound": "latency", "bytes_per_decision": nbytes,
+                     "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "note": "three launches per decision (two fixed-order relative-L1 reductions and one "
+                             "deciding wave); HBM moves 512 KB per decision; the time includes the "
+                             "Python binding's per-call work, which here exceeds the GPU's"}}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -364,6 +411,9 @@ def main():
         return
     if args.hadamard:
         hadamard(args, vq, gen, torch, dev)
+        return
+    if args.control:
+        control(args, vq, gen, torch, dev)
         return
     L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx)
     stream = torch.cuda.current_stream(dev)

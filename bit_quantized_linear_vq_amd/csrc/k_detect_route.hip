@@ -236,14 +236,30 @@ __global__ __launch_bounds__(256) void k_route_partial(const void* __restrict__ 
   }
 }
 
-__global__ void k_route_final(const double* ws, int blocks, double threshold, int hi, int lo, double* gamma,
-                              int32_t* bits) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double a = 0.0, b = 0.0;
-  for (int i = 0; i < blocks; ++i) {
+// Sums of the per-block partial pairs (ws[2i], ws[2i + 1]) by one wave in a fixed order:
+// lane l adds the pairs l, l + 64, ... in turn, then a butterfly over the lanes.  Every
+// lane returns the totals.
+__device__ __forceinline__ void sum_pairs_wave(const double* ws, int blocks, double& a, double& b) {
+  const int lane = threadIdx.x & 63;
+  a = 0.0;
+  b = 0.0;
+  for (int i = lane; i < blocks; i += 64) {
     a += ws[2 * i];
     b += ws[2 * i + 1];
   }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    a += __shfl_xor(a, d, 64);
+    b += __shfl_xor(b, d, 64);
+  }
+}
+
+__global__ void k_route_final(const double* ws, int blocks, double threshold, int hi, int lo, double* gamma,
+                              int32_t* bits) {
+  if (threadIdx.x >= 64 || blockIdx.x != 0) return;
+  double a, b;
+  sum_pairs_wave(ws, blocks, a, b);
+  if (threadIdx.x != 0) return;
   const double g = b > 0.0 ? a / b : __builtin_inf();
   if (gamma) *gamma = g;
   *bits = g > threshold ? hi : lo;
@@ -255,34 +271,26 @@ struct ControlParams {
   int max_skips, bits_hi, bits_lo;
 };
 
-__device__ __forceinline__ void sum_pairs(const double* ws, int blocks, double& a, double& b) {
-  a = 0.0;
-  b = 0.0;
-  for (int i = 0; i < blocks; ++i) {
-    a += ws[2 * i];
-    b += ws[2 * i + 1];
-  }
-}
-
 // ws_e / ws_g: partial sums of the two relative-L1 statistics (blocks_e / blocks_g = 0 when
 // absent).  state[0] = consecutive skips (int32), state + 8 = accumulated error (double).
 __global__ void k_control_final(const double* ws_e, int blocks_e, const double* ws_g, int blocks_g,
                                 const int32_t* n_out, int64_t channels, ControlParams p, uint8_t* state,
                                 int32_t* skip, int32_t* bits, double* e_out, double* g_out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int32_t* skips = reinterpret_cast<int32_t*>(state);
-  double* drift = reinterpret_cast<double*>(state + 8);
+  if (threadIdx.x >= 64 || blockIdx.x != 0) return;
   double e = __builtin_nan(""), g = __builtin_nan("");
   if (blocks_e) {
     double num, den;
-    sum_pairs(ws_e, blocks_e, num, den);
+    sum_pairs_wave(ws_e, blocks_e, num, den);
     e = num == 0.0 ? 0.0 : (den > 0.0 ? num / den : __builtin_inf());
   }
   if (blocks_g) {
     double num, den;
-    sum_pairs(ws_g, blocks_g, num, den);
+    sum_pairs_wave(ws_g, blocks_g, num, den);
     g = den > 0.0 ? num / den : __builtin_inf();
   }
+  if (threadIdx.x != 0) return;
+  int32_t* skips = reinterpret_cast<int32_t*>(state);
+  double* drift = reinterpret_cast<double*>(state + 8);
   if (e_out) *e_out = e;
   if (g_out) *g_out = g;
   const int s = *skips;
