@@ -65,15 +65,17 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 
 namespace vq_internal {
 
-// One persistent workgroup per compute unit (each needs most of a CU's LDS).
+// One persistent workgroup per compute unit (each needs most of a CU's LDS).  The count
+// is read once per process (thread-safe static initialization); without a visible device
+// it is taken as MI355X's 256.
 inline int persistent_blocks() {
-  static int n = 0;
-  if (n == 0) {
+  static const int n = [] {
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    n = cus;
-  }
+    return cus;
+  }();
   return n;
 }
 
