@@ -29,6 +29,7 @@ EXPORTS = (
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant", "vq_qgemm_workspace_bytes",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
     "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
+    "vq_mx_gemm_workspace_bytes",
     "vq_calib_hist_bins", "vq_calib_static_scale", "vq_control_workspace_elems", "vq_step_control",
     "vq_status_string", "vq_last_hip_error", "vq_version",
 )
@@ -73,7 +74,8 @@ def _load():
         "vq_mx_code_bytes": (I64, [I64, I64, I]),
         "vq_mx_scale_bytes": (I64, [I64, I64]),
         "vq_mx_quant": (I, [P, I, I64, I64, I64, I, P, P, P]),
-        "vq_mx_gemm": (I, [P, P, I, P, P, I, I64, I64, I64, P, I, I64, P]),
+        "vq_mx_gemm": (I, [P, P, I, P, P, I, I64, I64, I64, P, I, I64, P, P]),
+        "vq_mx_gemm_workspace_bytes": (I64, [I64, I64, I64]),
         "vq_calib_hist_bins": (I64, []),
         "vq_calib_static_scale": (I, [P, I, I64, I64, I64, I, P, I32, P, P, P, P, P, P, P]),
         "vq_status_string": (ctypes.c_char_p, [I]),
@@ -248,9 +250,13 @@ _GEMM_WS = {}
 
 
 def _gemm_workspace(m, n, k0, device):
-    """The remainder-split workspace for this shape: one zero-filled buffer per device and
-    stream, grown on demand (calls on one stream never overlap, and each leaves it zeroed)."""
-    need = int(_lib.vq_qgemm_workspace_bytes(m, n, k0))
+    return _workspace(int(_lib.vq_qgemm_workspace_bytes(m, n, k0)), device)
+
+
+def _workspace(need, device):
+    """A remainder-split workspace of `need` bytes: one zero-filled buffer per device and
+    stream, shared by both GEMMs and grown on demand (calls on one stream never overlap,
+    and each leaves it zeroed)."""
     if need == 0:
         return False
     key = (device, torch.cuda.current_stream(device).cuda_stream)
@@ -355,8 +361,11 @@ def vq_mx_quant(x: torch.Tensor, fmt: str = "fp4", codes=None, scales=None):
 
 
 def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: torch.Tensor, fb: str = "fp4",
-               out_dtype=torch.bfloat16, y=None):
-    """Y = dec(A) . dec(B)^T on the scaled MFMA; a, b are the MX code buffers of vq_mx_quant."""
+               out_dtype=torch.bfloat16, y=None, ws=None):
+    """Y = dec(A) . dec(B)^T on the scaled MFMA; a, b are the MX code buffers of vq_mx_quant.
+
+    ws: None uses the zero-filled workspace kept per device and stream, a tensor of
+    vq_mx_gemm_workspace_bytes() bytes is used as given, False runs without the split."""
     _dev(a, "a")
     m = a.shape[0]
     n = b.shape[0]
@@ -364,9 +373,13 @@ def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: 
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     _out2d(y, "y", m, n, a.device)
+    need = int(_lib.vq_mx_gemm_workspace_bytes(m, n, k))
+    ws = _workspace(need, a.device) if ws is None else ws
+    if ws is not False:
+        _buf(ws, "ws", need, a.device)
     _check("vq_mx_gemm", _lib.vq_mx_gemm(
         _ptr(a), _ptr(sa), _MX.get(fa, -1), _ptr(b), _ptr(sb), _MX.get(fb, -1), m, n, k,
-        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _stream(a)))
+        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), None if ws is False else _ptr(ws), _stream(a)))
     return y
 
 

@@ -61,6 +61,60 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = (t % width) / gsz;
 }
 
+// ---- remainder split: exchange of a K range's partial accumulators.
+// A lane's accumulators (MB x NB blocks of 16 32-bit values) travel as 64-bit words; word
+// w of thread t sits at part[w * nt + t], so each wave-wide access is contiguous.  The
+// words move with device-scope relaxed atomic stores and loads (write-through, no L2
+// write-back or invalidate), a store being performed device-wide once vmcnt reaches 0.
+template <typename V, int MB, int NB>
+__device__ __forceinline__ void split_publish(uint64_t* part, int nt, int tid, const V (&acc)[MB][NB]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // Elements are copied out first: a bit cast applied to a vector element in place
+        // reads the vector's first element whatever the index.
+        const auto lo = acc[mb][nb][2 * i], hi = acc[mb][nb][2 * i + 1];
+        const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+        __hip_atomic_store(part + (int64_t)((mb * NB + nb) * 8 + i) * nt + tid, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+}
+
+template <typename V, int MB, int NB>
+__device__ __forceinline__ void split_accumulate(const uint64_t* part, int nt, int tid, V (&acc)[MB][NB]) {
+  typedef decltype(acc[0][0][0] + 0) E;  // int or float
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint64_t v = __hip_atomic_load(part + (int64_t)((mb * NB + nb) * 8 + i) * nt + tid, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        acc[mb][nb][2 * i] += __builtin_bit_cast(E, (uint32_t)v);
+        acc[mb][nb][2 * i + 1] += __builtin_bit_cast(E, (uint32_t)(v >> 32));
+      }
+}
+
+// After this workgroup's partial is published: bump the tile's arrival count once the
+// stores are performed; true (for the whole workgroup) in the last of `parts` arrivals.
+__device__ __forceinline__ bool split_arrive(int32_t* cnt, int parts, int* s_flag) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// The last arrival, having added the other partials, leaves the count at zero.
+__device__ __forceinline__ void split_reset(int32_t* cnt) {
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace vqk
 
 namespace vq_internal {

@@ -140,6 +140,13 @@ struct MxArgs {
   int64_t ldy;
   int vec_store;
   int tiles_m, tiles_n;
+  // Remainder split (as in the integer GEMM): items [0, dp_items) are whole tiles, then
+  // every remaining tile as `split` ranges of K stages whose float32 partials meet in
+  // the workspace.  Two ranges at most: adding two partials is commutative, so the
+  // result does not depend on which range arrives last.
+  int dp_items, split, items;
+  int32_t* ws_cnt;
+  uint64_t* ws_part;
 };
 
 template <int FA, int S, int OUT_DT>
@@ -152,8 +159,8 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // wave grid 2 (M) x 4 (N)
-  const int T = g.tiles_m * g.tiles_n;
   const int nk = g.k / (MX_BK * S);  // ring stages along K
+  __shared__ int s_last;
   const int64_t a_rowb = (int64_t)g.k * MxFmt<FA>::W / 8;
   const int64_t b_rowb = g.k / 2;
 
@@ -208,9 +215,24 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const uint8_t* gs;
   int64_t s_pitch = 0;  // bytes between the scale slabs of consecutive steps
   int m0 = 0, n0 = 0;
-  auto set_tile = [&](int vt) {
+  int kb0 = 0, nks = nk;     // the item's first stage and stage count
+  int part = -1, rslot = 0;  // K range of a split tile (-1: whole tile) and its remainder index
+  auto set_tile = [&](int w) {
+    int ti = w;
+    if (w < g.dp_items) {
+      kb0 = 0;
+      nks = nk;
+      part = -1;
+    } else {
+      const int j = w - g.dp_items;
+      rslot = j / g.split;
+      part = j - rslot * g.split;
+      ti = g.dp_items + rslot;
+      kb0 = part * nk / g.split;
+      nks = (part + 1) * nk / g.split - kb0;
+    }
     int tm, tn;
-    tile_of(vt, g.tiles_m, g.tiles_n, tm, tn);
+    tile_of(ti, g.tiles_m, g.tiles_n, tm, tn);
     m0 = tm * MX_BM;
     n0 = tn * MX_BN;
 #pragma unroll
@@ -242,7 +264,7 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   auto issue_prologue = [&]() {
 #pragma unroll
     for (int s = 0; s < C::NST - 1; ++s)
-      if (s < nk) issue(s, s);
+      if (s < nks) issue(kb0 + s, s);
   };
 
   // ---- fragment offsets: rows 32*blk + (lane & 31); sub-step u, K half lane >> 5.
@@ -321,7 +343,7 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   };
 
   int vt = blockIdx.x;
-  if (vt >= T) return;
+  if (vt >= g.items) return;
   set_tile(vt);
   issue_prologue();
   for (;;) {
@@ -331,7 +353,7 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       for (int j = 0; j < MX_NBLK; ++j) acc[i][j] = v16f{};
 
     Frag f0, f1;
-    wait_loads(min(C::NST - 2, nk - 1));
+    wait_loads(min(C::NST - 2, nks - 1));
     barrier_nofence();
     load_sub(0, 0, f0);
     int kt = 0, slot = 0;
@@ -341,24 +363,24 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       // of stage kt+1 and meets the others at a barrier, which publishes stage kt+1 and
       // certifies that stage kt-1 is no longer read; that stage receives stage kt+NST-1,
       // and the first sub-step of stage kt+1 is read while the second one's MFMAs run.
-      for (; kt < nk - (C::NST - 1); ++kt) {
+      for (; kt < nks - (C::NST - 1); ++kt) {
         const int next = slot + 1 == C::NST ? 0 : slot + 1;
         const int refill = slot == 0 ? C::NST - 1 : slot - 1;
         load_sub(slot, 1, f1);
         mma_sub(f0);
         wait_vmcnt<(C::NST - 3) * C::L>();
         barrier_nofence();
-        issue(kt + C::NST - 1, refill);
+        issue(kb0 + kt + C::NST - 1, refill);
         load_sub(next, 0, f0);
         mma_sub(f1);
         slot = next;
       }
-      for (; kt < nk; ++kt) {
+      for (; kt < nks; ++kt) {
         const int next = slot + 1 == C::NST ? 0 : slot + 1;
         load_sub(slot, 1, f1);
         mma_sub(f0);
-        if (kt + 1 < nk) {
-          wait_loads(nk - 2 - kt);
+        if (kt + 1 < nks) {
+          wait_loads(nks - 2 - kt);
           barrier_nofence();
           load_sub(next, 0, f0);
         }
@@ -369,23 +391,23 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       // One sub-step per stage: the MFMAs of weight block 0 run on operands read during
       // stage kt-1, then the barrier as above, then the operands of stage kt+1 are read
       // while the MFMAs of weight block 1 run.
-      for (; kt < nk - (C::NST - 1); ++kt) {
+      for (; kt < nks - (C::NST - 1); ++kt) {
         const int next = slot + 1 == C::NST ? 0 : slot + 1;
         const int refill = slot == 0 ? C::NST - 1 : slot - 1;
         mma_nb(f0, 0);
         wait_vmcnt<(C::NST - 3) * C::L>();
         barrier_nofence();
-        issue(kt + C::NST - 1, refill);
+        issue(kb0 + kt + C::NST - 1, refill);
         load_sub(next, 0, f1);
         mma_nb(f0, 1);
         f0 = f1;
         slot = next;
       }
-      for (; kt < nk; ++kt) {
+      for (; kt < nks; ++kt) {
         const int next = slot + 1 == C::NST ? 0 : slot + 1;
         mma_nb(f0, 0);
-        if (kt + 1 < nk) {
-          wait_loads(nk - 2 - kt);
+        if (kt + 1 < nks) {
+          wait_loads(nks - 2 - kt);
           barrier_nofence();
           load_sub(next, 0, f1);
         }
@@ -395,9 +417,20 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       }
     }
 
+    // ------------------------------------------------------------ remainder split
+    if (part >= 0) {  // the block's last item: nothing is in flight
+      constexpr int WORDS = MX_MBLK * MX_NBLK * 8;
+      split_publish(g.ws_part + (int64_t)(rslot * g.split + part) * (WORDS * MX_NT), MX_NT, tid, acc);
+      if (!split_arrive(&g.ws_cnt[rslot], g.split, &s_last)) break;
+      for (int p2 = 0; p2 < g.split; ++p2)
+        if (p2 != part)
+          split_accumulate(g.ws_part + (int64_t)(rslot * g.split + p2) * (WORDS * MX_NT), MX_NT, tid, acc);
+      split_reset(&g.ws_cnt[rslot]);
+    }
+
     // ------------------------------------------------------------ epilogue
     const int nvt = vt + (int)gridDim.x;
-    const bool has_next = nvt < T;
+    const bool has_next = nvt < g.items;
     const int cm0 = m0, cn0 = n0;
     barrier_nofence();  // every wave is done with the ring
     if (has_next) {
@@ -487,8 +520,24 @@ hipError_t launch_mx_quant(const void* x, int dtype, int64_t ldx, int64_t rows, 
   return hipGetLastError();
 }
 
+// Remainder split of the MX GEMM: two K ranges per tile past the last whole round, when
+// K has at least 96 steps of 64 (the integer GEMM's measured break-even) and the ranges
+// fit in one round.
+static int mx_split_of(int tiles, int grid, int64_t k) {
+  const int rem = tiles % grid;
+  if (rem == 0 || k / 64 < 96 || grid > 1024 || grid / rem < 2) return 1;
+  return 2;
+}
+
+int64_t mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const int tiles = (int)(((m + MX_BM - 1) / MX_BM) * ((n + MX_BN - 1) / MX_BN));
+  const int grid = persistent_blocks();
+  if (mx_split_of(tiles, grid, k) == 1) return 0;
+  return 4096 + (int64_t)(tiles % grid) * 2 * (MX_MBLK * MX_NBLK * 8) * MX_NT * 8;
+}
+
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uint8_t* b, const uint8_t* sb, int64_t m,
-                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, hipStream_t st) {
+                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, void* ws, hipStream_t st) {
   MxArgs g{};
   g.a = a;
   g.sa = sa;
@@ -506,7 +555,13 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uin
   g.tiles_m = (int)((m + MX_BM - 1) / MX_BM);
   g.tiles_n = (int)((n + MX_BN - 1) / MX_BN);
   const int tiles = g.tiles_m * g.tiles_n;
-  const int grid = tiles < persistent_blocks() ? tiles : persistent_blocks();
+  const int pb = persistent_blocks();
+  g.split = ws ? mx_split_of(tiles, pb, k) : 1;
+  g.dp_items = g.split > 1 ? tiles - tiles % pb : tiles;
+  g.items = g.dp_items + (tiles - g.dp_items) * g.split;
+  g.ws_cnt = g.split > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  g.ws_part = g.split > 1 ? reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(ws) + 4096) : nullptr;
+  const int grid = g.items < pb ? g.items : pb;
   // Two 64-deep sub-steps per ring stage for FP4 activations when K allows it (with FP6
   // the doubled operand registers do not fit).
   const bool two = fa == MX_FP4 && k % 128 == 0;

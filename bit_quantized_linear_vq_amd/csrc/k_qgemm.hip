@@ -363,40 +363,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       // L2 under every other workgroup of the XCD.  A store is performed device-wide once
       // vmcnt reaches 0, and the count is bumped only after that; the last arrival loads
       // the other partials only after it has read the count.
-      uint64_t* mine = g.ws_part + (int64_t)(rslot * g.split + part) * (64 * NT) + tid;
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NBLK; ++nb)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint64_t v = (uint64_t)(uint32_t)acc[mb][nb][2 * i] | ((uint64_t)(uint32_t)acc[mb][nb][2 * i + 1] << 32);
-            __hip_atomic_store(mine + (int64_t)((mb * NBLK + nb) * 8 + i) * NT, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (tid == 0)
-        s_last = __hip_atomic_fetch_add(&g.ws_cnt[rslot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 g.split - 1;
-      __syncthreads();
-      if (!s_last) break;
-      for (int p2 = 0; p2 < g.split; ++p2) {
-        if (p2 == part) continue;
-        const uint64_t* src = g.ws_part + (int64_t)(rslot * g.split + p2) * (64 * NT) + tid;
-#pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NBLK; ++nb)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const uint64_t v = __hip_atomic_load(src + (int64_t)((mb * NBLK + nb) * 8 + i) * NT, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-              acc[mb][nb][2 * i] += (int)(uint32_t)v;
-              acc[mb][nb][2 * i + 1] += (int)(uint32_t)(v >> 32);
-            }
-      }
-      if (tid == 0) __hip_atomic_store(&g.ws_cnt[rslot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      split_publish(g.ws_part + (int64_t)(rslot * g.split + part) * (64 * NT), NT, tid, acc);
+      if (!split_arrive(&g.ws_cnt[rslot], g.split, &s_last)) break;
+      for (int p2 = 0; p2 < g.split; ++p2)
+        if (p2 != part) split_accumulate(g.ws_part + (int64_t)(rslot * g.split + p2) * (64 * NT), NT, tid, acc);
+      split_reset(&g.ws_cnt[rslot]);
     }
 
     // ------------------------------------------------------------ epilogue

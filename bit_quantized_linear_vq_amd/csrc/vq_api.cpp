@@ -330,9 +330,14 @@ vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64
   return hip_status(vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream));
 }
 
+int64_t vq_mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || n < 1 || k < 1 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % VQ_K_ALIGN) return 0;
+  return vq_internal::mx_gemm_workspace_bytes(m, n, k);
+}
+
 vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const uint8_t* b, const uint8_t* sb,
                      vq_mx_fmt fb, int64_t m, int64_t n, int64_t k, void* y, vq_dtype out_dt, int64_t ldy,
-                     hipStream_t stream) {
+                     void* ws, hipStream_t stream) {
   if (!a || !sa || !b || !sb || !y) return VQ_ERR_INVALID_ARG;
   if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
   if (m < 1 || n < 1 || k < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return VQ_ERR_INVALID_ARG;
@@ -340,7 +345,8 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
   if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b) || !aligned16(sa) || !aligned16(sb)) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
-  return hip_status(vq_internal::launch_mx_gemm(a, sa, (int)fa, b, sb, m, n, k, y, (int)out_dt, ldy, stream));
+  if (ws && !aligned16(ws)) return VQ_ERR_SHAPE;
+  return hip_status(vq_internal::launch_mx_gemm(a, sa, (int)fa, b, sb, m, n, k, y, (int)out_dt, ldy, ws, stream));
 }
 
 // ------------------------------------------------------------------ calibration

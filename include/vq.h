@@ -262,16 +262,23 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
  *   in fa (MXFP4 or MXFP6); b: weights [n x k], MXFP4 only (fb); codes and scales
  *   16-byte aligned; y as for vq_qgemm_dequant.  The sums are accumulated in float32 by
  *   the hardware, so y equals the exact sum rounded to float32 only up to the
- *   accumulation's rounding.  Errors: INVALID_ARG, SHAPE (k % 64, alignment),
- *   UNSUPPORTED (fa, fb other than MXFP4).
+ *   accumulation's rounding.  ws: device workspace of vq_mx_gemm_workspace_bytes(m, n,
+ *   k) bytes (16-byte aligned, zero-filled before its first use) or NULL; with it, the
+ *   tiles past the last whole round of the persistent grid are split into two K ranges
+ *   whose float32 partials are added once (y then differs from the unsplit GEMM by that
+ *   one rounding, within the same bound, and does not depend on the order the ranges
+ *   finish).  Every call leaves the workspace zeroed; calls sharing one must not
+ *   overlap.  Errors: INVALID_ARG, SHAPE (k % 64, alignment), UNSUPPORTED (fa, fb other
+ *   than MXFP4).
  */
 int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt);
 int64_t vq_mx_scale_bytes(int64_t rows, int64_t k);
 vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt,
                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
+int64_t vq_mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const uint8_t* b,
                      const uint8_t* sb, vq_mx_fmt fb, int64_t m, int64_t n, int64_t k, void* y,
-                     vq_dtype out_dt, int64_t ldy, hipStream_t stream);
+                     vq_dtype out_dt, int64_t ldy, void* ws, hipStream_t stream);
 
 /*
  * Static per-tensor activation scale by clipping-percentile search (Q-ARVD, Technical

@@ -312,13 +312,23 @@ def test_mx_quant_validation(lib, kw, want):
     (dict(sa=ctypes.c_void_p(0x10008)), SHAPE),
     (dict(b=ctypes.c_void_p(0x10004)), SHAPE),
     (dict(y=ctypes.c_void_p(0x10001)), SHAPE),
+    (dict(ws=ctypes.c_void_p(0x10008)), SHAPE),
 ])
 def test_mx_gemm_validation(lib, kw, want):
     a = dict(a=FAKE, sa=FAKE, fa=MXFP4, b=FAKE, sb=FAKE, fb=MXFP4, m=64, n=64, k=128, y=FAKE, out=BF16, ldy=64,
-             stream=NULL)
+             ws=NULL, stream=NULL)
     a.update(kw)
     assert lib.vq_mx_gemm(a["a"], a["sa"], a["fa"], a["b"], a["sb"], a["fb"], a["m"], a["n"], a["k"], a["y"],
-                          a["out"], a["ldy"], a["stream"]) == want
+                          a["out"], a["ldy"], a["ws"], a["stream"]) == want
+
+
+def test_mx_gemm_workspace_sizes(lib):
+    """Two float32 partials of 256 KB per tile past the last whole round, from 96 steps of 64."""
+    part = 256 * 256 * 4
+    assert lib.vq_mx_gemm_workspace_bytes(17776, 3072, 12288) == 4096 + 72 * 2 * part
+    assert lib.vq_mx_gemm_workspace_bytes(300, 320, 6144) == 4096 + 4 * 2 * part
+    assert lib.vq_mx_gemm_workspace_bytes(17776, 5760, 1920) == 0
+    assert lib.vq_mx_gemm_workspace_bytes(300, 320, 6100) == 0  # K not a multiple of 64
 
 
 def test_calib_validation(lib):

@@ -135,3 +135,27 @@ def test_fullsize_w4a4_ffn_down_sampled_rows(vq):
     bc, bsc = mx.quantize(numerics.to_f32(npb(w), "bf16"), "fp4")
     assert np.array_equal(ac_d[torch.from_numpy(rows).to(DEV)].cpu().numpy(), mx.pack(ac, "fp4"))
     check_gemm(y[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ac, asc, "fp4", bc, bsc)
+
+
+@pytest.mark.parametrize("fa", ["fp4", "fp6"])
+def test_mx_gemm_remainder_split(vq, fa):
+    """Every tile of a 4-tile GEMM with K = 6144 is split into two K ranges whose float32
+    partials are added once: within the same bound, close to the unsplit GEMM, identical
+    across calls, and the workspace is left zeroed."""
+    m, n, k = 300, 320, 6144
+    assert vq._lib.vq_mx_gemm_workspace_bytes(m, n, k) > 0
+    x = rand_x(m, k, torch.bfloat16, 77)
+    w = rand_x(n, k, torch.bfloat16, 78, spread=False)
+    ac_d, as_d = vq.vq_mx_quant(x.to(DEV), fa)
+    bc_d, bs_d = vq.vq_mx_quant(w.to(DEV), "fp4")
+    ws = torch.zeros(vq._lib.vq_mx_gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device=DEV)
+    y1 = vq.vq_mx_gemm(ac_d, as_d, fa, bc_d, bs_d, "fp4", torch.float32, ws=ws)
+    y2 = vq.vq_mx_gemm(ac_d, as_d, fa, bc_d, bs_d, "fp4", torch.float32, ws=ws)
+    y0 = vq.vq_mx_gemm(ac_d, as_d, fa, bc_d, bs_d, "fp4", torch.float32, ws=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert not ws[:4096].any()
+    ac, asc = mx.quantize(numerics.to_f32(npb(x), "bf16"), fa)
+    bc, bsc = mx.quantize(numerics.to_f32(npb(w), "bf16"), "fp4")
+    check_gemm(y1.cpu().numpy(), ac, asc, fa, bc, bsc)
+    check_gemm(y0.cpu().numpy(), ac, asc, fa, bc, bsc)
