@@ -161,7 +161,10 @@ class Layer:
                              device=dev)
         # The GEMM's remainder-split workspace (zeroed once; every call leaves it zeroed),
         # made here so that nothing is allocated while a step is captured in a graph.
+        # One buffer serves both GEMMs (calls on one stream never overlap).
         need = int(vq._lib.vq_qgemm_workspace_bytes(self.M, self.N, self.k0))
+        if mx:
+            need = max(need, int(vq._lib.vq_mx_gemm_workspace_bytes(self.M, self.N, self.K)))
         self.gws = torch.zeros(need, dtype=torch.uint8, device=dev) if need else False
         if mx:
             fmt = "fp4" if cfg == 5 else mx
@@ -199,7 +202,8 @@ class Layer:
     def gemm(self, layer):
         if self.use_mx(layer):
             bc, bs = self.mx_w[layer]
-            self.vq.vq_mx_gemm(self.mx_codes, self.mx_scales, self.mx_fmt, bc, bs, "fp4", self.y.dtype, y=self.y)
+            self.vq.vq_mx_gemm(self.mx_codes, self.mx_scales, self.mx_fmt, bc, bs, "fp4", self.y.dtype, y=self.y,
+                               ws=self.gws)
             return
         wc, ws = self.w[layer]
         if self.R:
