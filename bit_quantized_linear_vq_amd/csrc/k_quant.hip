@@ -9,10 +9,15 @@
 // Hadamard, weights quantized offline to 4 bits.
 //
 // Work layout: a row of K elements is read in passes of 1024 elements; in a pass each
-// of the 64 lanes of a wave owns 16 contiguous elements (two 16-byte loads, one
-// 16-byte store of codes).  A row is owned by W waves (W = 1, 2, 4 or 8) so that every
-// lane keeps at most 4 passes (64 floats) in registers: the row is read from HBM once,
-// reduced to its absolute maximum, and quantized from registers.
+// of the 64 lanes of a wave owns 16 elements as two 8-element pieces (one 16-byte load
+// and one 8-byte store of codes each).  Without rotation lane l owns elements 8l..8l+7
+// of each 512-element half of the pass, so every load and store instruction of a wave
+// covers one contiguous span; the rotation needs 16 contiguous elements per lane (see
+// fwht128).  A row is owned by W waves (W = 1, 2, 4 or 8) so that every lane keeps at
+// most 4 passes (64 floats) in registers: the row is read from HBM once, reduced to its
+// absolute maximum, and quantized from registers.  All loads of a row are issued before
+// any of them is used (addresses past the row end are clamped into the row and their
+// values discarded), so a wave waits for one memory latency per row, not one per pass.
 #include "dev_common.h"
 #include "vq_internal.h"
 
@@ -53,10 +58,21 @@ __device__ __forceinline__ void static_scale(float sgiven, float& r, float& s) {
   if (!(sgiven != 0.0f) || __builtin_isinf(r)) r = 0.0f;
 }
 
+// Eight storage elements (one 16-byte word) as float.
+template <int DT>
+__device__ __forceinline__ void decode8(const u4v& w, float* v) {
+  decode2<DT>(w.x, v[0], v[1]);
+  decode2<DT>(w.y, v[2], v[3]);
+  decode2<DT>(w.z, v[4], v[5]);
+  decode2<DT>(w.w, v[6], v[7]);
+}
+
 template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY, int NP>
 __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
+  static_assert(!(HAD && DUAL), "the rotation and the outlier partition are not combined");
   __shared__ float s_red[8][2];
-  __shared__ unsigned s_mask[DUAL ? MAX_MASK_WORDS : 1];
+  // Per wave: the outlier bits of the wave's NP passes (32 words of 32 channels each).
+  __shared__ unsigned s_mask[DUAL ? 8 * NPMAX * 32 : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -67,6 +83,11 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   const int slot = HAD ? ((lane & ~7) | perm8(lane & 7)) : lane;
   const float sigma = HAD ? had_sigma(perm8(lane & 7)) : 1.0f;
   const float qf = qmax_f(a);
+  // First element of piece h (0, 1) of pass j in this lane.
+  auto piece = [&](int j, int h) {
+    const int p0 = (wr + a.W * j) * 1024;
+    return HAD ? p0 + 16 * slot + 8 * h : p0 + 512 * h + 8 * lane;
+  };
 
   // Outlier channels gathered by this lane (the same for every row).
   int oidx[2] = {0, 0};
@@ -75,19 +96,32 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
     for (int i = 0; i < 2; ++i)
       if (lane + 64 * i < a.n_out) oidx[i] = a.idx[lane + 64 * i];
   }
-  // Bit mask of the outlier channels in LDS, built once the first row's loads are in
-  // flight (the index loads above are then the only ones it waits for).
-  bool mask_ready = !DUAL;
-  auto build_mask = [&]() {
-    const int words = (a.k + 31) >> 5;
-    for (int i = threadIdx.x; i < words; i += blockDim.x) s_mask[i] = 0u;
-    __syncthreads();
-    if (wave == 0) {
+  // Outlier bits of this lane's pieces (bit t: element t of the piece is an outlier), from
+  // the wave's own mask in LDS: cleared, outliers of its passes set, pieces read.  LDS
+  // operations of one wave complete in program order, so no barrier is involved (the
+  // fences keep the compiler from moving them across one another).  Built once the first
+  // row's loads are in flight.
+  unsigned obits[NP][2] = {};
+  bool bits_ready = !DUAL;
+  auto build_bits = [&]() {
+    unsigned* wm = s_mask + wave * (NPMAX * 32);
+    for (int i = lane; i < NP * 32; i += 64) wm[i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (lane + 64 * i < a.n_out) atomicOr(&s_mask[oidx[i] >> 5], 1u << (oidx[i] & 31));
+    for (int i = 0; i < 2; ++i) {
+      const int o = oidx[i];
+      const int pass = o >> 10;
+      if (lane + 64 * i < a.n_out && pass % a.W == wr && pass / a.W < NP)
+        atomicOr(&wm[(pass / a.W) * 32 + ((o & 1023) >> 5)], 1u << (o & 31));
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = piece(j, h) & 1023;
+        obits[j][h] = (wm[j * 32 + (e >> 5)] >> (e & 31)) & 0xFFu;
+      }
   };
 
   // Scales common to the whole tensor.
@@ -103,56 +137,70 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   for (int64_t rowbase = (int64_t)blockIdx.x * rpb; rowbase < a.rows; rowbase += (int64_t)gridDim.x * rpb) {
     const int64_t row = rowbase + rib;
     const bool row_ok = row < a.rows;
-    const char* xrow = reinterpret_cast<const char*>(a.x) + (row_ok ? row : 0) * a.ldx * (DT == DT_F32 ? 4 : 2);
+    const char* xrow = reinterpret_cast<const char*>(a.x) + (row_ok ? row : 0) * a.ldx * 2;
+
+    // Every load first (clamped into the row), then the decoding.
+    u4v raw[NP][2];
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = piece(j, h);
+        raw[j][h] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xrow + (int64_t)(e < a.k ? e : 0) * 2));
+      }
+    // The row's loads go out before anything that waits for the outlier indices.
+    __builtin_amdgcn_sched_barrier(0);
+    // Outlier partition: gathered by wave 0 of the row, at most 128 values.
+    unsigned short oraw[2] = {0, 0};
+    if constexpr (DUAL) {
+      if (wr == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) oraw[i] = reinterpret_cast<const unsigned short*>(xrow)[oidx[i]];
+      }
+    }
+
+    if constexpr (DUAL) {
+      if (!bits_ready) {  // wave-uniform
+        build_bits();
+        bits_ready = true;
+      }
+    }
 
     float v[NP][16];
     float lmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int e = (wr + a.W * j) * 1024 + 16 * slot;
-      if (row_ok && e < a.k) {
-        load16<DT>(xrow + (int64_t)e * (DT == DT_F32 ? 4 : 2), v[j]);
-      } else {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) v[j][t] = 0.0f;
-      }
-    }
-    if constexpr (DUAL) {
-      if (!mask_ready) {  // block-uniform: every thread of the block runs the same rows loop
-        build_mask();
-        mask_ready = true;
-      }
-    }
+      for (int h = 0; h < 2; ++h) {
+        decode8<DT>(raw[j][h], &v[j][8 * h]);
+        if (!(row_ok && piece(j, h) < a.k)) {
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int e = (wr + a.W * j) * 1024 + 16 * slot;
-      const bool act = row_ok && e < a.k;
+          for (int t = 0; t < 8; ++t) v[j][8 * h + t] = 0.0f;
+        }
+      }
       if constexpr (HAD) {
         fwht128(v[j], perm8(lane & 7));
       }
       if constexpr (DUAL) {
-        if (act) {
-          const unsigned bits16 = (s_mask[e >> 5] >> (e & 31)) & 0xFFFFu;
-          if (bits16) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
-              if ((bits16 >> t) & 1u) v[j][t] = 0.0f;
-          }
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if ((obits[j][h] >> t) & 1u) v[j][8 * h + t] = 0.0f;
       }
 #pragma unroll
       for (int t = 0; t < 16; ++t) lmax = fmaxf(lmax, fabsf(v[j][t]));
     }
 
-    // Outlier partition: gathered by wave 0 of the row, at most 128 values.
     float ov[2] = {0.0f, 0.0f};
     float omax = 0.0f;
     if constexpr (DUAL) {
       if (wr == 0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int jj = lane + 64 * i;
-          if (row_ok && jj < a.n_out) ov[i] = load1<DT>(xrow, oidx[i]);
+          float lo, hi;
+          decode2<DT>((unsigned)oraw[i], lo, hi);
+          ov[i] = (row_ok && lane + 64 * i < a.n_out) ? lo : 0.0f;
           omax = fmaxf(omax, fabsf(ov[i]));
         }
         omax = wave_max(omax);
@@ -191,27 +239,23 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
 
     if (row_ok) {
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const int e = (wr + a.W * j) * 1024 + 16 * slot;
-        if (e < a.k) {
-          unsigned u[16];
+      for (int j = 0; j < NP; ++j)
 #pragma unroll
-          for (int t = 0; t < 16; ++t) u[t] = qbyte(v[j][t], rr, qf);
-          if constexpr (OUT4) {
-            u2v w;
-            w.x = pack8_nibbles(u);
-            w.y = pack8_nibbles(u + 8);
-            *reinterpret_cast<u2v*>(reinterpret_cast<uint8_t*>(a.codes) + row * (a.kp / 2) + e / 2) = w;
-          } else {
-            u4v w;
-            w.x = pack4_lo(u[0], u[1], u[2], u[3]);
-            w.y = pack4_lo(u[4], u[5], u[6], u[7]);
-            w.z = pack4_lo(u[8], u[9], u[10], u[11]);
-            w.w = pack4_lo(u[12], u[13], u[14], u[15]);
-            *reinterpret_cast<u4v*>(reinterpret_cast<int8_t*>(a.codes) + row * a.kp + e) = w;
+        for (int h = 0; h < 2; ++h) {
+          const int e = piece(j, h);
+          if (e < a.k) {
+            unsigned u[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) u[t] = qbyte(v[j][8 * h + t], rr, qf);
+            if constexpr (OUT4) {
+              reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(a.codes) + row * (a.kp / 2) + e / 2)[0] =
+                  pack8_nibbles(u);
+            } else {
+              *reinterpret_cast<u2v*>(reinterpret_cast<int8_t*>(a.codes) + row * a.kp + e) =
+                  u2v{pack4_lo(u[0], u[1], u[2], u[3]), pack4_lo(u[4], u[5], u[6], u[7])};
+            }
           }
         }
-      }
       if constexpr (DUAL) {
         if (wr == 0) {
 #pragma unroll
@@ -362,6 +406,9 @@ hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st) {
   const int rpb = (block / 64) / W;
   int64_t blocks = (p.rows + rpb - 1) / rpb;
   if (p.maxonly && blocks > 2048) blocks = 2048;
+  // With the outlier partition every wave first waits for the outlier indices (its
+  // gathers need them); a bounded grid lets each wave pay that once over several rows.
+  if (p.n_out > 0 && blocks > 1024) blocks = 1024;
   if (blocks > (1 << 30)) blocks = 1 << 30;
   const int grid = (int)blocks;
   const int mode = p.mode;
