@@ -110,6 +110,31 @@ def test_quant_dual_c3_small(vq, gran):
     assert_same(scales.cpu().numpy(), rs, "scales")
 
 
+@pytest.mark.parametrize("k,m,n_out,dt,gran", [
+    (1088, 5000, 100, "bf16", "token"),   # one wave per row, a partial pass; the grid walks several rows per wave
+    (4160, 37, 128, "fp16", "token"),     # two waves per row
+    (9216, 21, 77, "bf16", "tensor"),     # four waves per row
+    (17408, 9, 128, "bf16", "token"),     # eight waves per row, a partial last pass
+    (32768, 5, 50, "fp16", "token"),      # eight waves of four passes
+])
+def test_quant_dual_row_lengths(vq, k, m, n_out, dt, gran):
+    """Dual scale in every row-length regime: outlier channels in every pass (adjacent
+    channels inside one 8-element piece, the row's first and last channels), each wave
+    owning the outliers of its own passes."""
+    rng = np.random.default_rng(k + n_out)
+    inner = rng.choice(np.arange(3, k - 2), n_out - 5, replace=False)
+    idx = np.sort(np.concatenate([[0, 1, 2, k - 2, k - 1], inner])).astype(np.int32)
+    assert len(idx) == n_out and len(np.unique(idx)) == n_out
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, idx] *= 20.0
+    t = gen.to_storage(x, dt)
+    codes, scales = vq.vq_quant_act(t.to(DEV), 8, gran, idx=torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(t), dt, 8, gran, 0, idx)
+    assert_same(codes.cpu().numpy(), rc, f"codes k={k}")
+    assert_same(scales.cpu().numpy(), rs, f"scales k={k}")
+
+
 @pytest.mark.parametrize("bits,gran", [(6, "token"), (8, "token"), (4, "tensor")])
 def test_quant_hadamard_c4_small(vq, bits, gran):
     x = gen.make_x(4, m=40)
