@@ -65,6 +65,23 @@ def test_mx_quant_bit_exact(vq, fmt, dtype):
     assert np.array_equal(got[:, :m], step_major(rs, m)[:, :m])
 
 
+@pytest.mark.parametrize("fmt", ["fp4", "fp6"])
+@pytest.mark.parametrize("m,k,pad", [(1, 64, 0), (3, 64, 64), (37, 192, 32), (1000, 1920, 128), (9, 12288, 0)])
+def test_mx_quant_shapes_and_strides(vq, fmt, m, k, pad):
+    """Block numbering over the whole matrix: rows whose block count is not a multiple of
+    the 64 blocks a wave takes (waves spanning row ends), a single block pair per row, and
+    rows read through a pitch wider than K (a column slice of a wider tensor)."""
+    full = rand_x(m, k + pad, torch.bfloat16, m + k + pad)
+    x = full.to(DEV)[:, :k]
+    assert x.stride(0) == k + pad
+    codes, scales = vq.vq_mx_quant(x, fmt)
+    torch.cuda.synchronize()
+    rc, rs = mx.quantize(numerics.to_f32(npb(full)[:, :k], "bf16"), fmt)
+    assert np.array_equal(codes.cpu().numpy(), mx.pack(rc, fmt))
+    got = device_scales(scales, m, k)
+    assert np.array_equal(got[:, :m], step_major(rs, m)[:, :m])
+
+
 def test_mx_quant_edge_values(vq):
     k = 128
     x = np.zeros((4, k), np.float32)
