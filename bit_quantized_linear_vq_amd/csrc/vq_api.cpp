@@ -327,7 +327,6 @@ vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64
   if (!mx_fmt_ok(fmt)) return VQ_ERR_UNSUPPORTED;
   if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
   if (!aligned16(x) || ldx % 8 || reinterpret_cast<uintptr_t>(codes) % 8) return VQ_ERR_SHAPE;
-  if (rows * (k / 32) >= kMaxDim) return VQ_ERR_SHAPE;  // blocks are numbered in 31 bits
   return hip_status(vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream));
 }
 

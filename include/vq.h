@@ -255,8 +255,7 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
  * vq_mx_code_bytes / vq_mx_scale_bytes give the buffer sizes (0 for invalid sizes).
  *
  * vq_mx_quant: x device, dt in {F16, BF16}, [rows x k], stride ldx; 16-byte aligned,
- *   ldx % 8 == 0, k % 64 == 0, codes 8-byte aligned, rows * k / 32 < 2^31 (blocks).
- *   Finite inputs.  The element codes come from the matrix unit's MX conversion
+ *   ldx % 8 == 0, k % 64 == 0, codes 8-byte aligned.  Finite inputs.  The element codes come from the matrix unit's MX conversion
  *   instructions (round to nearest even, saturation), which match the rule above.
  *   Errors: INVALID_ARG, SHAPE, UNSUPPORTED (fmt).
  * vq_mx_gemm: y[i,j] = sum_k dec(a[i,k]) * dec(b[j,k]) on the matrix cores (block scales
