@@ -153,6 +153,42 @@ __device__ __forceinline__ float fwht128(float v[16], int g) {
   return had_sigma(g);
 }
 
+// The same transform with the block held as two 8-element pieces per lane, 64 elements
+// apart: lane slot l holds elements 8g .. 8g+7 (v[0..7]) and 64 + 8g .. 64 + 8g+7
+// (v[8..15]), g = perm8(l).  Distances 1, 2, 4 are inside a piece, 8, 16, 32 are the
+// three DPP moves above (lane xor 1, xor 2, 7 - lane), and 64 pairs the two pieces of a
+// lane; the stages still run in ascending h, and sigma is the same.  A wave's loads of
+// one piece then cover whole 128-byte lines (8 lanes x 16 bytes per block half).
+__device__ __forceinline__ float fwht128_pieces(float v[16], int g) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  const float c0 = (g & 1) ? -1.0f : 1.0f;
+  const float c1 = (g & 2) ? -1.0f : 1.0f;
+  const float c2 = (g & 4) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0xB1>(v[i]), c0, v[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x4E>(v[i]), c1, v[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x141>(v[i]), c2, v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float a = v[i], b = v[i + 8];
+    v[i] = a + b;
+    v[i + 8] = a - b;
+  }
+  return had_sigma(g);
+}
+
 // ---------------------------------------------------------------------------
 // Round-half-even quantization through the float32 magic constant 1.5 * 2^23:
 // for |t| <= 2^22, fl(t + 12582912) = 12582912 + rne(t) exactly (the sum is

@@ -12,8 +12,9 @@
 // of the 64 lanes of a wave owns 16 elements as two 8-element pieces (one 16-byte load
 // and one 8-byte store of codes each).  Without rotation lane l owns elements 8l..8l+7
 // of each 512-element half of the pass, so every load and store instruction of a wave
-// covers one contiguous span; the rotation needs 16 contiguous elements per lane (see
-// fwht128).  A row is owned by W waves (W = 1, 2, 4 or 8) so that every lane keeps at
+// covers one contiguous span; with the rotation the 8 lanes of a 128-element block own
+// 8-element pieces of its two halves (see fwht128_pieces), so every load covers whole
+// 128-byte lines.  A row is owned by W waves (W = 1, 2, 4 or 8) so that every lane keeps at
 // most 4 passes (64 floats) in registers: the row is read from HBM once, reduced to its
 // absolute maximum, and quantized from registers.  All loads of a row are issued before
 // any of them is used (addresses past the row end are clamped into the row and their
@@ -80,13 +81,12 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   const int rpb = nwaves / a.W;  // rows per block
   const int rib = wave / a.W;
   const int wr = wave - rib * a.W;
-  const int slot = HAD ? ((lane & ~7) | perm8(lane & 7)) : lane;
   const float sigma = HAD ? had_sigma(perm8(lane & 7)) : 1.0f;
   const float qf = qmax_f(a);
   // First element of piece h (0, 1) of pass j in this lane.
   auto piece = [&](int j, int h) {
     const int p0 = (wr + a.W * j) * 1024;
-    return HAD ? p0 + 16 * slot + 8 * h : p0 + 512 * h + 8 * lane;
+    return HAD ? p0 + 128 * (lane >> 3) + 64 * h + 8 * perm8(lane & 7) : p0 + 512 * h + 8 * lane;
   };
 
   // Outlier channels gathered by this lane (the same for every row).
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
         }
       }
       if constexpr (HAD) {
-        fwht128(v[j], perm8(lane & 7));
+        fwht128_pieces(v[j], perm8(lane & 7));
       }
       if constexpr (DUAL) {
 #pragma unroll
