@@ -97,20 +97,24 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // ---------------------------------------------------------------------------
 // 128-point Sylvester Hadamard butterflies held in registers.
 //
-// A 128-element block is spread over 8 consecutive lanes, 16 contiguous elements
-// per lane.  Lane slot l (0..7) holds element group g = perm8(l), i.e. elements
-// 16g .. 16g+15, with perm8 = (0,1,2,3,7,6,5,4).  With that assignment the three
-// cross-lane butterfly distances map onto single DPP moves:
-//   h = 16 (group bit 0): lane xor 1      -> quad_perm [1,0,3,2]
-//   h = 32 (group bit 1): lane xor 2      -> quad_perm [2,3,0,1]
-//   h = 64 (group bit 2): lane 7 - lane   -> row_half_mirror
-// Distances 1, 2, 4, 8 are inside a lane.  The stages run in ascending h.
+// A 128-element block is spread over 8 consecutive lanes as two 8-element pieces per
+// lane, 64 elements apart: lane slot l (0..7) holds elements 8g .. 8g+7 (v[0..7]) and
+// 64 + 8g .. 64 + 8g+7 (v[8..15]), with g = perm8(l) and perm8 = (0,1,2,3,7,6,5,4).  A
+// wave's load of one piece then covers whole 128-byte lines (8 lanes x 16 bytes per
+// block half).  Butterfly distances 1, 2, 4 are inside a piece, 64 pairs the two pieces
+// of a lane, and with the slot assignment above the three cross-lane distances map onto
+// single DPP moves:
+//   h = 8  (group bit 0): lane xor 1      -> quad_perm [1,0,3,2]
+//   h = 16 (group bit 1): lane xor 2      -> quad_perm [2,3,0,1]
+//   h = 32 (group bit 2): lane 7 - lane   -> row_half_mirror
+// The stages run in ascending h, as the transform's definition does them.
 //
-// Cross-lane stages keep a per-lane sign: the lane holding the lower index of a
-// pair computes fl(mine + partner); the upper lane computes fl(mine - partner),
-// which is exactly -(z_lo - z_hi).  Partners always carry the same sign, so the
-// stored value is sigma * z with sigma = (-1)^popcount(g); negation is exact in
-// IEEE arithmetic, so sigma is folded into the consumer's multiplier.
+// Cross-lane stages keep a per-lane sign: the lane holding the lower index of a pair
+// computes fl(mine + partner); the upper lane computes fl(mine - partner), which is
+// exactly -(z_lo - z_hi).  Partners always carry the same sign, so the stored value is
+// sigma * z with sigma = (-1)^popcount(g); the last stage pairs two values of one lane,
+// which carry the same sign; negation is exact in IEEE arithmetic, so sigma is folded
+// into the consumer's multiplier.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int perm8(int l) { return l < 4 ? l : 11 - l; }
 
@@ -121,45 +125,10 @@ __device__ __forceinline__ float dpp_f(float v) {
   return bits_f((unsigned)__builtin_amdgcn_update_dpp(0, (int)f_bits(v), CTRL, 0xF, 0xF, false));
 }
 
-// In-lane stages h = 1, 2, 4, 8 over 16 contiguous elements.
-__device__ __forceinline__ void fwht16_inlane(float v[16]) {
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((i & h) == 0) {
-        float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-}
-
 // All seven stages; g = this lane's element group (0..7).  Returns sigma.
 // Cross-lane stage: v = fl(partner * c + mine) with c = +1 on the lower lane of the
 // pair and -1 on the upper lane; partner * c is exact, so the fma rounds once.
 __device__ __forceinline__ float fwht128(float v[16], int g) {
-  fwht16_inlane(v);
-  const float c0 = (g & 1) ? -1.0f : 1.0f;
-  const float c1 = (g & 2) ? -1.0f : 1.0f;
-  const float c2 = (g & 4) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0xB1>(v[i]), c0, v[i]);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x4E>(v[i]), c1, v[i]);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x141>(v[i]), c2, v[i]);
-  return had_sigma(g);
-}
-
-// The same transform with the block held as two 8-element pieces per lane, 64 elements
-// apart: lane slot l holds elements 8g .. 8g+7 (v[0..7]) and 64 + 8g .. 64 + 8g+7
-// (v[8..15]), g = perm8(l).  Distances 1, 2, 4 are inside a piece, 8, 16, 32 are the
-// three DPP moves above (lane xor 1, xor 2, 7 - lane), and 64 pairs the two pieces of a
-// lane; the stages still run in ascending h, and sigma is the same.  A wave's loads of
-// one piece then cover whole 128-byte lines (8 lanes x 16 bytes per block half).
-__device__ __forceinline__ float fwht128_pieces(float v[16], int g) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll

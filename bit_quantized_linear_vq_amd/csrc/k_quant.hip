@@ -13,7 +13,7 @@
 // and one 8-byte store of codes each).  Without rotation lane l owns elements 8l..8l+7
 // of each 512-element half of the pass, so every load and store instruction of a wave
 // covers one contiguous span; with the rotation the 8 lanes of a 128-element block own
-// 8-element pieces of its two halves (see fwht128_pieces), so every load covers whole
+// 8-element pieces of its two halves (see fwht128), so every load covers whole
 // 128-byte lines.  A row is owned by W waves (W = 1, 2, 4 or 8) so that every lane keeps at
 // most 4 passes (64 floats) in registers: the row is read from HBM once, reduced to its
 // absolute maximum, and quantized from registers.  All loads of a row are issued before
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
         }
       }
       if constexpr (HAD) {
-        fwht128_pieces(v[j], perm8(lane & 7));
+        fwht128(v[j], perm8(lane & 7));
       }
       if constexpr (DUAL) {
 #pragma unroll
