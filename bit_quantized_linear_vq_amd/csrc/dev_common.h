@@ -41,34 +41,6 @@ __device__ __forceinline__ void decode2(unsigned u, float& lo, float& hi) {
   }
 }
 
-// 16 consecutive elements starting at p (16-byte aligned) as float.
-template <int DT>
-__device__ __forceinline__ void load16(const void* p, float v[16]) {
-  if constexpr (DT == DT_F32) {
-    const u4v* q = reinterpret_cast<const u4v*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u4v w = __builtin_nontemporal_load(q + i);
-      v[4 * i + 0] = bits_f(w.x);
-      v[4 * i + 1] = bits_f(w.y);
-      v[4 * i + 2] = bits_f(w.z);
-      v[4 * i + 3] = bits_f(w.w);
-    }
-  } else {
-    const u4v* q = reinterpret_cast<const u4v*>(p);
-    u4v w0 = __builtin_nontemporal_load(q);
-    u4v w1 = __builtin_nontemporal_load(q + 1);
-    decode2<DT>(w0.x, v[0], v[1]);
-    decode2<DT>(w0.y, v[2], v[3]);
-    decode2<DT>(w0.z, v[4], v[5]);
-    decode2<DT>(w0.w, v[6], v[7]);
-    decode2<DT>(w1.x, v[8], v[9]);
-    decode2<DT>(w1.y, v[10], v[11]);
-    decode2<DT>(w1.z, v[12], v[13]);
-    decode2<DT>(w1.w, v[14], v[15]);
-  }
-}
-
 // One element of a storage dtype as float.
 template <int DT>
 __device__ __forceinline__ float load1(const void* p, int64_t i) {

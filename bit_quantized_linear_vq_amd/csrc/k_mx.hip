@@ -36,7 +36,6 @@ template <int FMT>
 struct MxFmt {
   static constexpr int M = FMT == MX_FP4 ? 1 : 3;  // mantissa bits (both have 2 exponent bits, bias 1)
   static constexpr int W = 3 + M;                  // bits per element
-  static constexpr float VMAX = FMT == MX_FP4 ? 6.0f : 7.5f;
   static constexpr int STEP_BYTES = 64 * W / 8;    // bytes of one row per 64-deep step
 };
 
