@@ -53,11 +53,26 @@ __device__ __forceinline__ float load1(const void* p, int64_t i) {
   }
 }
 
-// Wave-wide maximum of non-negative floats (exact: max is order independent).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return bits_f((unsigned)__builtin_amdgcn_update_dpp(0, (int)f_bits(v), CTRL, 0xF, 0xF, false));
+}
+
+// Wave-wide maximum of non-negative floats (exact: max is order independent).  Register
+// moves instead of LDS permutes: two quad swaps, the half-row and row mirrors make every
+// lane hold its 16-lane row's maximum, and the four rows are combined from lanes 0, 16,
+// 32 and 48 in scalar registers.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  const int b = (int)f_bits(v);
+  const float r0 = bits_f((unsigned)__builtin_amdgcn_readlane(b, 0));
+  const float r1 = bits_f((unsigned)__builtin_amdgcn_readlane(b, 16));
+  const float r2 = bits_f((unsigned)__builtin_amdgcn_readlane(b, 32));
+  const float r3 = bits_f((unsigned)__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -91,11 +106,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 __device__ __forceinline__ int perm8(int l) { return l < 4 ? l : 11 - l; }
 
 __device__ __forceinline__ float had_sigma(int g) { return (__builtin_popcount(g) & 1) ? -1.0f : 1.0f; }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return bits_f((unsigned)__builtin_amdgcn_update_dpp(0, (int)f_bits(v), CTRL, 0xF, 0xF, false));
-}
 
 // All seven stages; g = this lane's element group (0..7).  Returns sigma.
 // Cross-lane stage: v = fl(partner * c + mine) with c = +1 on the lower lane of the
