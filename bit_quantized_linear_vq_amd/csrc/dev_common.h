@@ -110,6 +110,11 @@ __device__ __forceinline__ float had_sigma(int g) { return (__builtin_popcount(g
 // All seven stages; g = this lane's element group (0..7).  Returns sigma.
 // Cross-lane stage: v = fl(partner * c + mine) with c = +1 on the lower lane of the
 // pair and -1 on the upper lane; partner * c is exact, so the fma rounds once.
+// FUSED_DPP: each cross-lane stage as one v_fmac_f32 reading the partner through DPP
+// (inline asm: the compiler keeps the DPP move and the fma apart), for the quantizer, whose
+// fused rotation is VALU-bound; the memory-bound standalone rotation keeps the compiler's
+// two-instruction form, which measured faster there.
+template <bool FUSED_DPP>
 __device__ __forceinline__ float fwht128(float v[16], int g) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
@@ -125,12 +130,35 @@ __device__ __forceinline__ float fwht128(float v[16], int g) {
   const float c0 = (g & 1) ? -1.0f : 1.0f;
   const float c1 = (g & 2) ? -1.0f : 1.0f;
   const float c2 = (g & 4) ? -1.0f : 1.0f;
+  if constexpr (FUSED_DPP) {
+    // v = fl(partner * c + v) in one instruction, exact product.  The s_nop covers the two
+    // wait states a DPP read needs after a VALU write of the same register.
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0xB1>(v[i]), c0, v[i]);
+    for (int i = 0; i < 16; ++i) {
+      const float src = v[i];
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                   : "+v"(v[i]) : "v"(src), "v"(c0));
+    }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x4E>(v[i]), c1, v[i]);
+    for (int i = 0; i < 16; ++i) {
+      const float src = v[i];
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                   : "+v"(v[i]) : "v"(src), "v"(c1));
+    }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x141>(v[i]), c2, v[i]);
+    for (int i = 0; i < 16; ++i) {
+      const float src = v[i];
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_half_mirror row_mask:0xf bank_mask:0xf"
+                   : "+v"(v[i]) : "v"(src), "v"(c2));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0xB1>(v[i]), c0, v[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x4E>(v[i]), c1, v[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(dpp_f<0x141>(v[i]), c2, v[i]);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float a = v[i], b = v[i + 8];

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_hadamard(const void* __restrict__ x, in
       decode2<IN_DT>(raw[h][0].w, v[8 * h + 6], v[8 * h + 7]);
     }
   }
-  const float sigma = fwht128(v, g);
+  const float sigma = fwht128<false>(v, g);
   const float c = sigma * cnorm;  // exact: sigma = +-1
 #pragma unroll
   for (int t = 0; t < 16; ++t) v[t] = v[t] * c;

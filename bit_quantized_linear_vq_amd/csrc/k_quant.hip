@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
         }
       }
       if constexpr (HAD) {
-        fwht128(v[j], perm8(lane & 7));
+        fwht128<true>(v[j], perm8(lane & 7));
       }
       if constexpr (DUAL) {
 #pragma unroll
