@@ -131,8 +131,11 @@ __device__ __forceinline__ float fwht128(float v[16], int g) {
   const float c1 = (g & 2) ? -1.0f : 1.0f;
   const float c2 = (g & 4) ? -1.0f : 1.0f;
   if constexpr (FUSED_DPP) {
-    // v = fl(partner * c + v) in one instruction, exact product.  The s_nop covers the two
-    // wait states a DPP read needs after a VALU write of the same register.
+    // v = fl(partner * c + v) in one instruction, exact product.  A DPP read needs two wait
+    // states after a VALU write of the same register: the first stage's inputs come from
+    // compiler-scheduled code, so each of its instructions starts with an s_nop; in the
+    // later stages every input was written by the previous stage's (ordered, volatile)
+    // instruction for the same element, 15 instructions earlier.
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float src = v[i];
@@ -142,13 +145,13 @@ __device__ __forceinline__ float fwht128(float v[16], int g) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float src = v[i];
-      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      asm volatile("v_fmac_f32_dpp %0, %1, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
                    : "+v"(v[i]) : "v"(src), "v"(c1));
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float src = v[i];
-      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_half_mirror row_mask:0xf bank_mask:0xf"
+      asm volatile("v_fmac_f32_dpp %0, %1, %2 row_half_mirror row_mask:0xf bank_mask:0xf"
                    : "+v"(v[i]) : "v"(src), "v"(c2));
     }
   } else {
