@@ -168,16 +168,14 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
 
     float v[NP][16];
     float lmax = 0.0f;
+    // Pieces past the row end hold clamped reads: a piece (and, with the rotation, its whole
+    // 128-element block) lies entirely inside or entirely past the row end, nothing past
+    // it is stored, so only the row maximum has to leave them out.  (A row past the last
+    // one is computed from row 0 and not stored at all.)
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        decode8<DT>(raw[j][h], &v[j][8 * h]);
-        if (!(row_ok && piece(j, h) < a.k)) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) v[j][8 * h + t] = 0.0f;
-        }
-      }
+      for (int h = 0; h < 2; ++h) decode8<DT>(raw[j][h], &v[j][8 * h]);
       if constexpr (HAD) {
         fwht128<true>(v[j], perm8(lane & 7));
       }
@@ -189,7 +187,12 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
             if ((obits[j][h] >> t) & 1u) v[j][8 * h + t] = 0.0f;
       }
 #pragma unroll
-      for (int t = 0; t < 16; ++t) lmax = fmaxf(lmax, fabsf(v[j][t]));
+      for (int h = 0; h < 2; ++h) {
+        float pm = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pm = fmaxf(pm, fabsf(v[j][8 * h + t]));
+        lmax = fmaxf(lmax, piece(j, h) < a.k ? pm : 0.0f);
+      }
     }
 
     float ov[2] = {0.0f, 0.0f};
