@@ -87,16 +87,24 @@ template <typename V, int MB, int NB>
 __device__ __forceinline__ void split_accumulate(const uint64_t* part, int nt, int tid, V (&acc)[MB][NB]) {
   typedef decltype(acc[0][0][0] + 0) E;  // int or float
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
+    // All words of a row of blocks are requested before any is added: these loads bypass
+    // the L2, and issued one at a time each would wait out the full memory latency.
+    uint64_t v[NB][8];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[nb][i] = __hip_atomic_load(part + (int64_t)((mb * NB + nb) * 8 + i) * nt + tid, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint64_t v = __hip_atomic_load(part + (int64_t)((mb * NB + nb) * 8 + i) * nt + tid, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        acc[mb][nb][2 * i] += __builtin_bit_cast(E, (uint32_t)v);
-        acc[mb][nb][2 * i + 1] += __builtin_bit_cast(E, (uint32_t)(v >> 32));
+        acc[mb][nb][2 * i] += __builtin_bit_cast(E, (uint32_t)v[nb][i]);
+        acc[mb][nb][2 * i + 1] += __builtin_bit_cast(E, (uint32_t)(v[nb][i] >> 32));
       }
+  }
 }
 
 // After this workgroup's partial is published: bump the tile's arrival count once the

@@ -524,10 +524,11 @@ namespace vq_internal {
 using namespace vqk;
 
 // Remainder split of a tile grid: K ranges per remaining tile (1: none).  A range's
-// partial (256 KB of int32) is stored and reloaded through one CU, which costs about
-// as much as 15-20 stages of its MFMA work: measured at the workload shapes, two ranges
-// pay off once K has at least 96 stages of 64 codes (17776 x 12288 x 3072: 5-6%
-// faster), while at 30 or 48 stages any split is slower or even.
+// partial (256 KB of int32) is stored and reloaded through one CU.  Measured at the
+// workload shapes, two ranges pay off once K has at least 96 stages of 64 codes
+// (17776 x 12288 x 3072: 5-6% faster), while at 30 or 48 stages two or three ranges are
+// slower or even: the last round's whole tiles, run on a few CUs, already go faster
+// than tiles of a full round.
 static int split_of(int tiles, int grid, int nk) {
   const int rem = tiles % grid;
   if (rem == 0 || nk < 96 || grid > QGEMM_WS_COUNTERS / 4) return 1;
