@@ -71,9 +71,16 @@ def parse():
     return p.parse_args()
 
 
+# The headers each kernel source compiles in: a change to any of them changes the kernel.
+KERNEL_DEPS = {"k_qgemm.hip": ("gemm_common.h", "dev_common.h"), "k_quant.hip": ("dev_common.h",)}
+
+
 def kernel_hash(name):
-    with open(os.path.join(ROOT, "bit_quantized_linear_vq_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for part in (name,) + KERNEL_DEPS.get(name, ()):
+        with open(os.path.join(ROOT, "bit_quantized_linear_vq_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload):
@@ -239,15 +246,13 @@ def stream_reference(L, torch, stream, reps=20):
     buf = torch.empty((L.M, L.K), dtype=torch.bool, device=L.x[0].device)
     for i in range(3):
         torch.ne(L.x[i % len(L.x)], 0, out=buf)
-    ev = []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)  # back-to-back launches, timed as the quantizer's are
     for i in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
         torch.ne(L.x[i % len(L.x)], 0, out=buf)
-        b.record(stream)
-        ev.append((a, b))
+    b.record(stream)
     torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+    us = a.elapsed_time(b) / reps * 1e3
     nbytes = 3 * L.M * L.K
     return {"op": "torch.ne(x, 0) on the same inputs: 2 B read, 1 B written per element",
             "avg_us": round(us, 2), "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s"}
@@ -431,16 +436,10 @@ def main():
     L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    def step(i):
         for l in range(L.layers):
-            if ev is not None:
-                ev[0].record(stream)
             L.quant(i, l)
-            if ev is not None:
-                ev[1].record(stream)
             L.gemm(l)
-            if ev is not None:
-                ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -481,23 +480,24 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    # Per-kernel durations: HIP events around every launch on the launch stream.  One
-    # untimed step is queued first so that the GPU is busy while the host enqueues the
-    # bracketed launches (otherwise the first interval holds the host's launch latency).
-    step(0)
-    evs = []
-    for i in range(args.steps):
-        for l in range(L.layers):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record(stream)
-            L.quant(i, l)
-            e[1].record(stream)
-            L.gemm(l)
-            e[2].record(stream)
-            evs.append(e)
-    torch.cuda.synchronize()
-    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
-    g_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    # Per-kernel durations: each kernel's `steps * layers` launches run back to back between
+    # two HIP events on the launch stream, and the interval is divided by the launch count.
+    # Events around every single launch would add their own few microseconds to each
+    # interval, a large share of an 18-microsecond quantization.  One untimed step is queued
+    # first so that the GPU is busy while the host enqueues the bracketed launches.
+    def batch_ms(launch):
+        step(0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            for l in range(L.layers):
+                launch(i, l)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (args.steps * L.layers)
+
+    q_ms = batch_ms(lambda i, l: L.quant(i, l))
+    g_ms = batch_ms(lambda i, l: L.gemm(l))
 
     gemm_tops = L.gemm_ops() / (g_ms * 1e-3) / 1e12
     quant_gbs = L.quant_bytes() / (q_ms * 1e-3) / 1e9
