@@ -411,7 +411,8 @@ hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st) {
   if (p.maxonly && blocks > 2048) blocks = 2048;
   // With the outlier partition every wave first waits for the outlier indices (its
   // gathers need them); a bounded grid lets each wave pay that once over several rows.
-  if (p.n_out > 0 && blocks > 1024) blocks = 1024;
+  // At 17776 x 3072: 512 blocks 31.2 us, 1024 30.6, 2048 29.9, no bound 30.2.
+  if (p.n_out > 0 && blocks > 2048) blocks = 2048;
   if (blocks > (1 << 30)) blocks = 1 << 30;
   const int grid = (int)blocks;
   const int mode = p.mode;
