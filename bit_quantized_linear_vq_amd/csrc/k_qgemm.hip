@@ -117,7 +117,8 @@ __device__ __forceinline__ v4i unpack_int4x16(u2v w) {
 
 template <int BBITS, int OUT_DT, bool DUAL, int H>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm(GArgs g) {
-  static_assert(!DUAL || H == 2, "the outlier partition is staged in 64-code stages");
+  static_assert(!DUAL || H == 2 || (H == 4 && BBITS == 4),
+                "the outlier partition is staged in 64-code stages, or in one 128-code stage");
   using C = GCfg<BBITS, H>;
   constexpr int BK = C::BK;
   constexpr int P = DUAL ? 2 : 1;
@@ -184,6 +185,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int kb = BBITS == 8 ? k : k / 2;
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) dma16(gb[i] + kb, base + lb_off[i]);
+  };
+  // The outlier partition [k0, kp) of 64 or 128 codes as one 128-code stage: columns past
+  // the partition wrap to its start (mask), so every load stays inside the row's
+  // partition; the wrapped chunks are never read.
+  auto issue_part = [&](int amask, int bmask) {
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) dma16(ga[i] - ca[i] + (ca[i] & amask) + g.k0, lds + la_off[i]);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) dma16(gb[i] - cb[i] + (cb[i] & bmask) + g.k0 / 2, lds + lb_off[i]);
   };
   auto issue_prologue = [&]() {
 #pragma unroll
@@ -392,9 +402,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     int steps1 = 0;
     if constexpr (DUAL) {
       // Outlier partition [k0, kp): at most two 64-code steps, staged in stages 0-1.
-      steps1 = (g.kp - g.k0) / BK;
-      issue(g.k0, 0);
-      if (steps1 > 1) issue(g.k0 + BK, 1);  // (H == 2 here: BK = 64)
+      if constexpr (H == 2) {
+        steps1 = (g.kp - g.k0) / BK;
+        issue(g.k0, 0);
+        if (steps1 > 1) issue(g.k0 + BK, 1);
+      } else {
+        steps1 = (g.kp - g.k0) / 32;  // k-halves of the partition: 2 or 4
+        issue_part(g.kp - g.k0 - 1, (g.kp - g.k0) / 2 - 1);
+      }
       wait_vmcnt<0>();
       barrier_nofence();
     } else {
@@ -425,13 +440,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int nb = 0; nb < NBLK; ++nb) {
         v16i t1 = v16i{};
         if constexpr (DUAL) {
+          if constexpr (H == 2) {
 #pragma unroll
-          for (int s1 = 0; s1 < 2; ++s1) {
-            if (s1 < steps1) {
+            for (int s1 = 0; s1 < 2; ++s1) {
+              if (s1 < steps1) {
 #pragma unroll
-              for (int h = 0; h < 2; ++h)
-                t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(s1, h, nb), afrag(s1, h, mb), t1, 0, 0, 0);
+                for (int h = 0; h < 2; ++h)
+                  t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(s1, h, nb), afrag(s1, h, mb), t1, 0, 0, 0);
+              }
             }
+          } else {
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+              if (h < steps1)
+                t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(0, h, nb), afrag(0, h, mb), t1, 0, 0, 0);
           }
         }
         u2v hw[4];  // 16-bit outputs of group q: columns 8q + 4 * (lane >> 5) + 0..3
@@ -513,7 +535,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 template <int BBITS, int OUT_DT>
 static hipError_t launch_dual(const GArgs& a, bool dual, int grid, hipStream_t st) {
-  if (dual)
+  const int part = a.kp - a.k0;
+  if (dual && BBITS == 4 && a.k0 % 128 == 0 && (part == 64 || part == 128))  // 128-code stages
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, BBITS == 4 ? 4 : 2>), dim3(grid), dim3(NT), 0, st, a);
+  else if (dual)
     hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, 2>), dim3(grid), dim3(NT), 0, st, a);
   else if (BBITS == 4 && a.k0 % 128 == 0)  // 4-bit weights: 128-code stages
     hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, BBITS == 4 ? 4 : 2>), dim3(grid), dim3(NT), 0, st, a);

@@ -286,6 +286,20 @@ def test_gemm_dual_two_outlier_steps(vq):
     assert_outputs(y, r["y_store"], "bf16", "output")
 
 
+def test_gemm_dual_w4_partition_of_128(vq):
+    """4-bit weights with an outlier partition of 128 codes: with K a multiple of 128 the
+    main loop takes 128-code stages and the partition is staged as one whole stage."""
+    x = gen.make_x(3, m=70)
+    w = gen.make_w(3, n=96)
+    idx = np.sort(np.random.default_rng(2).choice(3072, 100, replace=False)).astype(np.int32)
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 8, 4, idx=idx)
+    r = oracle_layer(x, w, 8, 4, idx=idx)
+    assert ac.shape[1] == 3072 + 128
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "partition 0")
+    assert_same(acc[1].cpu().numpy(), r["accs"][1], "partition 1")
+    assert_outputs(y, r["y_store"], "bf16", "output")
+
+
 def test_gemm_hadamard_w4a6_c4_small(vq):
     x = gen.make_x(4, m=40)
     w = gen.make_w(4, n=288)
