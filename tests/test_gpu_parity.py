@@ -300,6 +300,20 @@ def test_gemm_dual_w4_partition_of_128(vq):
     assert_outputs(y, r["y_store"], "bf16", "output")
 
 
+def test_gemm_dual_w4_k_not_multiple_of_128(vq):
+    """4-bit weights, dual scale, K = 1984 (31 x 64): the 64-code-stage kernel, with the
+    outlier partition staged as one 64-code stage."""
+    x = gen.make_x(3, m=70)[:, :1984].contiguous()
+    w = gen.make_w(3, n=96)[:, :1984].contiguous()
+    idx = np.sort(np.random.default_rng(3).choice(1984, 20, replace=False)).astype(np.int32)
+    ac, as_, wc, ws, y, acc = run_layer(vq, x, w, 8, 4, idx=idx)
+    r = oracle_layer(x, w, 8, 4, idx=idx)
+    assert ac.shape[1] == 1984 + 64
+    assert_same(acc[0].cpu().numpy(), r["accs"][0], "partition 0")
+    assert_same(acc[1].cpu().numpy(), r["accs"][1], "partition 1")
+    assert_outputs(y, r["y_store"], "bf16", "output")
+
+
 def test_gemm_hadamard_w4a6_c4_small(vq):
     x = gen.make_x(4, m=40)
     w = gen.make_w(4, n=288)
