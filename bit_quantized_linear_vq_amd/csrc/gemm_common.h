@@ -37,6 +37,29 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* ldst) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(gsrc) : "memory");
 }
 
+// 4 bytes per lane from global memory straight into LDS at ldst + 4 * lane (the same
+// form as dma16, one dword per lane): used for the tile's scales.
+__device__ __forceinline__ void dma4(const void* gsrc, void* ldst) {
+  const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_ptr_t)ldst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(la), "v"(gsrc) : "memory");
+}
+
+// Two float32 values rounded (to nearest even) to a pair of 16-bit values in one dword,
+// the first in the low half: one v_cvt_pk_{bf16,f16}_f32.  The inputs are fenced so that
+// each is a rounded float32 product before it is narrowed.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <int OUT_DT>
+__device__ __forceinline__ unsigned cvt_pair(float a, float b) {
+  const f32x2_t v = {f32_fence(a), f32_fence(b)};
+  if constexpr (OUT_DT == DT_BF16) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
+  } else {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2_t));
+  }
+}
+
 // Four consecutive float32 outputs of one row (16 B when aligned and whole).
 __device__ __forceinline__ void store4_f32(void* y, int64_t off, const float v[4], int cnt, bool vec) {
   float* p = reinterpret_cast<float*>(y) + off;

@@ -200,25 +200,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int s = 0; s < C::NST - 1; ++s)
       if (s < nks) issue((kb0 + s) * BK, s);
   };
-  // Scales of a tile's rows and columns: loaded into registers early, written to LDS late.
+  // Scales of a tile's rows and columns.  With 64-code stages they go straight to LDS by
+  // direct loads (64 lanes x 4 bytes per instruction, P per wave), issued before the
+  // tile's first stage so that the waits for that stage cover them: loaded into registers
+  // instead, they are the only loads the compiler tracks, and it drains every direct load
+  // in flight (vmcnt(0)) before their first use.  The 128-code-stage kernels, whose scalar
+  // registers are spoken for by their wider ring, load them into registers early and write
+  // them to LDS late.
+  constexpr bool SC_DMA = H == 2;
   float sc_a[P], sc_b[P];
-  const int srow = tid & (BM - 1);  // 512 threads: each loads one row scale or one column scale
-  auto load_scales = [&]() {
+  const int srow = tid & (BM - 1);  // register path: each thread loads one row or column scale
+  auto load_scales = [&](int buf) {
+    if constexpr (SC_DMA) {
+      const int r = 64 * (wave & 3) + lane;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (tid < BM)
-        sc_a[p] = g.sa_tok ? g.sa[(int64_t)min(m0 + srow, g.m - 1) * P + p] : g.sa[p];
-      else
-        sc_b[p] = g.sb[(int64_t)min(n0 + srow, g.n - 1) * P + p];
+      for (int p = 0; p < P; ++p) {
+        if (wave < 4) {
+          const float* src = g.sa_tok ? g.sa + (int64_t)min(m0 + r, g.m - 1) * P + p : g.sa + p;
+          dma4(src, &s_sa[buf][p][64 * wave]);
+        } else {
+          dma4(g.sb + (int64_t)min(n0 + r, g.n - 1) * P + p, &s_sb[buf][p][64 * (wave - 4)]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if (tid < BM)
+          sc_a[p] = g.sa_tok ? g.sa[(int64_t)min(m0 + srow, g.m - 1) * P + p] : g.sa[p];
+        else
+          sc_b[p] = g.sb[(int64_t)min(n0 + srow, g.n - 1) * P + p];
+      }
     }
   };
   auto store_scales = [&](int buf) {
+    if constexpr (!SC_DMA) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (tid < BM)
-        s_sa[buf][p][srow] = sc_a[p];
-      else
-        s_sb[buf][p][srow] = sc_b[p];
+      for (int p = 0; p < P; ++p) {
+        if (tid < BM)
+          s_sa[buf][p][srow] = sc_a[p];
+        else
+          s_sb[buf][p][srow] = sc_b[p];
+      }
     }
   };
 
@@ -298,9 +320,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   int vt = blockIdx.x;
   if (vt >= g.items) return;
   set_tile(vt);
-  issue_prologue();
-  load_scales();
-  store_scales(0);
+  if constexpr (SC_DMA) {
+    load_scales(0);  // ahead of the first stage, whose waits then cover it
+    issue_prologue();
+  } else {
+    issue_prologue();
+    load_scales(0);
+    store_scales(0);
+  }
   int buf = 0;
   for (;;) {
 #pragma unroll
@@ -415,7 +442,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     } else {
       if (has_next) {
         set_tile(nvt);
-        load_scales();
+        load_scales(buf ^ 1);
         issue_prologue();
       }
     }
@@ -428,6 +455,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int ncol = wn * WTN + 4 * (lane >> 5);
     const int64_t mn = (int64_t)g.m * g.n;
     typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+    // A tile inside the output with aligned rows stores without per-lane guards.
+    const bool full = g.vec_store && cm0 + BM <= g.m && cn0 + BN <= g.n && !g.accd;
 
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
@@ -456,7 +485,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfrag(0, h, nb), afrag(0, h, mb), t1, 0, 0, 0);
           }
         }
-        u2v hw[4];  // 16-bit outputs of group q: columns 8q + 4 * (lane >> 5) + 0..3
+        unsigned pk[8];  // 16-bit outputs of group q as pairs: columns 8q + 4 * (lane >> 5) + 0..3
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nl = ncol + nb * 32 + 8 * q;
@@ -483,29 +512,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             out[r] = yv;
           }
           if constexpr (HALF_OUT) {
-            h_t hv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) hv[r] = (h_t)f32_fence(out[r]);
-            hw[q] = u2v{(unsigned)__builtin_bit_cast(unsigned short, hv[0]) |
-                            ((unsigned)__builtin_bit_cast(unsigned short, hv[1]) << 16),
-                        (unsigned)__builtin_bit_cast(unsigned short, hv[2]) |
-                            ((unsigned)__builtin_bit_cast(unsigned short, hv[3]) << 16)};
+            pk[2 * q] = cvt_pair<OUT_DT>(out[0], out[1]);
+            pk[2 * q + 1] = cvt_pair<OUT_DT>(out[2], out[3]);
           } else {
             if (m < g.m && n < g.n) store4_f32(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
           }
         }
         if constexpr (HALF_OUT) {
-          // Groups (q, q+1) of the two half-waves are exchanged so that each lane holds eight
+          // Groups (q, q+2) of the two half-waves are exchanged so that each lane holds eight
           // consecutive columns: lanes 0-31 columns 16pr + 0..7, lanes 32-63 16pr + 8..15.
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
-            const u2v X = hw[2 * pr], Y = hw[2 * pr + 1];
-            const auto s0 = __builtin_amdgcn_permlane32_swap(X.x, Y.x, false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(X.y, Y.y, false, false);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * pr], pk[4 * pr + 2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * pr + 1], pk[4 * pr + 3], false, false);
             const u4v w = {s0[0], s1[0], s0[1], s1[1]};
             const int no = cn0 + wn * WTN + nb * 32 + 16 * pr + 8 * (lane >> 5);
-            if (m < g.m && no < g.n) {
-              h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + no;
+            h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + no;
+            if (full) {
+              *reinterpret_cast<u4v*>(dst) = w;
+            } else if (m < g.m && no < g.n) {
               if (g.vec_store && no + 8 <= g.n) {
                 *reinterpret_cast<u4v*>(dst) = w;
               } else {
@@ -524,12 +549,243 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if constexpr (DUAL) {
       barrier_nofence();  // stages 0-1 (outlier partition) are no longer read
       set_tile(nvt);
-      load_scales();
+      load_scales(buf ^ 1);
       issue_prologue();
     }
-    store_scales(buf ^ 1);  // the next tile's epilogue reads them after several barriers
+    store_scales(buf ^ 1);  // register path: the next tile's epilogue reads them after several barriers
     buf ^= 1;
     vt = nvt;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Ping-pong schedule for int8 weights without an outlier partition and without the
+// remainder split (the W8A8 layers).  The two waves of a SIMD alternate between a memory
+// phase (the fragment reads of a whole 64-code stage and the refill loads) and a compute
+// phase (that stage's 16 MFMAs from registers), so each matrix pipe is fed by one wave
+// while the other reads LDS.  Waves 0-3 (one per SIMD) lead and waves 4-7 follow one
+// phase behind; two barriers per stage keep the phases apart.  The ring holds 4 stages,
+// refilled 2 stages ahead: a refill goes into the slot of the stage read 2 stages
+// earlier, whose last reader finished before the barrier that precedes the refill.
+// Measured at the fused-QKV shape (17776 x 1920 x 5760): 7-8% faster than the
+// interleaved schedule of k_qgemm.
+namespace ppc {
+constexpr int NST = 4, D = 2;
+constexpr int ROW = 64;                 // 64 int8 codes per row and stage
+constexpr int A_BYTES = BM * ROW;       // activations of a stage (16 KB)
+constexpr int STAGE = A_BYTES + BN * ROW;
+constexpr int LA = A_BYTES / (NT * 16);  // direct loads per wave per operand and stage (2)
+constexpr int L = 2 * LA;
+}  // namespace ppc
+
+__device__ __forceinline__ void sched_barrier_all() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int OUT_DT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm_pp(GArgs g) {
+  using namespace ppc;
+  constexpr bool HALF_OUT = OUT_DT != DT_F32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
+  __shared__ float s_sa[2][BM];
+  __shared__ float s_sb[2][BN];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nk = g.k0 / ROW;
+
+  int ra[LA], rb[LA], ca[LA], cb[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    dma_lane<ROW>(wave * LA + i, lane, ra[i], ca[i]);
+    dma_lane<ROW>(wave * LA + i, lane, rb[i], cb[i]);
+  }
+  const int8_t* ga[LA];
+  const uint8_t* gb[LA];
+  int m0 = 0, n0 = 0;
+  auto set_tile = [&](int t) {
+    int tm, tn;
+    tile_of(t, g.tiles_m, g.tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      ga[i] = g.a + (int64_t)min(m0 + ra[i], g.m - 1) * g.kp + ca[i];
+      gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * g.kp + cb[i];
+    }
+  };
+  auto issue = [&](int k, int slot) {
+    uint8_t* base = lds + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) dma16(ga[i] + k, base + (wave * LA + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) dma16(gb[i] + k, base + A_BYTES + (wave * LA + i) * 1024);
+  };
+  // Scales straight to LDS, one direct load per wave, ahead of the tile's first stage.
+  auto load_scales = [&](int buf) {
+    const int r = 64 * (wave & 3) + lane;
+    if (wave < 4)
+      dma4(g.sa_tok ? g.sa + min(m0 + r, g.m - 1) : g.sa, &s_sa[buf][64 * wave]);
+    else
+      dma4(g.sb + min(n0 + r, g.n - 1), &s_sb[buf][64 * (wave - 4)]);
+  };
+  const int rl = lane & 31, kc = lane >> 5;
+  int fa[2], fb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    fa[h] = (wm * WTM + rl) * ROW + 16 * ((2 * h + kc) ^ swz64(rl));
+    fb[h] = A_BYTES + (wn * WTN + rl) * ROW + 16 * ((2 * h + kc) ^ swz64(rl));
+  }
+  v16i acc[MBLK][NBLK];
+  v4i fA[2][MBLK], fB[2][NBLK];
+  auto read_stage = [&](int slot) {
+    const uint8_t* base = lds + slot * STAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb) fB[h][nb] = *reinterpret_cast<const v4i*>(base + fb[h] + nb * 32 * ROW);
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) fA[h][mb] = *reinterpret_cast<const v4i*>(base + fa[h] + mb * 32 * ROW);
+    }
+  };
+  auto compute = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fB[h][nb], fA[h][mb], acc[mb][nb], 0, 0, 0);
+  };
+  auto lds_reads_done = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };  // lgkmcnt(0)
+  auto wait_groups = [&](int later) {  // at most `later` stages of loads in flight
+    if (later >= 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+  };
+
+  int t = blockIdx.x;
+  if (t >= g.items) return;
+  set_tile(t);
+  load_scales(0);
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < nk) issue(s * ROW, s);
+  int buf = 0;
+  // pend: the previous tile issued exactly 16 vector stores after this tile's first loads,
+  // so waits for this tile's first stages leave those stores in flight (vmcnt is in order).
+  bool pend = false;
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
+    if (pend && nk > D) wait_vmcnt<(D - 1) * L + 16>();
+    else wait_groups(min(D, nk) - 1);
+    sched_barrier_all();
+    if (grp == 1) sched_barrier_all();
+    int p = 0;
+    for (; p + D < nk; ++p) {
+      // memory phase (leaders: while the followers compute stage p - 1)
+      read_stage(p % NST);
+      issue((p + D) * ROW, (p + D) % NST);
+      const bool early = pend && p < D - 1;  // stage p + 1 was loaded before the stores
+      if (grp == 1) {
+        if (early) wait_vmcnt<(D - 1) * L + 16>();
+        else wait_vmcnt<(D - 1) * L>();
+      }
+      lds_reads_done();
+      sched_barrier_all();
+      // compute phase
+      compute();
+      if (grp == 0) {
+        if (early) wait_vmcnt<(D - 1) * L + 16>();
+        else wait_vmcnt<(D - 1) * L>();
+      }
+      sched_barrier_all();
+    }
+    for (; p < nk; ++p) {
+      read_stage(p % NST);
+      const int later = nk - p - 2;
+      if (grp == 1) wait_groups(later < 0 ? 0 : later);
+      lds_reads_done();
+      sched_barrier_all();
+      compute();
+      if (grp == 0) wait_groups(later < 0 ? 0 : later);
+      sched_barrier_all();
+    }
+    if (grp == 0) sched_barrier_all();
+
+    const int nt = t + (int)gridDim.x;
+    const bool has_next = nt < g.items;
+    const int cm0 = m0, cn0 = n0;
+    if (has_next) {
+      set_tile(nt);
+      load_scales(buf ^ 1);
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (s < nk) issue(s * ROW, s);
+    }
+    const bool full = g.vec_store && cm0 + BM <= g.m && cn0 + BN <= g.n && !g.accd;
+    pend = HALF_OUT && has_next && full;
+    typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) {
+      const int ml = wm * WTM + rl + mb * 32;
+      const int m = cm0 + ml;
+      const float sa0 = s_sa[buf][ml];
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb) {
+        unsigned pk[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * WTN + 4 * kc + nb * 32 + 8 * q;
+          const int n = cn0 + nl;
+          const v4f sb0 = *reinterpret_cast<const v4f*>(&s_sb[buf][nl]);
+          float out[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int a0 = acc[mb][nb][4 * q + r];
+            const float t0 = sa0 * sb0[r];
+            out[r] = (float)a0 * t0;
+            if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
+          }
+          if constexpr (HALF_OUT) {
+            pk[2 * q] = cvt_pair<OUT_DT>(out[0], out[1]);
+            pk[2 * q + 1] = cvt_pair<OUT_DT>(out[2], out[3]);
+          } else {
+            if (m < g.m && n < g.n) store4_f32(g.y, (int64_t)m * g.ldy + n, out, min(4, g.n - n), g.vec_store != 0);
+          }
+        }
+        if constexpr (HALF_OUT) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * pr], pk[4 * pr + 2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * pr + 1], pk[4 * pr + 3], false, false);
+            const u4v w = {s0[0], s1[0], s0[1], s1[1]};
+            const int no = cn0 + wn * WTN + nb * 32 + 16 * pr + 8 * kc;
+            h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + no;
+            if (full) {
+              *reinterpret_cast<u4v*>(dst) = w;
+            } else if (m < g.m && no < g.n) {
+              if (g.vec_store && no + 8 <= g.n) {
+                *reinterpret_cast<u4v*>(dst) = w;
+              } else {
+                for (int e = 0; e < 8 && no + e < g.n; ++e) {
+                  const unsigned d = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+                  dst[e] = __builtin_bit_cast(h_t, (unsigned short)(d >> (16 * (e & 1))));
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    if (!has_next) break;
+    buf ^= 1;
+    t = nt;
   }
 }
 
@@ -613,6 +869,14 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.ws_part = split > 1 ? reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(p.ws) + QGEMM_WS_COUNTERS) : nullptr;
   const int grid = a.items < pb ? a.items : pb;
   const bool dual = p.k0 < p.kp;
+  if (p.b_bits == 8 && !dual && split == 1) {
+    switch (p.out_dt) {
+      case DT_F16: hipLaunchKernelGGL(k_qgemm_pp<DT_F16>, dim3(grid), dim3(NT), 0, st, a); break;
+      case DT_BF16: hipLaunchKernelGGL(k_qgemm_pp<DT_BF16>, dim3(grid), dim3(NT), 0, st, a); break;
+      default: hipLaunchKernelGGL(k_qgemm_pp<DT_F32>, dim3(grid), dim3(NT), 0, st, a); break;
+    }
+    return hipGetLastError();
+  }
   if (p.b_bits == 8) return launch_out<8>(a, p.out_dt, dual, grid, st);
   return launch_out<4>(a, p.out_dt, dual, grid, st);
 }
