@@ -125,6 +125,26 @@ def _buf(t, name, nbytes, device):
     return t
 
 
+def _in(t, name, dtypes, numel, device):
+    """A caller-given device input read by a kernel: on `device`, one of `dtypes`,
+    contiguous, with at least `numel` elements.  Checked before any launch, since a host
+    tensor or a short buffer would be read out of bounds by the GPU."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.device == device):
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor on {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} are needed")
+    return t
+
+
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_U8 = (torch.uint8,)
+
+
 def _out2d(t, name, rows, cols, device):
     """A caller-given [rows x cols] output with unit stride along its rows (any row pitch >= cols)."""
     if not (isinstance(t, torch.Tensor) and t.is_cuda and t.device == device):
@@ -151,6 +171,8 @@ def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kf
     if ws is None:
         ws = torch.empty(int(_lib.vq_detect_workspace_elems(rows, cols)), dtype=torch.float64, device=x.device)
     _buf(ws, "ws", 8 * int(_lib.vq_detect_workspace_elems(rows, cols)), x.device)
+    if n_out_dev is not None:
+        _in(n_out_dev, "n_out_dev", _I32, 1, x.device)
     norms = torch.empty(cols, dtype=torch.float64)
     mask = torch.empty(cols, dtype=torch.uint8)
     idx = torch.empty(cols, dtype=torch.int32)
@@ -167,6 +189,8 @@ def vq_pack_weights(w: torch.Tensor, bits: int, idx: torch.Tensor | None = None,
     _dev(w, "w")
     n, k = w.shape
     n_out = 0 if idx is None else int(idx.numel())
+    if idx is not None:
+        _in(idx, "idx", _I32, n_out, w.device)
     kp = vq_packed_k(k, n_out)
     if codes is None:
         codes = (torch.empty((n, kp), dtype=torch.int8, device=w.device) if bits == 8
@@ -188,8 +212,14 @@ def vq_quant_act(x: torch.Tensor, bits: int, gran: str = "token", had_block: int
     _dev(x, "x")
     m, k = x.shape
     n_out = 0 if idx is None else int(idx.numel())
+    if idx is not None:
+        _in(idx, "idx", _I32, n_out, x.device)
+    if static_scale is not None:
+        _in(static_scale, "static_scale", _F32, 2 if n_out else 1, x.device)
+    if bits_dev is not None:
+        _in(bits_dev, "bits_dev", _I32, 1, x.device)
     kp = vq_packed_k(k, n_out)
-    g = _GRAN[gran]
+    g = _GRAN.get(gran, -1)
     if codes is None:
         codes = torch.empty((m, kp), dtype=torch.int8, device=x.device)
     if scales is None:
@@ -229,6 +259,7 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
     m, kp = a.shape
     n = b.shape[0]
     k0 = kp if k0 is None else k0
+    _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token)
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if acc_debug and acc is None:
@@ -244,6 +275,29 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None),
         None if ws is False else _ptr(ws), _stream(a)))
     return (y, acc) if acc_debug else y
+
+
+def _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token=True):
+    """The GEMM's codes and scales as the kernels read them: A int8 [M x kp] dense; B int8
+    [N x kp] (8-bit weights) or uint8 [N x kp/2] (4-bit); scales float32 with one or two
+    partitions (k0 < kp: two per row, column and tensor)."""
+    dev = a.device
+    m = a.shape[0]
+    parts = 2 if k0 < kp else 1
+    _in(a, "a", (torch.int8,), m * kp, dev)
+    if not (isinstance(b, torch.Tensor) and b.dim() == 2):
+        raise TypeError("b must be a 2-D CUDA (HIP) tensor of packed weight codes")
+    n = b.shape[0]
+    if b_bits == 8:
+        _in(b, "b", (torch.int8,), n * kp, dev)
+        if b.shape[1] != kp:
+            raise ValueError(f"b must be [N x {kp}] int8 codes for 8-bit weights")
+    elif b_bits == 4:
+        _in(b, "b", _U8, n * kp // 2, dev)
+        if b.shape[1] != kp // 2:
+            raise ValueError(f"b must be [N x {kp // 2}] packed nibbles for 4-bit weights")
+    _in(sa, "sa", _F32, (m if sa_per_token else 1) * parts, dev)
+    _in(sb, "sb", _F32, n * parts, dev)
 
 
 _GEMM_WS = {}
@@ -262,6 +316,13 @@ def _workspace(need, device):
     key = (device, torch.cuda.current_stream(device).cuda_stream)
     t = _GEMM_WS.get(key)
     if t is None or t.numel() < need:
+        # Under graph capture a new buffer's zero fill would only be recorded, while the
+        # buffer would be cached for eager calls that run before the first replay.
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                "the GEMM's remainder-split workspace must exist before graph capture: pass ws= (a zero-filled "
+                "buffer of vq_qgemm_workspace_bytes / vq_mx_gemm_workspace_bytes bytes) or ws=False, or make one "
+                "eager call on the capturing stream first")
         t = torch.zeros(need, dtype=torch.uint8, device=device)
         _GEMM_WS[key] = t
     return t
@@ -272,6 +333,8 @@ def vq_route_rel_l1(x: torch.Tensor, y: torch.Tensor, threshold: float = 0.1, bi
     """Device-side DMPQ route: returns (bits int32 [1], gamma float64 [1]) on the device."""
     _dev(x, "x")
     n = x.numel()
+    _in(x, "x", (x.dtype,), n, x.device)
+    _in(y, "y", (x.dtype,), n, x.device)
     if ws is None:
         ws = torch.empty(int(_lib.vq_route_workspace_elems(n)), dtype=torch.float64, device=x.device)
     if gamma is None:
@@ -301,7 +364,7 @@ def vq_quant_residual(x: torch.Tensor, rows: torch.Tensor, bits1: int, bits2: in
         codes = torch.empty((2 * n_rows, k), dtype=torch.int8, device=x.device)
     if scales is None:
         scales = torch.empty((2 * n_rows,), dtype=torch.float32, device=x.device)
-    _dev(rows, "rows")
+    _in(rows, "rows", _I32, n_rows, x.device)
     _buf(codes, "codes", 2 * n_rows * k, x.device)
     _buf(scales, "scales", 8 * n_rows, x.device)
     _check("vq_quant_residual", _lib.vq_quant_residual(
@@ -327,8 +390,11 @@ def vq_qgemm_dequant_residual(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor
     if ws is None and n_rows:
         ws = torch.empty(vq_residual_workspace_bytes(m, n_rows, n), dtype=torch.uint8, device=a.device)
     _out2d(y, "y", m, n, a.device)
+    _check_gemm_operands(a, sa, b, sb, b_bits, kp, kp)
     if n_rows:
-        _dev(rows, "rows")
+        _in(rows, "rows", _I32, n_rows, a.device)
+        _in(a2, "a2", (torch.int8,), 2 * n_rows * kp, a.device)
+        _in(sa2, "sa2", _F32, 2 * n_rows, a.device)
         _buf(ws, "ws", vq_residual_workspace_bytes(m, n_rows, n), a.device)
     _check("vq_qgemm_dequant_residual", _lib.vq_qgemm_dequant_residual(
         _ptr(a), _ptr(sa), _ptr(b), b_bits, _ptr(sb), m, n, kp, _ptr(a2), _ptr(sa2), _ptr(rows), n_rows,
@@ -373,6 +439,11 @@ def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: 
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     _out2d(y, "y", m, n, a.device)
+    if fa in _MX and fb in _MX:
+        _in(a, "a", _U8, vq_mx_code_bytes(m, k, fa), a.device)
+        _in(sa, "sa", _U8, vq_mx_scale_bytes(m, k), a.device)
+        _in(b, "b", _U8, vq_mx_code_bytes(n, k, fb), a.device)
+        _in(sb, "sb", _U8, vq_mx_scale_bytes(n, k), a.device)
     need = int(_lib.vq_mx_gemm_workspace_bytes(m, n, k))
     ws = _workspace(need, a.device) if ws is None else ws
     if ws is not False:
@@ -454,7 +525,7 @@ def vq_step_control(state: torch.Tensor, params: ControlParams, delta_new=None, 
     for t, name, nb in ((skip, "skip", 4), (bits, "bits", 4), (e, "e", 8), (gamma, "gamma", 8)):
         _buf(t, name, nb, dev)
     if n_out_dev is not None:
-        _buf(n_out_dev, "n_out_dev", 4, dev)
+        _in(n_out_dev, "n_out_dev", _I32, 1, dev)
     dnew_dt = _DT.get(delta_new.dtype, -1) if delta_new is not None else 0
     xy_dt = _DT.get(x_prev.dtype, -1) if x_prev is not None else 0
     _check("vq_step_control", _lib.vq_step_control(

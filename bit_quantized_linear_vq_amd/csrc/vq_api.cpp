@@ -222,9 +222,9 @@ int64_t vq_qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0) {
   return vq_internal::qgemm_workspace_bytes(m, n, k0);
 }
 
-vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits,
-                           const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0, void* y, vq_dtype out_dt,
-                           int64_t ldy, int32_t* acc_debug, void* ws, hipStream_t stream) {
+namespace {
+vq_status check_gemm(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits, const float* sb,
+                     int64_t m, int64_t n, int64_t kp, int64_t k0, void* y, vq_dtype out_dt, int64_t ldy) {
   if (!a || !sa || !b || !sb || !y) return VQ_ERR_INVALID_ARG;
   if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
   if (sa_per_token != 0 && sa_per_token != 1) return VQ_ERR_INVALID_ARG;
@@ -232,9 +232,18 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
     return VQ_ERR_INVALID_ARG;
   if (b_bits != 4 && b_bits != 8) return VQ_ERR_UNSUPPORTED;
   if (kp % VQ_K_ALIGN || k0 % VQ_K_ALIGN || k0 > kp || kp - k0 > VQ_MAX_OUTLIERS) return VQ_ERR_SHAPE;
+  // The int32 accumulators must hold any sum of the longer partition (partition 0): 127
+  // per activation code times 127 per int8 weight code, or 112 = 16 * 7 per 4-bit weight
+  // code, which enters the MFMA as 16 times its value.
+  if ((double)k0 * 127.0 * (b_bits == 8 ? 127.0 : 112.0) >= 2147483648.0) return VQ_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b)) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
-  if (ws && !aligned16(ws)) return VQ_ERR_SHAPE;
+  return VQ_OK;
+}
+
+vq_internal::GemmParams gemm_params(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits,
+                                    const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0, void* y,
+                                    vq_dtype out_dt, int64_t ldy) {
   vq_internal::GemmParams p{};
   p.a = a;
   p.sa = sa;
@@ -249,6 +258,17 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
   p.y = y;
   p.out_dt = (int)out_dt;
   p.ldy = ldy;
+  return p;
+}
+}  // namespace
+
+vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits,
+                           const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0, void* y, vq_dtype out_dt,
+                           int64_t ldy, int32_t* acc_debug, void* ws, hipStream_t stream) {
+  vq_status s = check_gemm(a, sa, sa_per_token, b, b_bits, sb, m, n, kp, k0, y, out_dt, ldy);
+  if (s != VQ_OK) return s;
+  if (ws && !aligned16(ws)) return VQ_ERR_SHAPE;
+  vq_internal::GemmParams p = gemm_params(a, sa, sa_per_token, b, b_bits, sb, m, n, kp, k0, y, out_dt, ldy);
   p.acc_debug = acc_debug;
   p.ws = ws;
   return hip_status(vq_internal::launch_qgemm(p, stream));

@@ -172,7 +172,10 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
  *   sa       device float: sa_per_token ? [m] or [m x 2] : [1] or [2]
  *   b        device: b_bits 8 -> int8 [n x kp]; b_bits 4 -> uint8 [n x kp/2] packed nibbles
  *   sb       device float [n] or [n x 2]
- *   kp, k0   kp % 64 == 0, k0 % 64 == 0, 0 < k0 <= kp, kp - k0 <= 128
+ *   kp, k0   kp % 64 == 0, k0 % 64 == 0, 0 < k0 <= kp, kp - k0 <= 128; the int32
+ *            accumulators bound k0: k0 * 127 * 127 < 2^31 (int8 weights, k0 <= 133120) or
+ *            k0 * 127 * 112 < 2^31 (4-bit weights, which enter the MFMA as 16 * code,
+ *            k0 <= 150976); longer K is rejected with VQ_ERR_SHAPE
  *   y        device out_dt in {F16, BF16, F32}, [m x n], row stride ldy (element aligned;
  *            a 16-byte aligned y whose row pitch is a multiple of 16 bytes takes the
  *            vector-store path)

@@ -39,3 +39,36 @@ def test_rejects_strided_columns_and_bad_outputs(vq):
     big = torch.empty((64, 192), dtype=torch.bfloat16, device=DEV)
     y = vq.vq_qgemm_dequant(ac, as_, wc, ws, 8, y=big[:, 32:160])
     assert torch.equal(y, vq.vq_qgemm_dequant(ac, as_, wc, ws, 8))
+
+
+def test_rejects_inputs_the_kernels_would_misread(vq):
+    """Index, scale and code inputs are checked for device, dtype, contiguity and length
+    before any launch: a host or int64 index tensor, short scales or codes of the wrong
+    width must raise instead of reaching a kernel."""
+    x = torch.randn(64, 256, device=DEV).to(torch.bfloat16)
+    w = torch.randn(128, 256, device=DEV).to(torch.bfloat16)
+    idx = torch.tensor([3, 17], dtype=torch.int32)
+    with pytest.raises(TypeError):
+        vq.vq_pack_weights(w, 4, idx)  # host index tensor (as vq_detect_outliers returns it)
+    with pytest.raises(TypeError):
+        vq.vq_pack_weights(w, 4, idx.to(DEV).long())  # int64 index
+    with pytest.raises(TypeError):
+        vq.vq_quant_act(x, 8, idx=idx)
+    with pytest.raises(ValueError):
+        vq.vq_quant_act(x, 8, "static", static_scale=torch.ones(1, device=DEV), idx=idx.to(DEV))  # needs 2 scales
+    with pytest.raises(TypeError):
+        vq.vq_quant_act(x, 8, bits_dev=torch.tensor([8], device=DEV, dtype=torch.int64))
+    wc8, ws8 = vq.vq_pack_weights(w, 8)
+    wc4, ws4 = vq.vq_pack_weights(w, 4)
+    ac, as_ = vq.vq_quant_act(x, 8)
+    with pytest.raises(ValueError):
+        vq.vq_qgemm_dequant(ac, as_, wc8, ws8[:100], 8)  # short column scales
+    with pytest.raises(TypeError):
+        vq.vq_qgemm_dequant(ac, as_, wc4, ws4, 8)  # packed nibbles passed as 8-bit codes
+    with pytest.raises(TypeError):
+        vq.vq_qgemm_dequant(ac, as_.cpu(), wc8, ws8, 8)
+    with pytest.raises(ValueError):
+        vq.vq_qgemm_dequant(ac, as_, wc8, ws8, 8, k0=192)  # two partitions need two scales per row/column
+    with pytest.raises(ValueError):
+        vq.vq_qgemm_dequant(ac[:, :128].contiguous(), as_, wc8, ws8, 8)  # K of a and b disagree
+    torch.cuda.synchronize()

@@ -71,3 +71,42 @@ def test_graph_replays_match_eager(vq, m, n, k, gran):
         assert torch.equal(y, y_ref2), f"eager after replay {rep}"
     if need:
         assert not ws[:4096].any()
+
+
+def test_default_workspace_under_capture(vq, monkeypatch):
+    """ws=None under graph capture: with no workspace cached for the capturing stream the
+    binding refuses before any launch (a buffer created there would be cached with its zero
+    fill only recorded); after one eager call on that stream the cached, zeroed buffer
+    serves the capture and every replay."""
+    m, n, k = 300, 320, 6144  # four tiles, two K ranges each: the workspace is used
+    assert vq._lib.vq_qgemm_workspace_bytes(m, n, k) > 0
+    g = torch.Generator(device=DEV).manual_seed(7)
+    x = torch.randn(m, k, generator=g, device=DEV).to(torch.bfloat16)
+    w = (torch.randn(n, k, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    wc, wsc = vq.vq_pack_weights(w, 8)
+    ac, as_ = vq.vq_quant_act(x, 8)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    y_ref = vq.vq_qgemm_dequant(ac, as_, wc, wsc, 8, ws=False)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for key in [key for key in vq._GEMM_WS if key[1] == side.cuda_stream]:
+        del vq._GEMM_WS[key]  # pooled stream handles repeat: start without a cached buffer
+    with torch.cuda.stream(side):
+        with monkeypatch.context() as mp:  # as seen from inside a capture
+            mp.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+            with pytest.raises(RuntimeError, match="workspace"):
+                vq.vq_qgemm_dequant(ac, as_, wc, wsc, 8, y=y)
+        vq.vq_qgemm_dequant(ac, as_, wc, wsc, 8, y=y)  # eager: creates and zero-fills the buffer
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            vq.vq_qgemm_dequant(ac, as_, wc, wsc, 8, y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
