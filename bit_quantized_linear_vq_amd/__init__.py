@@ -27,6 +27,7 @@ VQ_MAX_OUTLIERS = 128
 EXPORTS = (
     "vq_outlier_part_len", "vq_packed_k", "vq_detect_workspace_elems", "vq_detect_outliers",
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant", "vq_qgemm_workspace_bytes",
+    "vq_qgemm_scratch_bytes", "vq_qgemm_dequant_noalloc",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
     "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
     "vq_mx_gemm_workspace_bytes",
@@ -66,6 +67,8 @@ def _load():
         "vq_hadamard_block": (I, [P, I, I64, P, I, I64, I64, I64, I, I, P]),
         "vq_qgemm_dequant": (I, [P, P, I, P, I, P, I64, I64, I64, I64, P, I, I64, P, P, P]),
         "vq_qgemm_workspace_bytes": (I64, [I64, I64, I64]),
+        "vq_qgemm_scratch_bytes": (I64, []),
+        "vq_qgemm_dequant_noalloc": (I, [P, P, I, P, I, P, I64, I64, I64, I64, P, I, I64, P]),
         "vq_route_workspace_elems": (I64, [I64]),
         "vq_route_rel_l1": (I, [P, P, I, I64, D, I, I, P, P, P, P]),
         "vq_quant_residual": (I, [P, I, I64, I64, I64, I, I, P, I64, P, P, P]),
@@ -298,6 +301,22 @@ def _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token=True):
             raise ValueError(f"b must be [N x {kp // 2}] packed nibbles for 4-bit weights")
     _in(sa, "sa", _F32, (m if sa_per_token else 1) * parts, dev)
     _in(sb, "sb", _F32, n * parts, dev)
+
+
+def vq_qgemm_dequant_noalloc(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor, b_bits: int,
+                             y: torch.Tensor, k0: int | None = None, sa_per_token: bool = True):
+    """Y = dequant(A_codes . B_codes^T) into the caller's y, allocating nothing (the remainder
+    split uses the library's static scratch; overlapping calls on one GPU race)."""
+    _dev(a, "a")
+    m, kp = a.shape
+    n = b.shape[0]
+    k0 = kp if k0 is None else k0
+    _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token)
+    _out2d(y, "y", m, n, a.device)
+    _check("vq_qgemm_dequant_noalloc", _lib.vq_qgemm_dequant_noalloc(
+        _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
+        _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _stream(a)))
+    return y
 
 
 _GEMM_WS = {}

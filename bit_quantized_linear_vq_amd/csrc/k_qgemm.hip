@@ -38,6 +38,7 @@
 // sums are exact in any order, so the result is bit-identical to the unsplit tile, and
 // no workgroup ever waits for another.  The last arrival resets the tile's counter, so
 // the workspace is left zeroed for the next call.
+#include <mutex>
 #include <type_traits>
 
 #include "dev_common.h"
@@ -48,6 +49,9 @@ namespace vqk {
 
 constexpr int BM = 256, BN = 256;
 constexpr int64_t QGEMM_WS_COUNTERS = 4096;  // arrival counters of up to 1024 remaining tiles
+// Largest remainder-split workspace the scratch-free entry serves (40 MiB): the counters
+// plus two 256 KB partials for each of up to 159 remaining tiles.
+constexpr int64_t QGEMM_SCRATCH_BYTES = (int64_t)40 << 20;
 constexpr int NT = 512;           // threads per workgroup
 constexpr int WTM = 128, WTN = 64;  // wave tile
 constexpr int MBLK = WTM / 32, NBLK = WTN / 32;
@@ -879,6 +883,48 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   }
   if (p.b_bits == 8) return launch_out<8>(a, p.out_dt, dual, grid, st);
   return launch_out<4>(a, p.out_dt, dual, grid, st);
+}
+
+// ---- scratch-free entry: the remainder split's workspace in a static device array.
+// Each GPU the library runs on holds its own copy from the code object's load until the
+// process ends.  Host code never uses the array's name as an address (on the host it is a
+// stand-in): the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[QGEMM_SCRATCH_BYTES];
+
+int64_t qgemm_scratch_bytes() { return QGEMM_SCRATCH_BYTES; }
+
+static hipError_t scratch_address(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_qgemm_noalloc(const GemmParams& p, hipStream_t st) {
+  GemmParams q = p;
+  q.ws = nullptr;
+  if (qgemm_workspace_bytes(p.m, p.n, p.k0) > 0) {
+    hipError_t e = scratch_address(&q.ws);
+    if (e != hipSuccess) return e;
+    // The arrival counters must start at zero.  Every call leaves them zero, but the
+    // array's first contents are not the library's to rely on, so each call clears them
+    // with a fill kernel (which, unlike a memset node, also replays correctly in a graph).
+    e = launch_fill_u32(reinterpret_cast<unsigned*>(q.ws), (int)(QGEMM_WS_COUNTERS / 4), 0u, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_qgemm(q, st);
 }
 
 }  // namespace vq_internal

@@ -274,6 +274,18 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
   return hip_status(vq_internal::launch_qgemm(p, stream));
 }
 
+int64_t vq_qgemm_scratch_bytes(void) { return vq_internal::qgemm_scratch_bytes(); }
+
+vq_status vq_qgemm_dequant_noalloc(const int8_t* a, const float* sa, int sa_per_token, const void* b, int b_bits,
+                                   const float* sb, int64_t m, int64_t n, int64_t kp, int64_t k0, void* y,
+                                   vq_dtype out_dt, int64_t ldy, hipStream_t stream) {
+  vq_status s = check_gemm(a, sa, sa_per_token, b, b_bits, sb, m, n, kp, k0, y, out_dt, ldy);
+  if (s != VQ_OK) return s;
+  if (vq_internal::qgemm_workspace_bytes(m, n, k0) > vq_internal::qgemm_scratch_bytes()) return VQ_ERR_SHAPE;
+  return hip_status(vq_internal::launch_qgemm_noalloc(
+      gemm_params(a, sa, sa_per_token, b, b_bits, sb, m, n, kp, k0, y, out_dt, ldy), stream));
+}
+
 // ------------------------------------------------------------------ decomposition
 
 namespace {

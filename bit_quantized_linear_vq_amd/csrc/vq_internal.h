@@ -53,6 +53,9 @@ struct GemmParams {
 };
 int64_t qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0);
 hipError_t launch_qgemm(const GemmParams& g, hipStream_t st);
+// Scratch-free launch: the split workspace is the library's static device array.
+int64_t qgemm_scratch_bytes();
+hipError_t launch_qgemm_noalloc(const GemmParams& g, hipStream_t st);
 
 hipError_t launch_residual_quant(const void* x, int dtype, int64_t ldx, int64_t m, int64_t k, const int32_t* rows,
                                  int64_t n_rows, int bits1, int bits2, int8_t* codes2, float* scales2,

@@ -197,6 +197,25 @@ vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, c
                            hipStream_t stream);
 
 /*
+ * vq_qgemm_dequant without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  It computes exactly what vq_qgemm_dequant computes (bit-identical
+ * output) and allocates nothing: the remainder split's workspace is a static device array
+ * of vq_qgemm_scratch_bytes() bytes (40 MiB) that the library holds on each GPU it runs
+ * on until the process ends.  Each call clears the array's arrival counters with a fill
+ * kernel on `stream` before the GEMM, and leaves them zero.  Calls that overlap on one GPU
+ * (on different streams, or from different threads) share the array and race; serialize
+ * them.  Arguments as for vq_qgemm_dequant, without acc_debug and ws.
+ * Errors: as vq_qgemm_dequant, plus SHAPE when the shape's split needs more than the
+ * array holds (vq_qgemm_workspace_bytes(m, n, k0) > vq_qgemm_scratch_bytes()).
+ */
+int64_t vq_qgemm_scratch_bytes(void);
+vq_status vq_qgemm_dequant_noalloc(const int8_t* a, const float* sa, int sa_per_token, const void* b,
+                                   int b_bits, const float* sb, int64_t m, int64_t n, int64_t kp,
+                                   int64_t k0, void* y, vq_dtype out_dt, int64_t ldy,
+                                   hipStream_t stream);
+
+/*
  * Activation decomposition (SemanticDialect, gist.science summary of arXiv 2603.02883,
  * Methodology 2.2: the quantization error of the activation is quantized again and its
  * contribution added to the output, for selected tokens only).  For each listed row
