@@ -74,6 +74,10 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   __shared__ float s_red[8][2];
   // Per wave: the outlier bits of the wave's NP passes (32 words of 32 channels each).
   __shared__ unsigned s_mask[DUAL ? 8 * NPMAX * 32 : 1];
+  // Dual scale with one wave per row: per row of the block, an image of the loaded row
+  // (K 16-bit words, dynamic LDS sized at launch).
+  extern __shared__ u4v s_rowimg_v[];
+  unsigned short* s_rowimg = reinterpret_cast<unsigned short*>(s_rowimg_v);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -150,10 +154,12 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
       }
     // The row's loads go out before anything that waits for the outlier indices.
     __builtin_amdgcn_sched_barrier(0);
-    // Outlier partition: gathered by wave 0 of the row, at most 128 values.
+    // Outlier partition, at most 128 values.  A row held by several waves: gathered from
+    // memory by its wave 0.  A row held by one wave (K <= 4096): taken from the row's own
+    // loads through LDS (below), so no extra memory request is made.
     unsigned short oraw[2] = {0, 0};
     if constexpr (DUAL) {
-      if (wr == 0) {
+      if (wr == 0 && a.W > 1) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) oraw[i] = reinterpret_cast<const unsigned short*>(xrow)[oidx[i]];
       }
@@ -163,6 +169,25 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
       if (!bits_ready) {  // wave-uniform
         build_bits();
         bits_ready = true;
+      }
+      if (a.W == 1) {
+        // Each piece holding an outlier channel is copied, as loaded, into the wave's row
+        // image in LDS (channel-indexed 16-bit words); then lane i reads outlier i.  The
+        // LDS operations of one wave complete in program order; the fences keep the
+        // compiler from moving them across one another.
+        unsigned short* img = s_rowimg + rib * a.k;
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int e = piece(j, h);
+            if (obits[j][h] != 0u && e < a.k) *reinterpret_cast<u4v*>(img + e) = raw[j][h];
+          }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (lane + 64 * i < a.n_out) oraw[i] = img[oidx[i]];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       }
     }
 
@@ -337,11 +362,12 @@ __global__ void k_tensor_finalize(float* scales, const float* static_src, int pa
 template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
 static hipError_t launch_row(const RowArgs& a, int grid, int block, hipStream_t st) {
   // The pass count is a compile-time constant so that a lane holds exactly its passes.
+  const size_t shm = (DUAL && a.W == 1) ? (size_t)(block / 64) * a.k * 2 : 0;  // rows per block x K words
   switch (a.np) {
-    case 1: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 1>), dim3(grid), dim3(block), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 2>), dim3(grid), dim3(block), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 3>), dim3(grid), dim3(block), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, NPMAX>), dim3(grid), dim3(block), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 1>), dim3(grid), dim3(block), shm, st, a); break;
+    case 2: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 2>), dim3(grid), dim3(block), shm, st, a); break;
+    case 3: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 3>), dim3(grid), dim3(block), shm, st, a); break;
+    default: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, NPMAX>), dim3(grid), dim3(block), shm, st, a); break;
   }
   return hipGetLastError();
 }
