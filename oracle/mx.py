@@ -105,6 +105,26 @@ def quantize(x: np.ndarray, fmt: str):
     return encode(t, fmt), (e + 127).astype(np.uint8)
 
 
+def quantize_rotated(x: np.ndarray, fmt: str, exp_offset: int = 0, block: int = 128):
+    """MX quantization of the rows of float32 x rotated by the online block Hadamard
+    transform (6Bit-Diffusion page, Methodology B.1: the 4-bit floating-point route
+    rotates the activations by 128-point Hadamard blocks before quantizing them).
+
+    z = the unnormalized block FWHT of each row (fwht.fwht_blocks: float32 butterflies,
+    ascending distances); t = fl32(z * 2^exp_offset); then quantize(t).  Activations take
+    exp_offset = 0.  Weights pre-rotated offline take exp_offset = -7: their decoded values
+    approximate z_w / 128, so that products with unnormalized rotated activations give
+    sum_k z_x z_w / 128 = sum_k x w (H H^T = 128 I), with no irrational 1/sqrt(128) and no
+    extra operation in the GEMM.  Scaling by a power of two leaves the element codes
+    unchanged and moves the block exponents by exp_offset, unless it leaves the float32
+    normal range.
+    """
+    from .fwht import fwht_blocks
+    z = fwht_blocks(np.asarray(x, dtype=np.float32), block)
+    t = (z * np.float32(2.0 ** exp_offset)).astype(np.float32)
+    return quantize(t, fmt)
+
+
 def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
     e = scales.astype(np.int64) - 127
     return decode(codes, fmt) * np.ldexp(1.0, np.repeat(e, BLOCK, axis=1))

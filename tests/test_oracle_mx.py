@@ -120,3 +120,53 @@ def test_gemm_equals_table_lookup_product():
     da = lut6[ac] * np.ldexp(1.0, np.repeat(asc.astype(int) - 127, 32, axis=1))
     db = lut4[bc] * np.ldexp(1.0, np.repeat(bsc.astype(int) - 127, 32, axis=1))
     np.testing.assert_array_equal(mx.gemm(ac, asc, "fp6", bc, bsc, "fp4"), da @ db.T)
+
+
+# ---------------------------------------------------------------- rotated route (online block Hadamard)
+
+def test_rotated_hand_worked_blocks():
+    """x = e_0 rotates to a row of ones (column 0 of the Sylvester matrix): every 32-block
+    has amax 1, e = 0 - 2 = -2 (byte 125) and 1 / 2^-2 = 4 -> FP4 code 6.  x = e_1 gives
+    (+1, -1, +1, ...): codes alternate 6 and 14 (sign bit 8).  x = 2 e_0 + e_1 gives
+    (3, 1, 3, 1, ...): amax 3, e = 1 - 2 = -1 (byte 126), 3 / 0.5 = 6 -> code 7, 1 / 0.5 =
+    2 -> code 4."""
+    x = np.zeros((3, 128), np.float32)
+    x[0, 0] = 1.0
+    x[1, 1] = 1.0
+    x[2, 0], x[2, 1] = 2.0, 1.0
+    codes, scales = mx.quantize_rotated(x, "fp4")
+    assert codes[0].tolist() == [6] * 128
+    assert codes[1].tolist() == [6, 14] * 64
+    assert codes[2].tolist() == [7, 4] * 64
+    assert scales.tolist() == [[125] * 4, [125] * 4, [126] * 4]
+    # Weights pre-rotated with exp_offset = -7: same codes, exponents 7 lower; the decoded
+    # product of the two rotated e_0 rows is 128 * 1 * 2^-7 = 1 = e_0 . e_0.
+    wc, ws = mx.quantize_rotated(x[:1], "fp4", exp_offset=-7)
+    assert wc[0].tolist() == [6] * 128 and ws.tolist() == [[118] * 4]
+    y = mx.gemm(codes[:1], scales[:1], "fp4", wc, ws, "fp4")
+    assert y.tolist() == [[1.0]]
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp6"])
+def test_rotated_equals_explicit_hadamard_product(fmt):
+    """On small-integer rows the float32 butterflies are exact, so the rotated codes must
+    equal the codes of H x computed as a float64 product with the explicit +-1 matrix
+    (scipy's Sylvester construction), for both exponent offsets."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(11)
+    x = rng.integers(-9, 10, size=(16, 384)).astype(np.float32)
+    h = hadamard(128).astype(np.float64)
+    z = (x.astype(np.float64).reshape(16, 3, 128) @ h.T).reshape(16, 384)
+    for off in (0, -7):
+        got = mx.quantize_rotated(x, fmt, exp_offset=off)
+        want = mx.quantize((z * 2.0 ** off).astype(np.float32), fmt)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_rotated_offset_moves_only_exponents():
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    c0, s0 = mx.quantize_rotated(x, "fp6")
+    c7, s7 = mx.quantize_rotated(x, "fp6", exp_offset=-7)
+    assert np.array_equal(c0, c7)
+    assert np.array_equal(s0.astype(int) - 7, s7.astype(int))
