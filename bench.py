@@ -55,7 +55,9 @@ def parse():
                         "in the epilogue); per-token workloads without dual scale or rotation only")
     p.add_argument("--mx", choices=["fp4", "fp6"], default=None,
                    help="route the activations through the MX block formats (MXFP4 weights) on the scaled "
-                        "MFMA; with --config 5 the layers routed to 4 bits take MXFP4, the others INT8")
+                        "MFMA; with --config 4 the activations are rotated online by the 128-point block Hadamard "
+                        "and the weights offline; with --config 5 the layers routed to 4 bits take MXFP4, the "
+                        "others INT8")
     p.add_argument("--calibrate", action="store_true",
                    help="only time the static-scale calibration (clipping-percentile search) on the "
                         "workload's activations and exit")
@@ -143,10 +145,11 @@ class Layer:
             if c["dual"] or c["gran"] != "token":
                 raise SystemExit("--mx needs a per-token workload without dual scale")
             w = gen.make_w(cfg).to(dev)
-            self.mx_w = [vq.vq_mx_quant(w, "fp4")]
+            # With the workload's block Hadamard, the activations are rotated online and the
+            # weights offline (their block exponents 7 lower, so the GEMM needs no 1/128).
+            self.mx_w = [vq.vq_mx_quant(w, "fp4", had_block=self.had, exp_offset=-7 if self.had else 0)]
             self.w = [None]
             self.bits_dev = [None]
-            self.had = 0  # the MX blocks carry their own scales; no rotation on this route
             del w
         else:
             w = gen.make_w(cfg).to(dev)
@@ -199,7 +202,7 @@ class Layer:
     def quant(self, step, layer):
         x = self.x[step % len(self.x)]
         if self.use_mx(layer):
-            self.vq.vq_mx_quant(x, self.mx_fmt, self.mx_codes, self.mx_scales)
+            self.vq.vq_mx_quant(x, self.mx_fmt, self.mx_codes, self.mx_scales, had_block=self.had if self.cfg != 5 else 0)
             return
         self.vq.vq_quant_act(x, self.a_bits, self.gran, self.had, self.idx,
                              bits_dev=self.bits_dev[layer], codes=self.codes, scales=self.scales)
@@ -541,10 +544,10 @@ def main():
         out["dtype"] = L.mx_fmt
         out["config"]["w_bits"] = "mxfp4"
         out["config"]["a_bits"] = "mx" + L.mx_fmt
-        out["config"]["hadamard_block"] = 0
+        out["config"]["hadamard_block"] = L.had
         out["roofline"].update({"peak": FP4_FP6_PEAK_TFLOPS, "frac": round(gemm_tops / FP4_FP6_PEAK_TFLOPS, 4),
                                 "kernel": "k_mxgemm (scaled MFMA f8f6f4, MX block scales)"})
-        out["act_quant"]["kernel"] = "k_mxquant"
+        out["act_quant"]["kernel"] = "k_mxquant (fused 128-point block Hadamard)" if L.had else "k_mxquant"
     if L.mx and args.config == 5:
         out["config"]["route_4bit"] = "mxfp4 x mxfp4 on the scaled MFMA"
     if L.R:

@@ -29,7 +29,8 @@ EXPORTS = (
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant", "vq_qgemm_workspace_bytes",
     "vq_qgemm_scratch_bytes", "vq_qgemm_dequant_noalloc",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
-    "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_gemm",
+    "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_quant_rotated",
+    "vq_mx_gemm",
     "vq_mx_gemm_workspace_bytes",
     "vq_calib_hist_bins", "vq_calib_static_scale", "vq_control_workspace_elems", "vq_step_control",
     "vq_status_string", "vq_last_hip_error", "vq_version",
@@ -77,6 +78,7 @@ def _load():
         "vq_mx_code_bytes": (I64, [I64, I64, I]),
         "vq_mx_scale_bytes": (I64, [I64, I64]),
         "vq_mx_quant": (I, [P, I, I64, I64, I64, I, P, P, P]),
+        "vq_mx_quant_rotated": (I, [P, I, I64, I64, I64, I, I, P, P, P]),
         "vq_mx_gemm": (I, [P, P, I, P, P, I, I64, I64, I64, P, I, I64, P, P]),
         "vq_mx_gemm_workspace_bytes": (I64, [I64, I64, I64]),
         "vq_calib_hist_bins": (I64, []),
@@ -429,17 +431,28 @@ def vq_mx_scale_bytes(rows: int, k: int) -> int:
     return int(_lib.vq_mx_scale_bytes(rows, k))
 
 
-def vq_mx_quant(x: torch.Tensor, fmt: str = "fp4", codes=None, scales=None):
-    """MX codes of X [rows x K].  Returns (codes uint8 [rows x K*w/8], scales uint8 E8M0 in step-major order)."""
+def vq_mx_quant(x: torch.Tensor, fmt: str = "fp4", codes=None, scales=None, had_block: int = 0,
+                exp_offset: int = 0):
+    """MX codes of X [rows x K].  Returns (codes uint8 [rows x K*w/8], scales uint8 E8M0 in step-major order).
+
+    had_block=128 rotates each row by the unnormalized 128-point block Hadamard transform
+    first (vq_mx_quant_rotated), scaled by 2^exp_offset (-7 for weights rotated offline)."""
     _dev(x, "x")
     rows, k = x.shape
     if codes is None:
-        codes = torch.empty((rows, k * _MX_BITS[fmt] // 8), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((rows, k * _MX_BITS.get(fmt, 8) // 8), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(max(vq_mx_scale_bytes(rows, k), 1), dtype=torch.uint8, device=x.device)
     if fmt in _MX:
         _buf(codes, "codes", vq_mx_code_bytes(rows, k, fmt), x.device)
         _buf(scales, "scales", vq_mx_scale_bytes(rows, k), x.device)
+    if had_block:
+        if had_block != VQ_HAD_BLOCK:
+            raise ValueError(f"had_block must be 0 or {VQ_HAD_BLOCK}")
+        _check("vq_mx_quant_rotated", _lib.vq_mx_quant_rotated(
+            _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), _MX.get(fmt, -1), exp_offset, _ptr(codes),
+            _ptr(scales), _stream(x)))
+        return codes, scales
     _check("vq_mx_quant", _lib.vq_mx_quant(
         _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), _MX.get(fmt, -1), _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales

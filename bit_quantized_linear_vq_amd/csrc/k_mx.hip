@@ -58,6 +58,7 @@ typedef _Float16 f16x32_t __attribute__((ext_vector_type(32)));
 typedef unsigned u32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x6_t __attribute__((ext_vector_type(6)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // One block: E8M0 exponent from its largest magnitude, scale byte, element codes.
 template <int DT, int FMT>
@@ -116,6 +117,80 @@ __device__ __forceinline__ void mxq_block(const unsigned (&d)[16], int64_t row, 
   }
 }
 
+// One block of float32 values (the rotated route): E8M0 exponent from the float32
+// largest magnitude, scale byte, element codes from the fp32-input conversions
+// (v_cvt_scalef32_pk_fp4_f32: two elements; v_cvt_scalef32_2xpk16_fp6_f32: the block).
+template <int FMT>
+__device__ __forceinline__ void mxq_block_f32(const float (&v)[32], int64_t row, int blk, int64_t rows8,
+                                              uint8_t* codes_row, uint8_t* scales) {
+  using F = MxFmt<FMT>;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+  const int ex = (int)((f_bits(m) >> 23) & 0xFF);
+  int e = ex == 0 ? -127 : ex - 127 - 2;  // floor(log2 max) - 2; zero or subnormal maxima clamp to -127
+  e = e < -127 ? -127 : e;
+  scales[((int64_t)(blk >> 1) * rows8 + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
+  const float sc = bits_f((unsigned)(e + 127) << 23);
+  u2v* dst = reinterpret_cast<u2v*>(codes_row + (int64_t)blk * (32 * F::W / 8));
+  if constexpr (FMT == MX_FP4) {
+    unsigned o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      unsigned r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 0], v[8 * q + 1], sc, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 2], v[8 * q + 3], sc, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 4], v[8 * q + 5], sc, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 6], v[8 * q + 7], sc, 3);
+      o[q] = r;
+    }
+    dst[0] = u2v{o[0], o[1]};
+    dst[1] = u2v{o[2], o[3]};
+  } else {
+    // The instruction interleaves its two sources (output element 2i from the first, 2i + 1
+    // from the second; lane-layout probe), and its destination must not overlap them: the
+    // compiler allocated overlapping registers for the builtin, and the result then held a
+    // value written before it was read.  Hence inline asm with an early-clobber output.
+    v16f ev, od;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ev[i] = v[2 * i];
+      od[i] = v[2 * i + 1];
+    }
+    u32x6_t o;
+    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(o) : "v"(ev), "v"(od), "v"(sc));
+    dst[0] = u2v{o[0], o[1]};
+    dst[1] = u2v{o[2], o[3]};
+    dst[2] = u2v{o[4], o[5]};
+  }
+}
+
+// 128-point block Hadamard rotation of the four 32-element blocks held by a lane quad
+// (lane q of the quad holds elements 32q .. 32q + 31 of the 128-element block): float32
+// butterflies with distances 1, 2, 4, 8, 16 inside the lane, then 32 and 64 across the
+// quad, each pair (i, i + h) becoming (z_i + z_{i+h}, z_i - z_{i+h}), in ascending order.
+// Across lanes the lower lane of a pair computes fl(mine + partner) and the upper lane
+// fl(partner - mine), both as one fma with the exact product mine * (+-1).
+__device__ __forceinline__ void fwht128_quad(float (&v)[32], int q) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  const float c32 = (q & 1) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], c32, dpp_f<0xB1>(v[i]));  // quad_perm [1,0,3,2]
+  const float c64 = (q & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], c64, dpp_f<0x4E>(v[i]));  // quad_perm [2,3,0,1]
+}
+
 // A wave takes tiles of 8 rows x 8 blocks (tile t: row group t / nbg, block group t % nbg,
 // nbg = ceil(nb / 8), nb = k / 32), so that the scale bytes it writes for one 64-deep step
 // are 16 contiguous bytes of the step-major layout (8 rows x 2 blocks).  The loads are
@@ -127,9 +202,12 @@ __device__ __forceinline__ void mxq_block(const unsigned (&d)[16], int64_t row, 
 // each block straight into its lane, 64 bytes per lane, measured 1.5x slower; 64
 // consecutive blocks of one row per wave wrote each step's scale bytes two at a time into
 // 32 different cache lines, 42% more bytes written than the codes and scales.)
-template <int DT, int FMT>
+// HAD: the rows are first rotated by 128-point Hadamard blocks (each a lane quad, K a
+// multiple of 128) and scaled by pscale (an exact power of two); the block scales then
+// come from the float32 rotated values.
+template <int DT, int FMT, bool HAD>
 __global__ __launch_bounds__(256) void k_mxquant(const void* x, int64_t ldx, int64_t rows, int k, int64_t rows8,
-                                                 uint8_t* codes, uint8_t* scales) {
+                                                 uint8_t* codes, uint8_t* scales, float pscale) {
   using F = MxFmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 4096];
   const int lane = threadIdx.x & 63;
@@ -174,7 +252,21 @@ __global__ __launch_bounds__(256) void k_mxquant(const void* x, int64_t ldx, int
     }
     const int64_t row = row0 + (lane >> 3);
     const int blk = blk0 + (lane & 7);
-    if (row < rows && blk < nb) mxq_block<DT, FMT>(d, row, blk, rows8, codes + row * row_bytes, scales);
+    if constexpr (HAD) {
+      // Every lane of the quad takes part in the butterflies (a quad lies entirely inside
+      // or entirely past the row's blocks; rows past the end hold zeros and are not stored).
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) decode2<DT>(d[i], v[2 * i], v[2 * i + 1]);
+      fwht128_quad(v, lane & 3);
+      if (pscale != 1.0f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] *= pscale;
+      }
+      if (row < rows && blk < nb) mxq_block_f32<FMT>(v, row, blk, rows8, codes + row * row_bytes, scales);
+    } else {
+      if (row < rows && blk < nb) mxq_block<DT, FMT>(d, row, blk, rows8, codes + row * row_bytes, scales);
+    }
     // LDS operations of one wave complete in order, so the next pass's writes cannot pass
     // these reads; this only keeps the compiler from moving them across.
     __builtin_amdgcn_wave_barrier();
@@ -583,17 +675,27 @@ using namespace vqk;
 int64_t mx_rows8(int64_t rows) { return (rows + 7) / 8 * 8; }
 
 hipError_t launch_mx_quant(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int fmt, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st) {
+                           uint8_t* scales, hipStream_t st, bool had, int exp_offset) {
   const int64_t tiles = (rows + 7) / 8 * ((k / 32 + 7) / 8);
   const int64_t wgs = (tiles + 3) / 4;  // four waves, one 8 x 8-block tile each, per workgroup and pass
   const unsigned grid = (unsigned)(wgs < 8192 ? wgs : 8192);
   const int64_t r8 = mx_rows8(rows);
-#define MXQ(DTV, FV) \
-  hipLaunchKernelGGL((k_mxquant<DTV, FV>), dim3(grid), dim3(256), 0, st, x, ldx, rows, (int)k, r8, codes, scales)
+  const float pscale = ldexpf(1.0f, exp_offset);  // exact: |exp_offset| <= 64
+#define MXQ(DTV, FV, H)                                                                                       \
+  hipLaunchKernelGGL((k_mxquant<DTV, FV, H>), dim3(grid), dim3(256), 0, st, x, ldx, rows, (int)k, r8, codes, \
+                     scales, pscale)
   if (dtype == DT_F16) {
-    if (fmt == MX_FP4) MXQ(DT_F16, MX_FP4); else MXQ(DT_F16, MX_FP6);
+    if (fmt == MX_FP4) {
+      if (had) MXQ(DT_F16, MX_FP4, true); else MXQ(DT_F16, MX_FP4, false);
+    } else {
+      if (had) MXQ(DT_F16, MX_FP6, true); else MXQ(DT_F16, MX_FP6, false);
+    }
   } else {
-    if (fmt == MX_FP4) MXQ(DT_BF16, MX_FP4); else MXQ(DT_BF16, MX_FP6);
+    if (fmt == MX_FP4) {
+      if (had) MXQ(DT_BF16, MX_FP4, true); else MXQ(DT_BF16, MX_FP4, false);
+    } else {
+      if (had) MXQ(DT_BF16, MX_FP6, true); else MXQ(DT_BF16, MX_FP6, false);
+    }
   }
 #undef MXQ
   return hipGetLastError();

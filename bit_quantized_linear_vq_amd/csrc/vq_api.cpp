@@ -362,6 +362,19 @@ vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64
   return hip_status(vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream));
 }
 
+vq_status vq_mx_quant_rotated(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt,
+                              int exp_offset, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (!x || !codes || !scales) return VQ_ERR_INVALID_ARG;
+  if (!is_16bit(dt)) return VQ_ERR_INVALID_ARG;
+  if (rows < 1 || k < 1 || rows >= kMaxDim || k >= kMaxDim || ldx < k) return VQ_ERR_INVALID_ARG;
+  if (exp_offset < -64 || exp_offset > 64) return VQ_ERR_INVALID_ARG;
+  if (!mx_fmt_ok(fmt)) return VQ_ERR_UNSUPPORTED;
+  if (k % VQ_HAD_BLOCK) return VQ_ERR_SHAPE;
+  if (!aligned16(x) || ldx % 8 || reinterpret_cast<uintptr_t>(codes) % 8) return VQ_ERR_SHAPE;
+  return hip_status(
+      vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream, true, exp_offset));
+}
+
 int64_t vq_mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 1 || n < 1 || k < 1 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % VQ_K_ALIGN) return 0;
   return vq_internal::mx_gemm_workspace_bytes(m, n, k);

@@ -298,6 +298,19 @@ int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt);
 int64_t vq_mx_scale_bytes(int64_t rows, int64_t k);
 vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt,
                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
+/*
+ * MX quantization of rotated rows: the 4-bit floating-point route with the online block
+ * Hadamard transform (6Bit-Diffusion, Methodology B.1).  Each row is first rotated by the
+ * unnormalized 128-point Sylvester Hadamard butterflies (float32, distances 1, 2, ..., 64
+ * in that order, as vq_hadamard_block with normalize = 0), scaled by 2^exp_offset
+ * (exact), and the float32 result is quantized as by vq_mx_quant (same layouts).
+ * Activations take exp_offset = 0; weights rotated offline take -7, so that the MX GEMM
+ * of the two returns sum_k (Hx)_k (Hw)_k / 128 = sum_k x_k w_k up to quantization.
+ *   x, codes, scales as for vq_mx_quant; k % 128 == 0; -64 <= exp_offset <= 64.
+ * Errors: INVALID_ARG, SHAPE (k % 128, alignment), UNSUPPORTED (fmt).
+ */
+vq_status vq_mx_quant_rotated(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt,
+                              int exp_offset, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 int64_t vq_mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const uint8_t* b,
                      const uint8_t* sb, vq_mx_fmt fb, int64_t m, int64_t n, int64_t k, void* y,

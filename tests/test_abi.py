@@ -308,6 +308,19 @@ def test_mx_quant_validation(lib, kw, want):
                            a["stream"]) == want
 
 
+def test_mx_quant_rotated_validation(lib):
+    def call(x=FAKE, dt=BF16, rows=64, k=256, ldx=256, fmt=MXFP4, off=0, codes=FAKE, scales=FAKE):
+        return lib.vq_mx_quant_rotated(x, dt, rows, k, ldx, fmt, off, codes, scales, NULL)
+    assert call(x=NULL) == INVALID
+    assert call(dt=F32) == INVALID
+    assert call(rows=0) == INVALID
+    assert call(ldx=128) == INVALID
+    assert call(off=65) == INVALID
+    assert call(fmt=3) == UNSUP
+    assert call(k=192, ldx=192) == SHAPE  # not a multiple of the 128-point block
+    assert call(codes=ctypes.c_void_p(0x10004)) == SHAPE
+
+
 @pytest.mark.parametrize("kw,want", [
     (dict(a=NULL), INVALID),
     (dict(sb=NULL), INVALID),

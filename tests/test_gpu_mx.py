@@ -125,8 +125,18 @@ def test_mx_gemm_within_float32_bound(vq, fa, m, n, k):
     check_gemm(y.cpu().numpy(), ac, asc, fa, bc, bsc)
 
 
+def ulp16(v, out):
+    """Spacing of the 16-bit output format at |v| (normal range; subnormal spacing below)."""
+    mant, emin = (7, -126) if out == torch.bfloat16 else (10, -14)
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
+    return np.exp2(e - mant)
+
+
 @pytest.mark.parametrize("out", [torch.bfloat16, torch.float16])
 def test_mx_gemm_16bit_outputs(vq, out):
+    """16-bit outputs against the oracle's exact sum: within the float32 accumulation bound
+    plus half a 16-bit ulp (one rounding of the float32 result), and equal to the device's
+    own float32 result rounded once."""
     m, n, k = 256, 256, 512
     x = rand_x(m, k, torch.bfloat16, 5)
     w = rand_x(n, k, torch.bfloat16, 6, spread=False)
@@ -135,8 +145,71 @@ def test_mx_gemm_16bit_outputs(vq, out):
     y32 = vq.vq_mx_gemm(ac_d, as_d, "fp4", bc_d, bs_d, "fp4", torch.float32)
     y16 = vq.vq_mx_gemm(ac_d, as_d, "fp4", bc_d, bs_d, "fp4", out)
     torch.cuda.synchronize()
-    # The 16-bit output is the float32 result rounded once (round to nearest even).
     assert torch.equal(y16, y32.to(out))
+    ac, asc = mx.quantize(numerics.to_f32(npb(x), "bf16"), "fp4")
+    bc, bsc = mx.quantize(numerics.to_f32(npb(w), "bf16"), "fp4")
+    exact = mx.gemm(ac, asc, "fp4", bc, bsc, "fp4")
+    mag = np.abs(mx.dequantize(ac, asc, "fp4")) @ np.abs(mx.dequantize(bc, bsc, "fp4")).T
+    bound = (k / 32 + 2) * 2.0 ** -24 * mag
+    got = y16.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - exact)
+    assert np.all(err <= bound + 0.5 * ulp16(np.abs(exact) + bound, out))
+
+
+# ------------------------------------------------------------------ rotated route
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp6"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("off", [0, -7])
+def test_mx_quant_rotated_bit_exact(vq, fmt, dtype, off):
+    """Rows rotated by the 128-point block Hadamard transform, scaled by 2^off, then MX codes
+    and scales: bit for bit against oracle/mx.quantize_rotated."""
+    m, k = 300, 640
+    x = rand_x(m, k, dtype, 23 + off)
+    codes, scales = vq.vq_mx_quant(x.to(DEV), fmt, had_block=128, exp_offset=off)
+    torch.cuda.synchronize()
+    name = "bf16" if dtype == torch.bfloat16 else "fp16"
+    rc, rs = mx.quantize_rotated(numerics.to_f32(npb(x), name), fmt, exp_offset=off)
+    assert np.array_equal(codes.cpu().numpy(), mx.pack(rc, fmt))
+    assert np.array_equal(device_scales(scales, m, k)[:, :m], step_major(rs, m)[:, :m])
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp6"])
+@pytest.mark.parametrize("m,k,pad", [(1, 128, 0), (3, 128, 64), (37, 384, 128), (9, 12288, 0), (1000, 1920, 0)])
+def test_mx_quant_rotated_shapes(vq, fmt, m, k, pad):
+    """Single rows, a single Hadamard block per row, rows whose block count leaves half a
+    wave tile (K = 384: 12 blocks), the widest rows, and a pitch wider than K."""
+    full = rand_x(m, k + pad, torch.bfloat16, 3 * m + k + pad)
+    x = full.to(DEV)[:, :k]
+    codes, scales = vq.vq_mx_quant(x, fmt, had_block=128)
+    torch.cuda.synchronize()
+    rc, rs = mx.quantize_rotated(numerics.to_f32(npb(full)[:, :k], "bf16"), fmt)
+    assert np.array_equal(codes.cpu().numpy(), mx.pack(rc, fmt))
+    assert np.array_equal(device_scales(scales, m, k)[:, :m], step_major(rs, m)[:, :m])
+
+
+@pytest.mark.parametrize("fa", ["fp4", "fp6"])
+def test_mx_gemm_rotated_operands(vq, fa):
+    """Rotated activations (offset 0) against weights rotated offline (offset -7): the MX GEMM
+    output within the float32 bound of the oracle's exact sum of the rotated operands, and
+    that sum close to the unrotated float64 product x . w^T."""
+    m, n, k = 257, 320, 1024
+    x = rand_x(m, k, torch.bfloat16, 61)
+    w = rand_x(n, k, torch.bfloat16, 62, spread=False)
+    ac_d, as_d = vq.vq_mx_quant(x.to(DEV), fa, had_block=128)
+    bc_d, bs_d = vq.vq_mx_quant(w.to(DEV), "fp4", had_block=128, exp_offset=-7)
+    y = vq.vq_mx_gemm(ac_d, as_d, fa, bc_d, bs_d, "fp4", torch.float32)
+    torch.cuda.synchronize()
+    xf, wf = numerics.to_f32(npb(x), "bf16"), numerics.to_f32(npb(w), "bf16")
+    ac, asc = mx.quantize_rotated(xf, fa)
+    bc, bsc = mx.quantize_rotated(wf, "fp4", exp_offset=-7)
+    exact = check_gemm(y.cpu().numpy(), ac, asc, fa, bc, bsc)
+    ref = xf.astype(np.float64) @ wf.astype(np.float64).T
+    # Sanity of the composition (rotation, offset -7, no 1/128 in the GEMM): the FP4 weights
+    # dominate the quantization error (about 0.1 relative here); a wrong offset would be off
+    # by a power of two (relative error >= 0.5).
+    rel = np.linalg.norm(exact - ref) / np.linalg.norm(ref)
+    assert rel < 0.25, rel
 
 
 def test_fullsize_w4a4_ffn_down_sampled_rows(vq):
