@@ -109,12 +109,58 @@ def test_fullsize_c4_standalone_hadamard(vq):
     assert np.array_equal(npb(y[torch.from_numpy(rows).to(DEV)]), onum.from_f32(ref, "bf16"))
 
 
-@pytest.mark.parametrize("layer", [0, 1])
-def test_fullsize_c5_routed_layer(vq, layer):
-    """One 3072 x 3072 layer of the routed batch on the full 35552-row CFG batch."""
+def oracle_route(layer):
+    xp, yp, _ = gen.make_route_pair(5, layer)
+    return oroute.route_bits(oroute.relative_l1(onum.to_f32(npb(xp), "bf16"), onum.to_f32(npb(yp), "bf16")))
+
+
+@pytest.mark.parametrize("layer,route", [(0, 4), (1, 4), (3, 8)])
+def test_fullsize_c5_routed_layer(vq, layer, route):
+    """One 3072 x 3072 layer of the routed batch on the full 35552-row CFG batch, with the
+    width read on the device from the route (layers 0 and 1 route to 4-bit activations,
+    layer 3, the first with Gamma above 0.1, to INT8)."""
     xp, yp, _ = gen.make_route_pair(5, layer)
     bits, gamma = vq.vq_route_rel_l1(xp.to(DEV), yp.to(DEV), 0.1, 8, 4)
     torch.cuda.synchronize()
-    want = oroute.route_bits(oroute.relative_l1(onum.to_f32(npb(xp), "bf16"), onum.to_f32(npb(yp), "bf16")))
-    assert bits.item() == want
+    want = oracle_route(layer)
+    assert want == route and bits.item() == want
     check_rows(vq, 5, gen.make_x(5), gen.make_w(5, layer=layer), want, 4, bits_dev=bits, seed=50 + layer)
+
+
+def test_fullsize_c5_routed_step_42_layers(vq):
+    """The whole routed step as the benchmark runs it: 42 layers on the 35552-row batch,
+    each routed on the device and quantized with the width read from the route, its GEMM
+    writing into one output buffer.  The first two layers of each route are checked on
+    sampled rows against the oracle; every route matches the oracle's."""
+    c = gen.CONFIGS[5]
+    x = gen.make_x(5)
+    xd = x.to(DEV)
+    m, k = x.shape
+    routes = [oracle_route(l) for l in range(c["layers"])]
+    checked = [l for l in range(c["layers"]) if routes[l] == 4][:2] + [l for l in range(c["layers"]) if routes[l] == 8][:2]
+    assert len(checked) == 4
+    rows = sample_rows(m, 500, 12)
+    rows_d = torch.from_numpy(rows).to(DEV)
+    codes = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    scales = torch.empty(m, dtype=torch.float32, device=DEV)
+    y = torch.empty((m, c["N"]), dtype=torch.bfloat16, device=DEV)
+    seen = {}
+    for layer in range(c["layers"]):
+        w = gen.make_w(5, layer=layer)
+        wc, ws = vq.vq_pack_weights(w.to(DEV), 4)
+        xp, yp, _ = gen.make_route_pair(5, layer)
+        bits, _ = vq.vq_route_rel_l1(xp.to(DEV), yp.to(DEV), 0.1, 8, 4)
+        vq.vq_quant_act(xd, 8, "token", bits_dev=bits, codes=codes, scales=scales)
+        vq.vq_qgemm_dequant(codes, scales, wc, ws, 4, y=y)
+        assert bits.item() == routes[layer], f"layer {layer}"
+        if layer in checked:
+            seen[layer] = (w, codes[rows_d].cpu().numpy(), scales[rows_d].cpu().numpy(), npb(y[rows_d]))
+    torch.cuda.synchronize()
+    for layer, (w, qa_got, sa_got, y_got) in seen.items():
+        bits = routes[layer]
+        rcodes, _, rws = oracle.linear.prepare_weights(npb(w), "bf16", 4)
+        qa, sa = oq.quant_act(npb(x)[rows], "bf16", bits, "token")
+        assert np.array_equal(qa_got, qa), f"layer {layer} codes"
+        assert np.array_equal(sa_got, sa), f"layer {layer} scales"
+        _, _, ys = ogemm.qgemm_dequant(qa, sa, True, rcodes, rws, k, "bf16")
+        assert np.array_equal(y_got, ys), f"layer {layer} outputs ({bits}-bit route)"
