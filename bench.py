@@ -16,8 +16,11 @@ Prints one JSON line.  ``value`` = 2*M*N*K integer operations per step / step ti
 average duration taken from HIP events recorded around each launch on the launch
 stream.  ``act_quant`` gives the quantization kernel against the 8 TB/s HBM peak, and,
 as ``stream_ref``, what a plain elementwise kernel moving the same bytes per element
-reaches on this part.  ``cpu_baseline`` times the CPU oracle on a bounded row sample of
-the same workload.
+reaches on this part.  ``side_kernels`` (default workload only) times the memory-bound
+kernels of the other workloads on their full tensors (standalone block Hadamard, fused
+rotation + 6-bit quantizer, dual-scale quantizer) against the same peak, and the latency
+of the tiny per-tensor layer in microseconds.  ``cpu_baseline`` times the CPU oracle on a
+bounded row sample of the same workload.
 """
 from __future__ import annotations
 
@@ -47,6 +50,9 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-side", action="store_true",
+                   help="skip the side measurements of the default run (block Hadamard, fused rotation + "
+                        "6-bit quantizer, dual-scale quantizer on their full tensors; tiny-layer latency)")
     p.add_argument("--graph", action="store_true",
                    help="replay one HIP graph per step instead of launching every kernel from the host "
                         "(measured about 10%% slower than host launches on this part)")
@@ -293,6 +299,102 @@ def cpu_baseline(cfg, budget_s):
     return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {x.shape[0]} rows of X against the full W (one layer), {dt:.1f} s; "
                       f"steps: activation quantization, exact integer GEMM (float64 BLAS), float32 epilogue"}
+
+
+def launches_us(fn, torch, stream, reps=40, warm=10):
+    """Average duration of one call of fn: `reps` calls back to back between two HIP
+    events on the launch stream (after `warm` untimed calls), divided by `reps`."""
+    for _ in range(warm):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def hbm_entry(kernel, workload, nbytes, us, note=None):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    e = {"kernel": kernel, "workload": workload, "bytes": int(nbytes), "avg_us": round(us, 2),
+         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if note:
+        e["note"] = note
+    return e
+
+
+def side_kernels(vq, gen, torch, dev, stream):
+    """The memory-bound kernels of the other workloads, timed beside the headline layer on
+    their full tensors, and the latency of the tiny per-tensor layer.
+
+    * the standalone 128-point block Hadamard (bf16 in, bf16 out) of the 17776 x 12288
+      FFN-down activations: 2 B read and 2 B written per element;
+    * the fused rotation + 6-bit per-token quantizer on the same tensor: 2 B read, 1 B of
+      code written per element, 4 B of scale per row;
+    * the dual-scale quantizer of the 17776 x 3072 FFN-up activations (outlier channels
+      from the weights' detection): 2 B read per element, 1 B per packed code (the outlier
+      partition padded to 64 codes), 8 B of scales per row;
+    * the 256 x 512 x 512 per-tensor W8A8 layer: one whole step (four quantization
+      launches: clear, maxima, codes, finalize; one GEMM) in microseconds, back to back on
+      the stream, synchronized one step at a time from the host, and replayed as a graph.
+    """
+    out = {}
+    x = gen.make_x(4).to(dev)
+    m, k = x.shape
+    y = torch.empty_like(x)
+    us = launches_us(lambda: vq.vq_hadamard_block(x, y=y), torch, stream, reps=20)
+    out["hadamard_c4"] = hbm_entry("k_hadamard", f"c4 activations {m} x {k} bf16 -> bf16, normalized", 4 * m * k, us)
+    del y
+    codes = torch.empty((m, k), dtype=torch.int8, device=dev)
+    scales = torch.empty(m, dtype=torch.float32, device=dev)
+    us = launches_us(lambda: vq.vq_quant_act(x, 6, "token", 128, codes=codes, scales=scales), torch, stream, reps=20)
+    out["fwht_quant_a6_c4"] = hbm_entry("k_rowquant (fused 128-point block Hadamard)",
+                                        f"c4 activations {m} x {k} bf16, 6-bit per token", 3 * m * k + 4 * m, us)
+    del x, codes, scales
+
+    x = gen.make_x(3).to(dev)
+    m, k = x.shape
+    w = gen.make_w(3).to(dev)
+    _, idx, _ = vq.vq_detect_outliers(w)
+    del w
+    idx = idx.to(dev)
+    kp = vq.vq_packed_k(k, int(idx.numel()))
+    codes = torch.empty((m, kp), dtype=torch.int8, device=dev)
+    scales = torch.empty((m, 2), dtype=torch.float32, device=dev)
+    us = launches_us(lambda: vq.vq_quant_act(x, 8, "token", 0, idx, codes=codes, scales=scales), torch, stream)
+    out["dual_quant_c3"] = hbm_entry("k_rowquant (dual scale)",
+                                     f"c3 activations {m} x {k} bf16, {int(idx.numel())} outlier channels, 8-bit",
+                                     2 * m * k + m * kp + 8 * m, us)
+    del x, codes, scales
+
+    L = Layer(1, vq, gen, torch, dev)
+
+    def step1():
+        L.quant(0, 0)
+        L.gemm(0)
+    stream_us = launches_us(step1, torch, stream, reps=200, warm=50)
+    walls = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        step1()
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - t0) * 1e6)
+    walls.sort()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step1()
+    stream.wait_stream(side)
+    graph_us = launches_us(g.replay, torch, stream, reps=200, warm=20)
+    out["c1_latency"] = {
+        "workload": "c1 256 x 512 x 512 W8A8, per-tensor activations, fp16", "unit": "us per step",
+        "stream_us": round(stream_us, 2), "graph_us": round(graph_us, 2),
+        "sync_median_us": round(walls[len(walls) // 2], 1), "bound": "latency",
+        "launches": 5, "ops": 2 * L.M * L.N * L.K}
+    return out
 
 
 def calibrate(args, vq, gen, torch, dev):
@@ -559,6 +661,8 @@ def main():
     if args.config == 5:
         out["config"]["routes_int8"] = L.routes.count(8)
         out["config"]["routes_int4"] = L.routes.count(4)
+    if args.config == 2 and not L.mx and not L.R and not args.no_side:
+        out["side_kernels"] = side_kernels(vq, gen, torch, dev, stream)
     if not args.no_cpu and not L.mx and not L.R:  # the oracle baseline is the plain integer layer
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(out), flush=True)
