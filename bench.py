@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--act-gran", choices=["token", "tensor", "static"], default=None,
+                   help="activation scale granularity instead of the workload's own: per token, per tensor "
+                        "(dynamic absmax: a maximum pass, then the code pass) or static per tensor (the scale "
+                        "found offline by the clipping-percentile search on the same activations)")
     p.add_argument("--no-side", action="store_true",
                    help="skip the side measurements of the default run (block Hadamard, fused rotation + "
                         "6-bit quantizer, dual-scale quantizer on their full tensors; tiny-layer latency)")
@@ -114,7 +118,7 @@ def load_traffic(workload):
 class Layer:
     """Device buffers and launch closures for one configuration."""
 
-    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0, mx=None):
+    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0, mx=None, gran=None):
         c = gen.CONFIGS[cfg]
         self.mx = mx
         self.cfg, self.c = cfg, c
@@ -125,7 +129,12 @@ class Layer:
         self.idx = None
         self.had = c["had"]
         self.a_bits = c["a_bits"] or 8
-        self.gran = c["gran"]
+        self.gran = gran or c["gran"]
+        self.static = None
+        if self.gran == "static":
+            if c["dual"] or c["had"]:
+                raise SystemExit("--act-gran static needs a workload without dual scale or rotation")
+            self.static = vq.vq_calib_static_scale(xd, self.a_bits)["scale"]
         self.layers = c.get("layers", 1)
         if cfg == 5:
             self.w = []
@@ -148,7 +157,7 @@ class Layer:
                         self.mx_w[l] = vq.vq_mx_quant(w, "fp4")
                         del w
         elif mx:
-            if c["dual"] or c["gran"] != "token":
+            if c["dual"] or self.gran != "token":
                 raise SystemExit("--mx needs a per-token workload without dual scale")
             w = gen.make_w(cfg).to(dev)
             # With the workload's block Hadamard, the activations are rotated online and the
@@ -210,7 +219,7 @@ class Layer:
         if self.use_mx(layer):
             self.vq.vq_mx_quant(x, self.mx_fmt, self.mx_codes, self.mx_scales, had_block=self.had if self.cfg != 5 else 0)
             return
-        self.vq.vq_quant_act(x, self.a_bits, self.gran, self.had, self.idx,
+        self.vq.vq_quant_act(x, self.a_bits, self.gran, self.had, self.idx, static_scale=self.static,
                              bits_dev=self.bits_dev[layer], codes=self.codes, scales=self.scales)
         if self.R:
             self.vq.vq_quant_residual(x, self.rows, self.a_bits, self.a_bits, self.codes2, self.scales2)
@@ -241,7 +250,10 @@ class Layer:
         # decomposed rows read their input once more and write K residual codes and a scale
         if self.mx and self.cfg != 5:  # MX: 2 B read, w/8 B of code and 1/32 B of scale written per element
             return self.M * self.K * 2 + self.mx_codes.numel() + self.M * self.K // 32
-        return (self.M * self.K * 2 + self.M * self.kp + self.scales.numel() * 4
+        # a dynamic per-tensor scale needs the whole tensor's maximum before any code: the
+        # tensor is read twice (a maximum pass, then the code pass)
+        reads = 2 if self.gran == "tensor" else 1
+        return (reads * self.M * self.K * 2 + self.M * self.kp + self.scales.numel() * 4
                 + self.R * (self.K * 2 + self.K + 4))
 
 
@@ -267,8 +279,9 @@ def stream_reference(L, torch, stream, reps=20):
             "avg_us": round(us, 2), "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s"}
 
 
-def cpu_baseline(cfg, budget_s):
-    """The CPU oracle, as it stands, on a bounded row sample of the workload."""
+def cpu_baseline(cfg, budget_s, gran=None, static=None):
+    """The CPU oracle, as it stands, on a bounded row sample of the workload (a per-tensor
+    granularity takes each 256-row chunk as the tensor)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -276,6 +289,7 @@ def cpu_baseline(cfg, budget_s):
     import oracle
 
     c = gen.CONFIGS[cfg]
+    gran = gran or c["gran"]
     if cfg == 5:
         w = gen.make_w(cfg, layer=0)
     else:
@@ -291,7 +305,8 @@ def cpu_baseline(cfg, budget_s):
     t0 = time.perf_counter()
     while rows < x.shape[0] and time.perf_counter() - t0 < budget_s:
         xs = x[rows:rows + chunk]
-        oracle.linear.forward(xs, c["dtype"], c["a_bits"] or 8, c["gran"], wcodes, wscales, c["had"], idx)
+        oracle.linear.forward(xs, c["dtype"], c["a_bits"] or 8, gran, wcodes, wscales, c["had"], idx,
+                              static_scale=static)
         rows += xs.shape[0]
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -301,11 +316,18 @@ def cpu_baseline(cfg, budget_s):
                       f"steps: activation quantization, exact integer GEMM (float64 BLAS), float32 epilogue"}
 
 
-def launches_us(fn, torch, stream, reps=40, warm=10):
+def launches_us(fn, torch, stream, reps=50, warm=100, warm_s=0.05):
     """Average duration of one call of fn: `reps` calls back to back between two HIP
-    events on the launch stream (after `warm` untimed calls), divided by `reps`."""
-    for _ in range(warm):
-        fn()
+    events on the launch stream, divided by `reps`.  Untimed calls come first, at least
+    `warm` of them and at least `warm_s` seconds of them: after an idle spell the part
+    runs its first tens of milliseconds of work more slowly."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < warm or time.perf_counter() - t0 < warm_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        done += 10
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(reps):
@@ -324,7 +346,7 @@ def hbm_entry(kernel, workload, nbytes, us, note=None):
     return e
 
 
-def side_kernels(vq, gen, torch, dev, stream):
+def side_kernels(vq, gen, torch, dev, stream, head):
     """The memory-bound kernels of the other workloads, timed beside the headline layer on
     their full tensors, and the latency of the tiny per-tensor layer.
 
@@ -335,20 +357,38 @@ def side_kernels(vq, gen, torch, dev, stream):
     * the dual-scale quantizer of the 17776 x 3072 FFN-up activations (outlier channels
       from the weights' detection): 2 B read per element, 1 B per packed code (the outlier
       partition padded to 64 codes), 8 B of scales per row;
-    * the 256 x 512 x 512 per-tensor W8A8 layer: one whole step (four quantization
-      launches: clear, maxima, codes, finalize; one GEMM) in microseconds, back to back on
-      the stream, synchronized one step at a time from the host, and replayed as a graph.
+    * per-tensor activation scales on the 17776 x 1920 fused-QKV activations: dynamic (a
+      maximum pass, then the code pass: 2 B read twice, 1 B written per element) and
+      static (the clipping-percentile scale found offline: 2 B read, 1 B written);
+    * the 256 x 512 x 512 per-tensor W8A8 layer: one whole step (the one-launch per-tensor
+      quantizer, then the GEMM) in microseconds, back to back on the stream, synchronized
+      one step at a time from the host, and replayed as a graph.
     """
     out = {}
+    x = head.x[0]
+    m, k = x.shape
+    codes = torch.empty((m, k), dtype=torch.int8, device=dev)
+    scales = torch.empty(1, dtype=torch.float32, device=dev)
+    us = launches_us(lambda: vq.vq_quant_act(x, 8, "tensor", codes=codes, scales=scales), torch, stream)
+    out["per_tensor_quant_c2"] = hbm_entry("k_fill_u32 + k_rowquant (maximum pass) + k_rowquant (codes) + "
+                                           "k_tensor_finalize", f"c2 activations {m} x {k} bf16, dynamic per tensor",
+                                           5 * m * k + 4, us)
+    static = vq.vq_calib_static_scale(x, 8)["scale"]
+    us = launches_us(lambda: vq.vq_quant_act(x, 8, "static", static_scale=static, codes=codes, scales=scales),
+                     torch, stream)
+    out["static_quant_c2"] = hbm_entry("k_rowquant (static scale) + k_tensor_finalize",
+                                       f"c2 activations {m} x {k} bf16, static per tensor", 3 * m * k + 4, us)
+    del codes, scales
+
     x = gen.make_x(4).to(dev)
     m, k = x.shape
     y = torch.empty_like(x)
-    us = launches_us(lambda: vq.vq_hadamard_block(x, y=y), torch, stream, reps=20)
+    us = launches_us(lambda: vq.vq_hadamard_block(x, y=y), torch, stream)
     out["hadamard_c4"] = hbm_entry("k_hadamard", f"c4 activations {m} x {k} bf16 -> bf16, normalized", 4 * m * k, us)
     del y
     codes = torch.empty((m, k), dtype=torch.int8, device=dev)
     scales = torch.empty(m, dtype=torch.float32, device=dev)
-    us = launches_us(lambda: vq.vq_quant_act(x, 6, "token", 128, codes=codes, scales=scales), torch, stream, reps=20)
+    us = launches_us(lambda: vq.vq_quant_act(x, 6, "token", 128, codes=codes, scales=scales), torch, stream)
     out["fwht_quant_a6_c4"] = hbm_entry("k_rowquant (fused 128-point block Hadamard)",
                                         f"c4 activations {m} x {k} bf16, 6-bit per token", 3 * m * k + 4 * m, us)
     del x, codes, scales
@@ -373,7 +413,7 @@ def side_kernels(vq, gen, torch, dev, stream):
     def step1():
         L.quant(0, 0)
         L.gemm(0)
-    stream_us = launches_us(step1, torch, stream, reps=200, warm=50)
+    stream_us = launches_us(step1, torch, stream, reps=200, warm=200)
     walls = []
     for _ in range(200):
         t0 = time.perf_counter()
@@ -388,12 +428,12 @@ def side_kernels(vq, gen, torch, dev, stream):
         with torch.cuda.graph(g, stream=side):
             step1()
     stream.wait_stream(side)
-    graph_us = launches_us(g.replay, torch, stream, reps=200, warm=20)
+    graph_us = launches_us(g.replay, torch, stream, reps=200, warm=50)
     out["c1_latency"] = {
         "workload": "c1 256 x 512 x 512 W8A8, per-tensor activations, fp16", "unit": "us per step",
         "stream_us": round(stream_us, 2), "graph_us": round(graph_us, 2),
         "sync_median_us": round(walls[len(walls) // 2], 1), "bound": "latency",
-        "launches": 5, "ops": 2 * L.M * L.N * L.K}
+        "launches": 2, "ops": 2 * L.M * L.N * L.K}
     return out
 
 
@@ -538,7 +578,7 @@ def main():
     if args.control:
         control(args, vq, gen, torch, dev)
         return
-    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx)
+    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx, args.act_gran)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -612,6 +652,9 @@ def main():
     if L.R:
         workload += f"+decompose_{L.R}_tokens"
         traffic = q_traffic = None  # the counter runs cover the plain layer only
+    if L.gran != gen.CONFIGS[args.config]["gran"]:
+        workload += "+act_" + {"token": "per_token", "tensor": "per_tensor", "static": "static_per_tensor"}[L.gran]
+        traffic = q_traffic = None  # the counter runs cover the workload's own granularity
     if L.mx:
         workload += "+mx_" + ("fp4_route" if args.config == 5 else f"{L.mx_fmt}_act_fp4_weights")
         traffic = q_traffic = None
@@ -656,15 +699,21 @@ def main():
         out["config"]["decomposed_tokens"] = L.R
         out["roofline"]["kernel"] = "k_qgemm over all rows + k_qgemm over the stacked residual rows + k_residual_merge"
         out["act_quant"]["kernel"] = "k_rowquant + k_residual_quant"
-    if not L.mx and not L.R and args.config != 5:
+    if L.gran == "tensor":
+        out["act_quant"]["kernel"] = ("k_fill_u32 + k_rowquant (maximum pass) + k_rowquant (codes) + k_tensor_finalize"
+                                      if L.M * L.K > 1 << 18 else "k_tensorquant_small (one launch)")
+    elif L.gran == "static":
+        out["act_quant"]["kernel"] = "k_rowquant (static scale) + k_tensor_finalize"
+    if not L.mx and not L.R and args.config != 5 and L.gran == "token":
         out["act_quant"]["stream_ref"] = stream_reference(L, torch, stream)
     if args.config == 5:
         out["config"]["routes_int8"] = L.routes.count(8)
         out["config"]["routes_int4"] = L.routes.count(4)
-    if args.config == 2 and not L.mx and not L.R and not args.no_side:
-        out["side_kernels"] = side_kernels(vq, gen, torch, dev, stream)
+    if args.config == 2 and not L.mx and not L.R and not args.act_gran and not args.no_side:
+        out["side_kernels"] = side_kernels(vq, gen, torch, dev, stream, L)
     if not args.no_cpu and not L.mx and not L.R:  # the oracle baseline is the plain integer layer
-        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds, L.gran,
+                                           None if L.static is None else L.static.cpu().numpy())
     print(json.dumps(out), flush=True)
 
 

@@ -359,6 +359,127 @@ __global__ void k_tensor_finalize(float* scales, const float* static_src, int pa
   }
 }
 
+// Dynamic per-tensor quantization of a small tensor in one launch.  Every workgroup
+// reduces the whole tensor's absolute maximum by itself (a maximum is exact in any order,
+// so all workgroups find the same value), derives r = fl32(Q/a) and s = fl32(a/Q) as the
+// two-pass path does, and quantizes its own range of 8-element pieces; workgroup 0 stores
+// s.  No clearing, no atomics and no finalizing launch: at a few hundred KB the launches
+// of the two-pass path cost more than the redundant reads, which the L2 serves.
+constexpr int SMALL_THREADS = 1024;
+constexpr int SMALL_UNROLL = 8;
+
+template <int DT>
+__global__ __launch_bounds__(SMALL_THREADS) void k_tensorquant_small(const void* x, int64_t ldx, int rows, int k,
+                                                                     int qbits, const int32_t* bits_dev,
+                                                                     int8_t* codes, float* scales) {
+  __shared__ float s_red[SMALL_THREADS / 64];
+  const int ppr = k / 8;  // pieces per row
+  const int n = rows * ppr;
+  const int tid = threadIdx.x;
+  auto load = [&](int i) {
+    const int r = i / ppr;
+    const int c = i - r * ppr;
+    return *reinterpret_cast<const u4v*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)r * ldx + 8 * c);
+  };
+  float m = 0.0f;
+  for (int i0 = 0; i0 < n; i0 += SMALL_THREADS * SMALL_UNROLL) {
+    u4v w[SMALL_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SMALL_UNROLL; ++u) {
+      const int i = i0 + u * SMALL_THREADS + tid;
+      w[u] = load(i < n ? i : 0);  // piece 0 again past the end: cannot raise the maximum
+    }
+#pragma unroll
+    for (int u = 0; u < SMALL_UNROLL; ++u) {
+      float v[8];
+      decode8<DT>(w[u], v);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+    }
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  float amax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < SMALL_THREADS / 64; ++w) amax = fmaxf(amax, s_red[w]);
+
+  int b = bits_dev ? *bits_dev : qbits;
+  b = (b == 4 || b == 6) ? b : 8;
+  const float qf = (float)((1 << (b - 1)) - 1);
+  float r, sc;
+  dyn_scale(amax, qf, r, sc);
+
+  const int per = (n + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int lo = (int)blockIdx.x * per;
+  const int hi = min(n, lo + per);
+  for (int i = lo + tid; i < hi; i += SMALL_THREADS) {
+    float v[8];
+    decode8<DT>(load(i), v);
+    unsigned u[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) u[t] = qbyte(v[t], r, qf);
+    const int row = i / ppr;
+    *reinterpret_cast<u2v*>(codes + (int64_t)row * k + 8 * (i - row * ppr)) =
+        u2v{pack4_lo(u[0], u[1], u[2], u[3]), pack4_lo(u[4], u[5], u[6], u[7])};
+  }
+  if (blockIdx.x == 0 && tid == 0) scales[0] = sc;
+}
+
+// Absolute maximum of a whole tensor (no outlier partition, no rotation) for the dynamic
+// per-tensor scale: a flat grid-stride pass over 8-element pieces with eight 16-byte loads
+// in flight per lane, one workgroup of 1024 lanes per CU and one atomic maximum per
+// workgroup (non-negative floats order like their bit patterns).  The row-structured
+// maximum pass needs a row's loads per wave and thousands of workgroups, each ending in
+// an atomic on the same word.
+constexpr int AMAX_THREADS = 1024;
+constexpr int AMAX_UNROLL = 8;
+
+template <int DT, bool CONTIG>
+__global__ __launch_bounds__(AMAX_THREADS) void k_tensor_absmax(const void* x, int64_t ldx, int rows, int k,
+                                                                unsigned* maxbits) {
+  __shared__ float s_red[AMAX_THREADS / 64];
+  const int ppr = k / 8;
+  const int n = rows * ppr;
+  const int stride = (int)gridDim.x * AMAX_THREADS;
+  const int tid = threadIdx.x;
+  auto load = [&](int i) {
+    int64_t off;
+    if constexpr (CONTIG) {
+      off = (int64_t)i * 8;
+    } else {
+      const int r = i / ppr;
+      off = (int64_t)r * ldx + 8 * (i - r * ppr);
+    }
+    return __builtin_nontemporal_load(reinterpret_cast<const u4v*>(reinterpret_cast<const uint16_t*>(x) + off));
+  };
+  float m = 0.0f;
+  for (int i0 = (int)blockIdx.x * AMAX_THREADS + tid; i0 < n; i0 += stride * AMAX_UNROLL) {
+    u4v w[AMAX_UNROLL];
+#pragma unroll
+    for (int u = 0; u < AMAX_UNROLL; ++u) {
+      const int i = i0 + u * stride;
+      w[u] = load(i < n ? i : i0);  // piece i0 again past the end: cannot raise the maximum
+    }
+#pragma unroll
+    for (int u = 0; u < AMAX_UNROLL; ++u) {
+      float v[8];
+      decode8<DT>(w[u], v);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+    }
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float b = 0.0f;
+#pragma unroll
+    for (int w = 0; w < AMAX_THREADS / 64; ++w) b = fmaxf(b, s_red[w]);
+    atomicMax(maxbits, f_bits(b));
+  }
+}
+
 template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
 static hipError_t launch_row(const RowArgs& a, int grid, int block, hipStream_t st) {
   // The pass count is a compile-time constant so that a lane holds exactly its passes.
@@ -447,6 +568,56 @@ hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st) {
     case DT_BF16: return dispatch_dt<DT_BF16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, grid, block, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+int64_t tensor_small_max_elems() { return (int64_t)1 << 18; }
+
+hipError_t launch_tensor_small(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int bits,
+                               const int32_t* bits_dev, int8_t* codes, float* scales, hipStream_t st) {
+  if (rows * k > tensor_small_max_elems() || k % 8) return hipErrorInvalidValue;
+  // About four pieces per thread in the code pass, at most 16 workgroups re-reading the tensor.
+  const int64_t pieces = rows * (k / 8);
+  int grid = (int)((pieces + 4 * SMALL_THREADS - 1) / (4 * SMALL_THREADS));
+  grid = grid < 1 ? 1 : grid > 16 ? 16 : grid;
+  switch (dtype) {
+    case DT_F16:
+      hipLaunchKernelGGL(k_tensorquant_small<DT_F16>, dim3(grid), dim3(SMALL_THREADS), 0, st, x, ldx, (int)rows,
+                         (int)k, bits, bits_dev, codes, scales);
+      break;
+    case DT_BF16:
+      hipLaunchKernelGGL(k_tensorquant_small<DT_BF16>, dim3(grid), dim3(SMALL_THREADS), 0, st, x, ldx, (int)rows,
+                         (int)k, bits, bits_dev, codes, scales);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int64_t tensor_absmax_max_pieces() { return (int64_t)1 << 30; }  // 32-bit piece indices
+
+hipError_t launch_tensor_absmax(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, unsigned* maxbits,
+                                hipStream_t st) {
+  const int64_t pieces = rows * (k / 8);
+  if (k % 8 || pieces > tensor_absmax_max_pieces()) return hipErrorInvalidValue;
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    return n;
+  }();
+  int64_t grid = (pieces + (int64_t)AMAX_THREADS * AMAX_UNROLL - 1) / ((int64_t)AMAX_THREADS * AMAX_UNROLL);
+  grid = grid < 1 ? 1 : grid > cus ? cus : grid;
+  const bool contig = ldx == k;
+  const int r = (int)rows, kk = (int)k;
+#define VQ_AMAX(D, C) hipLaunchKernelGGL((k_tensor_absmax<D, C>), dim3((int)grid), dim3(AMAX_THREADS), 0, st, x, ldx, r, kk, maxbits)
+  switch (dtype) {
+    case DT_F16: if (contig) VQ_AMAX(DT_F16, true); else VQ_AMAX(DT_F16, false); break;
+    case DT_BF16: if (contig) VQ_AMAX(DT_BF16, true); else VQ_AMAX(DT_BF16, false); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef VQ_AMAX
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st) {

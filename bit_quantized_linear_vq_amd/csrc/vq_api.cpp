@@ -178,11 +178,18 @@ vq_status vq_quant_act(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t
     return hip_status(vq_internal::launch_row_quant(p, stream));
   }
   if (gran == VQ_PER_TENSOR) {
+    if (parts == 1 && !had_block && m * k <= vq_internal::tensor_small_max_elems())
+      return hip_status(vq_internal::launch_tensor_small(x, (int)dt, ldx, m, k, bits, bits_dev, codes, scales,
+                                                         stream));
     e = vq_internal::launch_fill_u32(reinterpret_cast<unsigned*>(scales), parts, 0u, stream);
     if (e != hipSuccess) return hip_status(e);
-    vq_internal::RowQuantParams q = p;
-    q.maxonly = true;
-    e = vq_internal::launch_row_quant(q, stream);
+    if (parts == 1 && !had_block && m * (k / 8) <= vq_internal::tensor_absmax_max_pieces()) {
+      e = vq_internal::launch_tensor_absmax(x, (int)dt, ldx, m, k, reinterpret_cast<unsigned*>(scales), stream);
+    } else {
+      vq_internal::RowQuantParams q = p;
+      q.maxonly = true;
+      e = vq_internal::launch_row_quant(q, stream);
+    }
     if (e != hipSuccess) return hip_status(e);
     p.mode = 1;
     p.gsrc = scales;

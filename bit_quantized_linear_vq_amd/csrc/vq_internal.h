@@ -31,6 +31,16 @@ struct RowQuantParams {
 int row_quant_max_k();
 hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st);
+// Dynamic per-tensor quantization of at most tensor_small_max_elems() elements in one launch
+// (no outlier partition, no rotation, int8 code rows of length k).
+int64_t tensor_small_max_elems();
+// Atomic maximum of |x| over a whole tensor of at most tensor_absmax_max_pieces() 8-element
+// pieces into *maxbits (float bit pattern, cleared by the caller).
+int64_t tensor_absmax_max_pieces();
+hipError_t launch_tensor_absmax(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, unsigned* maxbits,
+                                hipStream_t st);
+hipError_t launch_tensor_small(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int bits,
+                               const int32_t* bits_dev, int8_t* codes, float* scales, hipStream_t st);
 hipError_t launch_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
                                   const int32_t* bits_dev, hipStream_t st);
 

@@ -87,6 +87,37 @@ def test_quant_per_tensor_c1_full(vq):
     assert_same(scales.cpu().numpy(), rs, "scale")
 
 
+@pytest.mark.parametrize("m,k,dt,bits,pitch", [
+    (1, 64, "fp16", 8, 0),       # one piece row: the smallest tensor
+    (3, 192, "bf16", 6, 0),
+    (70, 512, "bf16", 4, 64),    # rows with a wider pitch than K
+    (512, 512, "fp16", 8, 0),    # 2^18 elements: the largest one-launch tensor
+    (513, 512, "fp16", 8, 0),    # one row more: the two-pass path
+    (600, 1024, "bf16", 6, 0),   # the flat maximum pass over contiguous rows
+    (700, 1024, "fp16", 8, 128), # ... and over rows with a wider pitch
+])
+def test_quant_per_tensor_one_launch_and_two_pass(vq, m, k, dt, bits, pitch):
+    """Dynamic per-tensor scales: tensors of at most 2^18 elements are quantized in one
+    launch (every workgroup reduces the whole maximum), larger ones by a maximum pass and
+    a code pass; both must give the oracle's codes and scale, also with the width read
+    from the device."""
+    g = np.random.default_rng(m * 7 + k)
+    x32 = g.standard_normal((m, k + pitch)).astype(np.float32)
+    x32[g.integers(0, m), g.integers(0, k)] = 9.0  # one large element sets the scale
+    xs = gen.to_storage(x32, dt)
+    xv = xs.to(DEV)[:, :k]
+    for bd in (None, torch.tensor([bits], dtype=torch.int32, device=DEV)):
+        codes, scales = vq.vq_quant_act(xv, 8 if bd is not None else bits, "tensor", bits_dev=bd)
+        torch.cuda.synchronize()
+        rc, rs = oq.quant_act(npb(xs)[:, :k], dt, bits, "tensor")
+        assert_same(codes.cpu().numpy(), rc, f"codes ({'device' if bd is not None else 'host'} width)")
+        assert_same(scales.cpu().numpy(), rs, "scale")
+    zero = torch.zeros((m, k), dtype=xs.dtype, device=DEV)
+    codes, scales = vq.vq_quant_act(zero, bits, "tensor")
+    torch.cuda.synchronize()
+    assert not codes.any() and scales.item() == 0.0
+
+
 def test_quant_static_scale(vq):
     x = gen.make_x(1)
     s = torch.tensor([0.05], dtype=torch.float32)
