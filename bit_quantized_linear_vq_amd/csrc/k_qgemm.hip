@@ -793,6 +793,89 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Few-tile layers (int8 weights, no outlier partition): a 256 x 256 tile per CU would leave
+// the part nearly idle and run every 64-code stage at the latency of the LDS ring, so each
+// wave computes one 32 x 32 output block on its own, with its A and B fragments loaded
+// straight from global memory into registers (16 codes per lane and operand per 32-deep
+// MFMA, two batches of SMALL_KB steps in flight), no LDS and no barriers.
+// Each workgroup is one wave, so the blocks spread over as many CUs as there are blocks
+// (the operand loads of a 32-row fragment touch 32 lines each and are the per-CU cost).
+// The scales are requested before the K loop.  Epilogue arithmetic as in the tiled kernels.
+constexpr int SMALL_KB = 8;           // 32-deep steps per load batch
+constexpr int SMALL_MAX_TILES = 16;   // 256 x 256 tiles up to which this kernel is taken
+
+template <int OUT_DT>
+__global__ __launch_bounds__(64) void k_qgemm_small(GArgs g) {
+  const int lane = threadIdx.x;
+  const int m0 = blockIdx.x * 32;
+  const int n0 = blockIdx.y * 32;
+  const int rl = lane & 31, kc = lane >> 5;
+  // Scales first: their latency hides behind the K loop.
+  const int m = m0 + rl;
+  const float sa0 = g.sa_tok ? g.sa[min(m, g.m - 1)] : g.sa[0];
+  float sbv[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sbv[q][r] = g.sb[min(n0 + 8 * q + 4 * kc + r, g.n - 1)];
+  const int8_t* pa = g.a + (int64_t)min(m0 + rl, g.m - 1) * g.kp + 16 * kc;
+  const uint8_t* pb = g.b + (int64_t)min(n0 + rl, g.n - 1) * g.kp + 16 * kc;
+  const int nks = g.k0 / 32;
+  v16i acc = v16i{};
+  v4i fa[2][SMALL_KB], fb[2][SMALL_KB];
+  auto load = [&](int set, int kb) {
+#pragma unroll
+    for (int u = 0; u < SMALL_KB; ++u) {
+      const int ks = min(kb * SMALL_KB + u, nks - 1);  // past the end: a valid step, not used
+      fa[set][u] = *reinterpret_cast<const v4i*>(pa + 32 * ks);
+      fb[set][u] = *reinterpret_cast<const v4i*>(pb + 32 * ks);
+    }
+  };
+  auto mma = [&](int set, int kb) {
+#pragma unroll
+    for (int u = 0; u < SMALL_KB; ++u)
+      if (kb * SMALL_KB + u < nks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][u], fa[set][u], acc, 0, 0, 0);
+  };
+  const int nkb = (nks + SMALL_KB - 1) / SMALL_KB;
+  load(0, 0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    if (kb + 1 < nkb) load(1, kb + 1);
+    mma(0, kb);
+    if (kb + 2 < nkb) load(0, kb + 2);
+    if (kb + 1 < nkb) mma(1, kb + 1);
+  }
+
+  if (m >= g.m) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = n0 + 8 * q + 4 * kc;
+    if (n >= g.n) continue;
+    const int cnt = min(4, g.n - n);
+    float out[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a0 = acc[4 * q + r];
+      const float t0 = sa0 * sbv[q][r];
+      out[r] = (float)a0 * t0;
+      if (g.accd && r < cnt) g.accd[(int64_t)m * g.n + n + r] = a0;
+    }
+    if constexpr (OUT_DT == DT_F32) {
+      store4_f32(g.y, (int64_t)m * g.ldy + n, out, cnt, g.vec_store != 0);
+    } else {
+      typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+      const unsigned p0 = cvt_pair<OUT_DT>(out[0], out[1]), p1 = cvt_pair<OUT_DT>(out[2], out[3]);
+      h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + n;
+      if (g.vec_store && cnt == 4) {
+        *reinterpret_cast<u2v*>(dst) = u2v{p0, p1};
+      } else {
+        for (int e = 0; e < cnt; ++e)
+          dst[e] = __builtin_bit_cast(h_t, (unsigned short)((e < 2 ? p0 : p1) >> (16 * (e & 1))));
+      }
+    }
+  }
+}
+
 template <int BBITS, int OUT_DT>
 static hipError_t launch_dual(const GArgs& a, bool dual, int grid, hipStream_t st) {
   const int part = a.kp - a.k0;
@@ -873,6 +956,15 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.ws_part = split > 1 ? reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(p.ws) + QGEMM_WS_COUNTERS) : nullptr;
   const int grid = a.items < pb ? a.items : pb;
   const bool dual = p.k0 < p.kp;
+  if (p.b_bits == 8 && !dual && tiles <= SMALL_MAX_TILES) {
+    const dim3 sg((unsigned)((p.m + 31) / 32), (unsigned)((p.n + 31) / 32));
+    switch (p.out_dt) {
+      case DT_F16: hipLaunchKernelGGL(k_qgemm_small<DT_F16>, sg, dim3(64), 0, st, a); break;
+      case DT_BF16: hipLaunchKernelGGL(k_qgemm_small<DT_BF16>, sg, dim3(64), 0, st, a); break;
+      default: hipLaunchKernelGGL(k_qgemm_small<DT_F32>, sg, dim3(64), 0, st, a); break;
+    }
+    return hipGetLastError();
+  }
   if (p.b_bits == 8 && !dual && split == 1) {
     switch (p.out_dt) {
       case DT_F16: hipLaunchKernelGGL(k_qgemm_pp<DT_F16>, dim3(grid), dim3(NT), 0, st, a); break;

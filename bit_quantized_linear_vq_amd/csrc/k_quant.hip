@@ -363,12 +363,16 @@ __global__ void k_tensor_finalize(float* scales, const float* static_src, int pa
 // reduces the whole tensor's absolute maximum by itself (a maximum is exact in any order,
 // so all workgroups find the same value), derives r = fl32(Q/a) and s = fl32(a/Q) as the
 // two-pass path does, and quantizes its own range of 8-element pieces; workgroup 0 stores
-// s.  No clearing, no atomics and no finalizing launch: at a few hundred KB the launches
-// of the two-pass path cost more than the redundant reads, which the L2 serves.
+// s.  Each workgroup starts its pass at its own range, so the pieces it quantizes are
+// among its first loads and are still in registers when the maximum is known: one memory
+// latency for the whole kernel.  No clearing, no atomics and no finalizing launch: at a few
+// hundred KB the launches of the two-pass path cost more than the redundant reads, which
+// the L2 serves.
 constexpr int SMALL_THREADS = 1024;
 constexpr int SMALL_UNROLL = 8;
+constexpr int SMALL_MAX_GRID = 16;
 
-template <int DT>
+template <int DT, bool CONTIG>
 __global__ __launch_bounds__(SMALL_THREADS) void k_tensorquant_small(const void* x, int64_t ldx, int rows, int k,
                                                                      int qbits, const int32_t* bits_dev,
                                                                      int8_t* codes, float* scales) {
@@ -376,18 +380,34 @@ __global__ __launch_bounds__(SMALL_THREADS) void k_tensorquant_small(const void*
   const int ppr = k / 8;  // pieces per row
   const int n = rows * ppr;
   const int tid = threadIdx.x;
+  const int per = (n + (int)gridDim.x - 1) / (int)gridDim.x;  // at most SMALL_THREADS * SMALL_UNROLL
+  const int lo = min(n, (int)blockIdx.x * per);
+  const int hi = min(n, lo + per);
+  auto piece_of = [&](int j) {  // j-th piece of this workgroup's pass (j < n): starts at lo, wraps
+    const int i = lo + j;
+    return i < n ? i : i - n;
+  };
   auto load = [&](int i) {
-    const int r = i / ppr;
-    const int c = i - r * ppr;
-    return *reinterpret_cast<const u4v*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)r * ldx + 8 * c);
+    int64_t off = (int64_t)i * 8;
+    if constexpr (!CONTIG) {
+      const int r = i / ppr;
+      off = (int64_t)r * ldx + 8 * (i - r * ppr);
+    }
+    return *reinterpret_cast<const u4v*>(reinterpret_cast<const uint16_t*>(x) + off);
   };
   float m = 0.0f;
-  for (int i0 = 0; i0 < n; i0 += SMALL_THREADS * SMALL_UNROLL) {
+  u4v own[SMALL_UNROLL];  // the first batch: this workgroup's own pieces
+#pragma unroll
+  for (int u = 0; u < SMALL_UNROLL; ++u) {
+    const int j = u * SMALL_THREADS + tid;
+    own[u] = load(piece_of(j < n ? j : 0));
+  }
+  for (int j0 = SMALL_THREADS * SMALL_UNROLL; j0 < n; j0 += SMALL_THREADS * SMALL_UNROLL) {
     u4v w[SMALL_UNROLL];
 #pragma unroll
     for (int u = 0; u < SMALL_UNROLL; ++u) {
-      const int i = i0 + u * SMALL_THREADS + tid;
-      w[u] = load(i < n ? i : 0);  // piece 0 again past the end: cannot raise the maximum
+      const int j = j0 + u * SMALL_THREADS + tid;
+      w[u] = load(piece_of(j < n ? j : 0));  // a piece loaded again cannot raise the maximum
     }
 #pragma unroll
     for (int u = 0; u < SMALL_UNROLL; ++u) {
@@ -396,6 +416,13 @@ __global__ __launch_bounds__(SMALL_THREADS) void k_tensorquant_small(const void*
 #pragma unroll
       for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
     }
+  }
+  float vo[SMALL_UNROLL][8];
+#pragma unroll
+  for (int u = 0; u < SMALL_UNROLL; ++u) {
+    decode8<DT>(own[u], vo[u]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(vo[u][t]));
   }
   m = wave_max(m);
   if ((tid & 63) == 0) s_red[tid >> 6] = m;
@@ -410,18 +437,17 @@ __global__ __launch_bounds__(SMALL_THREADS) void k_tensorquant_small(const void*
   float r, sc;
   dyn_scale(amax, qf, r, sc);
 
-  const int per = (n + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int lo = (int)blockIdx.x * per;
-  const int hi = min(n, lo + per);
-  for (int i = lo + tid; i < hi; i += SMALL_THREADS) {
-    float v[8];
-    decode8<DT>(load(i), v);
-    unsigned u[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) u[t] = qbyte(v[t], r, qf);
-    const int row = i / ppr;
-    *reinterpret_cast<u2v*>(codes + (int64_t)row * k + 8 * (i - row * ppr)) =
-        u2v{pack4_lo(u[0], u[1], u[2], u[3]), pack4_lo(u[4], u[5], u[6], u[7])};
+  for (int u = 0; u < SMALL_UNROLL; ++u) {
+    const int i = lo + u * SMALL_THREADS + tid;
+    if (i < hi) {
+      unsigned q[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) q[t] = qbyte(vo[u][t], r, qf);
+      // code rows are k long, so piece i starts at code 8i
+      *reinterpret_cast<u2v*>(codes + (int64_t)i * 8) =
+          u2v{pack4_lo(q[0], q[1], q[2], q[3]), pack4_lo(q[4], q[5], q[6], q[7])};
+    }
   }
   if (blockIdx.x == 0 && tid == 0) scales[0] = sc;
 }
@@ -575,21 +601,23 @@ int64_t tensor_small_max_elems() { return (int64_t)1 << 18; }
 hipError_t launch_tensor_small(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int bits,
                                const int32_t* bits_dev, int8_t* codes, float* scales, hipStream_t st) {
   if (rows * k > tensor_small_max_elems() || k % 8) return hipErrorInvalidValue;
-  // About four pieces per thread in the code pass, at most 16 workgroups re-reading the tensor.
+  // One piece per thread where the grid allows it; every workgroup's range must fit in
+  // its first batch of loads (2^18 elements: 32768 pieces, 2048 per workgroup).
   const int64_t pieces = rows * (k / 8);
-  int grid = (int)((pieces + 4 * SMALL_THREADS - 1) / (4 * SMALL_THREADS));
-  grid = grid < 1 ? 1 : grid > 16 ? 16 : grid;
+  int grid = (int)((pieces + SMALL_THREADS - 1) / SMALL_THREADS);
+  grid = grid < 1 ? 1 : grid > SMALL_MAX_GRID ? SMALL_MAX_GRID : grid;
+  if ((pieces + grid - 1) / grid > (int64_t)SMALL_THREADS * SMALL_UNROLL) return hipErrorInvalidValue;
+  const bool contig = ldx == k;
+  const int r = (int)rows, kk = (int)k;
+#define VQ_SMALLQ(D, C)                                                                                          \
+  hipLaunchKernelGGL((k_tensorquant_small<D, C>), dim3(grid), dim3(SMALL_THREADS), 0, st, x, ldx, r, kk, bits, \
+                     bits_dev, codes, scales)
   switch (dtype) {
-    case DT_F16:
-      hipLaunchKernelGGL(k_tensorquant_small<DT_F16>, dim3(grid), dim3(SMALL_THREADS), 0, st, x, ldx, (int)rows,
-                         (int)k, bits, bits_dev, codes, scales);
-      break;
-    case DT_BF16:
-      hipLaunchKernelGGL(k_tensorquant_small<DT_BF16>, dim3(grid), dim3(SMALL_THREADS), 0, st, x, ldx, (int)rows,
-                         (int)k, bits, bits_dev, codes, scales);
-      break;
+    case DT_F16: if (contig) VQ_SMALLQ(DT_F16, true); else VQ_SMALLQ(DT_F16, false); break;
+    case DT_BF16: if (contig) VQ_SMALLQ(DT_BF16, true); else VQ_SMALLQ(DT_BF16, false); break;
     default: return hipErrorInvalidValue;
   }
+#undef VQ_SMALLQ
   return hipGetLastError();
 }
 

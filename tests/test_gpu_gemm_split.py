@@ -41,7 +41,7 @@ def operands(vq, m, n, k, w_bits, a_bits, seed, dual=False):
 
 @pytest.mark.parametrize("m,n,k,w_bits,dual,out", [
     (17776, 3072, 12288, 4, False, torch.bfloat16),  # 840 tiles: 72 left over, 128-code stages
-    (300, 320, 6144, 8, False, torch.float16),       # 4 tiles, ragged M and N
+    (300, 4400, 6144, 8, False, torch.float16),      # 36 tiles, ragged M and N
     (1000, 900, 8192, 4, False, torch.bfloat16),     # 16 tiles, 4-bit weights in 128-code stages
     (600, 520, 6144, 4, True, torch.float32),        # dual-scale outlier partition, 9 tiles
     (520, 33000, 6144, 8, True, torch.bfloat16),     # 387 tiles: 131 left over (one range each), dual
@@ -68,7 +68,7 @@ def test_split_equals_unsplit(vq, m, n, k, w_bits, dual, out):
 
 
 def test_caller_workspace_and_no_split_shape(vq):
-    m, n, k = 512, 512, 6144  # 4 tiles
+    m, n, k = 512, 4608, 6144  # 36 tiles
     ac, as_, wc, ws = operands(vq, m, n, k, 8, 8, 3)
     need = vq._lib.vq_qgemm_workspace_bytes(m, n, k)
     buf = torch.zeros(need, dtype=torch.uint8, device=DEV)

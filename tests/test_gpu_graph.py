@@ -26,7 +26,7 @@ def vq():
 @pytest.mark.parametrize("m,n,k,gran", [
     (1000, 640, 1920, "token"),
     (1000, 640, 1920, "tensor"),
-    (300, 320, 6144, "token"),   # 4 tiles, split into two K ranges through the workspace
+    (300, 4400, 6144, "token"),  # 36 tiles, split into two K ranges through the workspace
 ])
 def test_graph_replays_match_eager(vq, m, n, k, gran):
     g = torch.Generator(device=DEV).manual_seed(m + n + k)
@@ -78,7 +78,7 @@ def test_default_workspace_under_capture(vq, monkeypatch):
     binding refuses before any launch (a buffer created there would be cached with its zero
     fill only recorded); after one eager call on that stream the cached, zeroed buffer
     serves the capture and every replay."""
-    m, n, k = 300, 320, 6144  # four tiles, two K ranges each: the workspace is used
+    m, n, k = 300, 4400, 6144  # 36 tiles, two K ranges each: the workspace is used
     assert vq._lib.vq_qgemm_workspace_bytes(m, n, k) > 0
     g = torch.Generator(device=DEV).manual_seed(7)
     x = torch.randn(m, k, generator=g, device=DEV).to(torch.bfloat16)

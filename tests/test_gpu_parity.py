@@ -366,7 +366,9 @@ def test_gemm_per_tensor_c1_full(vq, out_dtype):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 64), (1, 4, 64), (3, 7, 128), (255, 257, 192), (257, 255, 64),
-                                   (513, 100, 320)])
+                                   (513, 100, 320),
+                                   (1100, 1030, 128),   # 25 tiles: the tiled kernels, ragged both ways
+                                   (4097, 1030, 64)])   # 85 tiles
 def test_gemm_ragged_shapes(vq, m, n, k):
     rng = np.random.default_rng(m * 1000 + n)
     qa = torch.from_numpy(rng.integers(-127, 128, size=(m, k)).astype(np.int8))
@@ -381,6 +383,35 @@ def test_gemm_ragged_shapes(vq, m, n, k):
         accs, yf, ys = ogemm.qgemm_dequant(qa.numpy(), sa.numpy(), True, qw, sb.numpy(), k, "bf16")
         assert_same(acc[0].cpu().numpy(), accs[0], f"acc bits={bits}")
         assert_outputs(y, ys, "bf16", f"y bits={bits}")
+
+
+@pytest.mark.parametrize("m,n,k,out,gran,pitch", [
+    (1, 1, 64, torch.bfloat16, "token", 0),
+    (31, 33, 320, torch.float16, "token", 0),     # ten 32-deep steps: a partial load batch
+    (256, 512, 512, torch.float16, "tensor", 0),  # the 256 x 512 x 512 layer
+    (300, 200, 6144, torch.bfloat16, "token", 3), # 192 steps; a row pitch that forbids vector stores
+    (97, 130, 1920, torch.float32, "token", 0),
+    (1000, 1000, 1920, torch.bfloat16, "token", 0),  # 16 tiles: the largest few-tile shape
+    (1025, 1000, 1920, torch.bfloat16, "token", 0),  # 20 tiles: the tiled kernel
+])
+def test_gemm_few_tiles(vq, m, n, k, out, gran, pitch):
+    """Layers of at most 16 tiles of 256 x 256 (int8 weights, no outlier partition) run one
+    32 x 32 block per wave with register operands; accumulators and outputs must equal the
+    oracle's, as for the tiled kernels."""
+    rng = np.random.default_rng(m + n + k)
+    qa = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    sa = rng.uniform(0.001, 0.1, size=m if gran == "token" else 1).astype(np.float32)
+    sb = rng.uniform(0.001, 0.1, size=n).astype(np.float32)
+    big = torch.empty((m, n + pitch), dtype=out, device=DEV)
+    y = big[:, :n]
+    _, acc = vq.vq_qgemm_dequant(torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV),
+                                 torch.from_numpy(qw).to(DEV), torch.from_numpy(sb).to(DEV), 8, None, out,
+                                 gran == "token", acc_debug=True, y=y)
+    torch.cuda.synchronize()
+    accs, yf, ys = ogemm.qgemm_dequant(qa, sa, gran == "token", qw, sb, k, dtname(y))
+    assert_same(acc[0].cpu().numpy(), accs[0], "accumulators")
+    assert_outputs(y, ys, dtname(y), "output")
 
 
 def test_gemm_extreme_accumulators(vq):

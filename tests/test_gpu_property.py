@@ -1,6 +1,6 @@
 """Property test of the whole layer on the GPU against the oracle, over drawn options.
 
-Hypothesis draws the shape (M, N, K with K a multiple of 64; ragged M and N across
+Hypothesis draws the shape (M, N up to 1300, K a multiple of 64; ragged M and N across
 256 x 256 tiles), the weight and activation widths, the activation granularity, the
 outlier partition (dual scale, at most 128 channels) or the 128-point block Hadamard
 rotation, and the output type; every drawn layer must match the oracle bit for bit:
@@ -38,8 +38,9 @@ def layers(draw):
     mode = draw(st.sampled_from(["plain", "dual", "hadamard"]))
     kb = draw(st.integers(1, 12))  # K in 64s (Hadamard: 128s)
     k = 128 * kb if mode == "hadamard" else 64 * max(kb, 2 if mode == "dual" else 1)
-    m = draw(st.integers(1, 600))
-    n = draw(st.integers(1, 600))
+    # up to 36 tiles of 256 x 256: the few-tile kernel (at most 16) and the tiled kernels
+    m = draw(st.integers(1, 1300))
+    n = draw(st.integers(1, 1300))
     w_bits = draw(st.sampled_from([4, 8]))
     a_bits = draw(st.sampled_from([4, 6, 8]))
     gran = draw(st.sampled_from(["token", "tensor"]))

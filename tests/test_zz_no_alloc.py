@@ -62,10 +62,10 @@ def _noalloc(vq, ac, as_, wc, ws, b_bits, k0, out_dt, y):
 # (first call, second smaller call): (m, n, k, weight bits, outlier channels, output dtype)
 CASES = [
     # both shapes take the remainder split (K of 96 stages), so the scratch is used twice
-    ((300, 320, 6144, 8, 0, BF16), (200, 256, 6144, 8, 0, BF16)),
+    ((300, 4400, 6144, 8, 0, BF16), (200, 4352, 6144, 8, 0, BF16)),
     ((520, 640, 8192, 4, 0, F16), (260, 300, 6144, 4, 0, F16)),
     # no split (the ping-pong W8A8 kernel), then a split shape; dual scale with 4-bit weights
-    ((1000, 640, 1920, 8, 0, BF16), (300, 320, 6144, 8, 0, F32)),
+    ((1000, 4400, 1920, 8, 0, BF16), (300, 4400, 6144, 8, 0, F32)),
     ((700, 512, 3072, 4, 30, BF16), (300, 320, 6144, 4, 0, BF16)),
 ]
 
