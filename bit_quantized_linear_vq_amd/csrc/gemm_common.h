@@ -87,8 +87,11 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 // ---- remainder split: exchange of a K range's partial accumulators.
 // A lane's accumulators (MB x NB blocks of 16 32-bit values) travel as 64-bit words; word
 // w of thread t sits at part[w * nt + t], so each wave-wide access is contiguous.  The
-// words move with device-scope relaxed atomic stores and loads (write-through, no L2
-// write-back or invalidate), a store being performed device-wide once vmcnt reaches 0.
+// words are plain stores and loads; the tile's arrival counter orders them by the memory
+// model: each workgroup bumps it with a device-scope release (after a workgroup barrier
+// that orders every wave's stores before it), and the last arrival takes a device-scope
+// acquire fence before anyone reads the other partials (the barrier after it orders the
+// reads of every wave after the fence).
 template <typename V, int MB, int NB>
 __device__ __forceinline__ void split_publish(uint64_t* part, int nt, int tid, const V (&acc)[MB][NB]) {
 #pragma unroll
@@ -101,8 +104,7 @@ __device__ __forceinline__ void split_publish(uint64_t* part, int nt, int tid, c
         // reads the vector's first element whatever the index.
         const auto lo = acc[mb][nb][2 * i], hi = acc[mb][nb][2 * i + 1];
         const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-        __hip_atomic_store(part + (int64_t)((mb * NB + nb) * 8 + i) * nt + tid, v, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        part[(int64_t)((mb * NB + nb) * 8 + i) * nt + tid] = v;
       }
 }
 
@@ -111,15 +113,15 @@ __device__ __forceinline__ void split_accumulate(const uint64_t* part, int nt, i
   typedef decltype(acc[0][0][0] + 0) E;  // int or float
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    // All words of a row of blocks are requested before any is added: these loads bypass
-    // the L2, and issued one at a time each would wait out the full memory latency.
+    // All words of a row of blocks are requested before any is added: the partial was
+    // written back past the L2 by its publisher, and loads issued one at a time would each
+    // wait out the full memory latency.
     uint64_t v[NB][8];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        v[nb][i] = __hip_atomic_load(part + (int64_t)((mb * NB + nb) * 8 + i) * nt + tid, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+        v[nb][i] = part[(int64_t)((mb * NB + nb) * 8 + i) * nt + tid];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -130,13 +132,17 @@ __device__ __forceinline__ void split_accumulate(const uint64_t* part, int nt, i
   }
 }
 
-// After this workgroup's partial is published: bump the tile's arrival count once the
-// stores are performed; true (for the whole workgroup) in the last of `parts` arrivals.
+// After this workgroup's partial is stored: bump the tile's arrival count with a release
+// (every wave's stores done first); true (for the whole workgroup) in the last of `parts`
+// arrivals, which acquires before the barrier that lets its waves read the partials.
 __device__ __forceinline__ bool split_arrive(int32_t* cnt, int parts, int* s_flag) {
   wait_vmcnt<0>();
   __syncthreads();
-  if (threadIdx.x == 0)
-    *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+  if (threadIdx.x == 0) {
+    const bool last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *s_flag = last;
+  }
   __syncthreads();
   return *s_flag != 0;
 }

@@ -33,10 +33,10 @@
 // Remainder split: the tiles fill whole rounds of the persistent grid except the last
 // round, which would leave most CUs idle.  With a workspace, each remaining tile is split
 // into S ranges of K stages handled by different workgroups; each stores its int32
-// partial tile (device-coherent stores), then bumps an atomic count, and the workgroup
-// that arrives last adds the other partials and runs the epilogue.  Integer
-// sums are exact in any order, so the result is bit-identical to the unsplit tile, and
-// no workgroup ever waits for another.  The last arrival resets the tile's counter, so
+// partial tile, then bumps an atomic count with a device-scope release, and the
+// workgroup that arrives last acquires, adds the other partials and runs the epilogue.
+// Integer sums are exact in any order, so the result is bit-identical to the unsplit
+// tile, and no workgroup ever waits for another.  The last arrival resets the tile's counter, so
 // the workspace is left zeroed for the next call.
 #include <mutex>
 #include <type_traits>
