@@ -412,12 +412,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // ------------------------------------------------------------ remainder split
     if (part >= 0) {
       // Every item after a split one is split too and belongs to another workgroup, so
-      // this is the block's last item and nothing is in flight.  The partials move with
-      // device-scope relaxed atomic stores and loads, which write through and bypass the
-      // per-XCD L2: a device-scope fence would instead write back and invalidate the whole
-      // L2 under every other workgroup of the XCD.  A store is performed device-wide once
-      // vmcnt reaches 0, and the count is bumped only after that; the last arrival loads
-      // the other partials only after it has read the count.
+      // this is the block's last item and nothing is in flight.  The partials are plain
+      // stores; the count is bumped with a device-scope release and the last arrival
+      // acquires before it loads the other partials (split_arrive).  Only these last-round
+      // items pay the release's L2 write-back and the acquire's invalidate.
       split_publish(g.ws_part + (int64_t)(rslot * g.split + part) * (64 * NT), NT, tid, acc);
       if (!split_arrive(&g.ws_cnt[rslot], g.split, &s_last)) break;
       for (int p2 = 0; p2 < g.split; ++p2)
