@@ -89,3 +89,73 @@ def test_layer_matches_oracle(vq, case):
     got = y.cpu().numpy() if case["out"] == "fp32" else gen.as_numpy_bits(y.cpu())
     bad = np.flatnonzero(got.reshape(-1).view(want.dtype) != want.reshape(-1))
     assert bad.size == 0, f"outputs: {bad.size} mismatches, first at {bad[:5]}"
+
+
+# ------------------------------------------------------------------ MX route
+
+def _step_major(scales_rows, rows):
+    """Oracle scales [rows x K/32] -> the device's step-major bytes [K/64][rows8][2]."""
+    k32 = scales_rows.shape[1]
+    r8 = (rows + 7) // 8 * 8
+    out = np.zeros((k32 // 2, r8, 2), dtype=np.uint8)
+    out[:, :rows, :] = scales_rows.reshape(rows, k32 // 2, 2).transpose(1, 0, 2)
+    return out[:, :rows, :]
+
+
+def _device_scales(s, rows, k):
+    r8 = (rows + 7) // 8 * 8
+    return s.cpu().numpy()[: (k // 64) * r8 * 2].reshape(k // 64, r8, 2)[:, :rows, :]
+
+
+@st.composite
+def mx_layers(draw):
+    rotate = draw(st.booleans())
+    k = 128 * draw(st.integers(1, 12)) if rotate else 64 * draw(st.integers(1, 24))
+    return dict(m=draw(st.integers(1, 700)), n=draw(st.integers(1, 700)), k=k, rotate=rotate,
+                fa=draw(st.sampled_from(["fp4", "fp6"])), dtype=draw(st.sampled_from(["bf16", "fp16"])),
+                out=draw(st.sampled_from(["fp32", "bf16", "fp16"])), seed=draw(st.integers(0, 2 ** 31 - 1)))
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(case=mx_layers())
+def test_mx_layer_matches_oracle(vq, case):
+    """Drawn MX layers (shape, activation format, input type, the online block Hadamard on
+    both operands, output type): codes and E8M0 scales of both operands bit for bit, and
+    the GEMM within the float32 summation bound of the oracle's exact sum (plus half an
+    output ulp for 16-bit outputs)."""
+    from oracle import mx
+    print(f"mx property case: {case}", flush=True)
+    rng = np.random.default_rng(case["seed"])
+    m, n, k = case["m"], case["n"], case["k"]
+    x32 = rng.standard_normal((m, k)).astype(np.float32)
+    x32 *= np.exp2(rng.integers(-6, 7, size=(m, k // 32))).repeat(32, axis=1).astype(np.float32)
+    w32 = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x, w = gen.to_storage(x32, case["dtype"]), gen.to_storage(w32, case["dtype"])
+    had = 128 if case["rotate"] else 0
+    ac_d, as_d = vq.vq_mx_quant(x.to(DEV), case["fa"], had_block=had)
+    bc_d, bs_d = vq.vq_mx_quant(w.to(DEV), "fp4", had_block=had, exp_offset=-7 if had else 0)
+    y = vq.vq_mx_gemm(ac_d, as_d, case["fa"], bc_d, bs_d, "fp4", OUT[case["out"]])
+    torch.cuda.synchronize()
+
+    xf, wf = onum.to_f32(gen.as_numpy_bits(x), case["dtype"]), onum.to_f32(gen.as_numpy_bits(w), case["dtype"])
+    if had:
+        ac, asc = mx.quantize_rotated(xf, case["fa"])
+        bc, bsc = mx.quantize_rotated(wf, "fp4", exp_offset=-7)
+    else:
+        ac, asc = mx.quantize(xf, case["fa"])
+        bc, bsc = mx.quantize(wf, "fp4")
+    assert np.array_equal(ac_d.cpu().numpy(), mx.pack(ac, case["fa"])), "activation codes"
+    assert np.array_equal(_device_scales(as_d, m, k), _step_major(asc, m)), "activation scales"
+    assert np.array_equal(bc_d.cpu().numpy(), mx.pack(bc, "fp4")), "weight codes"
+    assert np.array_equal(_device_scales(bs_d, n, k), _step_major(bsc, n)), "weight scales"
+    exact = mx.gemm(ac, asc, case["fa"], bc, bsc, "fp4")
+    mag = np.abs(mx.dequantize(ac, asc, case["fa"])) @ np.abs(mx.dequantize(bc, bsc, "fp4")).T
+    bound = (k / 32 + 2) * 2.0 ** -24 * mag
+    got = y.float().cpu().numpy().astype(np.float64)
+    if case["out"] != "fp32":  # one more rounding: half a 16-bit ulp of the value
+        mant, emin = (7, -126) if case["out"] == "bf16" else (10, -14)
+        v = np.abs(exact) + bound
+        bound = bound + 0.5 * np.exp2(np.floor(np.log2(np.maximum(v, 2.0 ** emin))) - mant)
+    err = np.abs(got - exact)
+    assert np.all(err <= bound + 1e-300), float((err / np.maximum(bound, 1e-300)).max())
