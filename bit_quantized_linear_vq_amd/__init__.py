@@ -9,6 +9,7 @@ import of this module fails.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -103,11 +104,14 @@ def _check(fn, status):
 
 
 def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """torch's current stream on t's device, as the raw handle (an int: the signatures
+    declare it a pointer).  The raw-handle accessor skips building a Stream object, which
+    dominates the host cost of a call on small layers."""
+    return torch._C._cuda_getCurrentRawStream(t.get_device())
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _dev(t, name):
@@ -163,8 +167,20 @@ def vq_outlier_part_len(n_out: int) -> int:
     return int(_lib.vq_outlier_part_len(n_out))
 
 
+@functools.lru_cache(maxsize=1024)
 def vq_packed_k(k: int, n_out: int) -> int:
     return int(_lib.vq_packed_k(k, n_out))
+
+
+# Workspace sizes depend only on the shape (and the device's CU count, fixed per process).
+@functools.lru_cache(maxsize=1024)
+def _qgemm_ws_bytes(m: int, n: int, k0: int) -> int:
+    return int(_lib.vq_qgemm_workspace_bytes(m, n, k0))
+
+
+@functools.lru_cache(maxsize=1024)
+def _mx_ws_bytes(m: int, n: int, k: int) -> int:
+    return int(_lib.vq_mx_gemm_workspace_bytes(m, n, k))
 
 
 def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kfac: float = 1.0, ws=None,
@@ -274,7 +290,7 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
         _buf(acc, "acc", 4 * (2 if k0 < kp else 1) * m * n, a.device)
     ws = _gemm_workspace(m, n, k0, a.device) if ws is None else ws
     if ws is not False:
-        _buf(ws, "ws", int(_lib.vq_qgemm_workspace_bytes(m, n, k0)), a.device)
+        _buf(ws, "ws", _qgemm_ws_bytes(m, n, k0), a.device)
     _check("vq_qgemm_dequant", _lib.vq_qgemm_dequant(
         _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None),
@@ -325,7 +341,7 @@ _GEMM_WS = {}
 
 
 def _gemm_workspace(m, n, k0, device):
-    return _workspace(int(_lib.vq_qgemm_workspace_bytes(m, n, k0)), device)
+    return _workspace(_qgemm_ws_bytes(m, n, k0), device)
 
 
 def _workspace(need, device):
@@ -334,7 +350,7 @@ def _workspace(need, device):
     and each leaves it zeroed)."""
     if need == 0:
         return False
-    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    key = (device, torch._C._cuda_getCurrentRawStream(device.index))
     t = _GEMM_WS.get(key)
     if t is None or t.numel() < need:
         # Under graph capture a new buffer's zero fill would only be recorded, while the
@@ -476,7 +492,7 @@ def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: 
         _in(sa, "sa", _U8, vq_mx_scale_bytes(m, k), a.device)
         _in(b, "b", _U8, vq_mx_code_bytes(n, k, fb), a.device)
         _in(sb, "sb", _U8, vq_mx_scale_bytes(n, k), a.device)
-    need = int(_lib.vq_mx_gemm_workspace_bytes(m, n, k))
+    need = _mx_ws_bytes(m, n, k)
     ws = _workspace(need, a.device) if ws is None else ws
     if ws is not False:
         _buf(ws, "ws", need, a.device)
