@@ -60,6 +60,11 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="replay one HIP graph per step instead of launching every kernel from the host "
                         "(measured about 10%% slower than host launches on this part)")
+    p.add_argument("--graph-steps", type=int, default=0, metavar="G",
+                   help="replay HIP graphs of G consecutive steps (G must divide --steps); per-kernel times "
+                        "from graphs of G launches.  Default: 10 for the 256 x 512 x 512 workload, whose "
+                        "kernels take less time than the binding's host work per call, else 1 with --graph "
+                        "and host launches without it")
     p.add_argument("--residual-frac", type=float, default=0.0, metavar="F",
                    help="decompose a seeded fraction F of the tokens (residual re-quantization added back "
                         "in the epilogue); per-token workloads without dual scale or rotation only")
@@ -595,37 +600,42 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # One HIP graph per activation copy, each holding one whole step (every kernel of every
-    # layer), so the timed steps carry no host launch gaps; captured after the eager
-    # warm-up, with every buffer already allocated.
-    graphs = []
-    if args.graph:
-        side = torch.cuda.Stream(dev)
+    # HIP graphs of `gsteps` consecutive steps (every kernel of every layer), one per
+    # activation copy, so the timed steps carry no host launch gaps; captured after the
+    # eager warm-up, with every buffer already allocated.
+    gsteps = args.graph_steps or (10 if args.config == 1 else (1 if args.graph else 0))
+    if gsteps and args.steps % gsteps:
+        raise SystemExit(f"--steps ({args.steps}) must be a multiple of the steps per graph ({gsteps})")
+    side = torch.cuda.Stream(dev)
+
+    def capture(body):
         side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(side):
-            for i in range(len(L.x)):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    step(i)
-                graphs.append(g)
+            with torch.cuda.graph(g, stream=side):
+                body()
         stream.wait_stream(side)
+        return g
+
+    graphs = []
+    if gsteps:
+        for i in range(len(L.x)):
+            graphs.append(capture(lambda i=i: [step(i + j) for j in range(gsteps)]))
         for i in range(2 * len(graphs)):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-
-    def run(i):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
-            step(i)
 
     # Timed region: exactly `steps` steps between two synchronizations.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
-        run(i)
+    if graphs:
+        for r in range(args.steps // gsteps):
+            graphs[r % len(graphs)].replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -635,7 +645,18 @@ def main():
     # Events around every single launch would add their own few microseconds to each
     # interval, a large share of an 18-microsecond quantization.  One untimed step is queued
     # first so that the GPU is busy while the host enqueues the bracketed launches.
+    # With graphs, the launches are replayed from graphs of `gsteps` steps' launches.
     def batch_ms(launch):
+        if graphs:
+            g = capture(lambda: [launch(i, l) for i in range(gsteps) for l in range(L.layers)])
+            g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps // gsteps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / (args.steps * L.layers)
         step(0)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -677,7 +698,7 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "launch": "hip graph per step" if args.graph else "host launches",
+        "launch": f"hip graphs of {gsteps} step(s)" if gsteps else "host launches",
         "config": {"workload": workload, "M": L.M, "K": L.K, "N": L.N, "layers": L.layers,
                    "w_bits": L.c["w_bits"], "a_bits": L.c["a_bits"] if L.c["a_bits"] else "routed 8/4",
                    "act_granularity": L.gran, "hadamard_block": L.had,
