@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--hadamard", action="store_true",
                    help="only time the standalone 128-point block Hadamard rotation on the 17776 x 12288 "
                         "activations (bf16 in and out) beside a device copy of the same bytes, and exit")
+    p.add_argument("--dense", action="store_true",
+                   help="only time the unquantized bf16 layer of the precision override (vq_gemm_dense) at the "
+                        "workload's shape, beside torch.matmul of the same operands, and exit")
     p.add_argument("--control", action="store_true",
                    help="only time the per-block step control (TDC skip test, PDR overrides, DMPQ route) "
                         "over the 42 routed blocks' statistics and exit")
@@ -513,6 +516,36 @@ def hadamard(args, vq, gen, torch, dev):
                        "unit": "GB/s"}}))
 
 
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+
+def dense(args, vq, gen, torch, dev):
+    """Time vq_gemm_dense (the unquantized bf16 layer that the precision override runs for
+    high-outlier layers) on the workload's X and W, and torch.matmul (the vendor library)
+    on the same operands, both over back-to-back launches between HIP events."""
+    c = gen.CONFIGS[args.config]
+    x = gen.make_x(args.config).to(dev)
+    w = gen.make_w(args.config).to(dev)
+    if x.dtype != w.dtype:
+        w = w.to(x.dtype)
+    y = torch.empty((x.shape[0], w.shape[0]), dtype=x.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    us = launches_us(lambda: vq.vq_gemm_dense(x, w, y=y), torch, stream)
+    wt = w.t()
+    ref_us = launches_us(lambda: torch.matmul(x, wt, out=y), torch, stream)
+    m, k = x.shape
+    n = w.shape[0]
+    tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "unquantized bf16 layer TFLOP/s (precision override)", "value": round(tf, 1), "unit": "TFLOP/s",
+        "higher_is_better": True, "dtype": str(x.dtype).replace("torch.", ""),
+        "config": {"workload": c["name"] + "_unquantized", "M": m, "K": k, "N": n},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "avg_us": round(us, 2), "kernel": "k_gemm_dense"},
+        "vendor_ref": {"op": "torch.matmul(x, w.t()) on the same operands", "avg_us": round(ref_us, 2),
+                       "achieved": round(2.0 * m * n * k / (ref_us * 1e-6) / 1e12, 1), "unit": "TFLOP/s"}}))
+
+
 def control(args, vq, gen, torch, dev):
     """Time vq_step_control for the 42 routed blocks of one denoising step: each decision
     reduces the block's two cached residual deltas (E) and its previous input/output
@@ -587,6 +620,9 @@ def main():
         return
     if args.control:
         control(args, vq, gen, torch, dev)
+        return
+    if args.dense:
+        dense(args, vq, gen, torch, dev)
         return
     L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx, args.act_gran)
     stream = torch.cuda.current_stream(dev)

@@ -32,7 +32,7 @@ EXPORTS = (
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
     "vq_qgemm_dequant_residual", "vq_mx_code_bytes", "vq_mx_scale_bytes", "vq_mx_quant", "vq_mx_quant_rotated",
     "vq_mx_gemm",
-    "vq_mx_gemm_workspace_bytes",
+    "vq_mx_gemm_workspace_bytes", "vq_gemm_dense",
     "vq_calib_hist_bins", "vq_calib_static_scale", "vq_control_workspace_elems", "vq_step_control",
     "vq_status_string", "vq_last_hip_error", "vq_version",
 )
@@ -82,6 +82,7 @@ def _load():
         "vq_mx_quant_rotated": (I, [P, I, I64, I64, I64, I, I, P, P, P]),
         "vq_mx_gemm": (I, [P, P, I, P, P, I, I64, I64, I64, P, I, I64, P, P]),
         "vq_mx_gemm_workspace_bytes": (I64, [I64, I64, I64]),
+        "vq_gemm_dense": (I, [P, P, I, I64, I64, I64, I64, I64, P, I, I64, P]),
         "vq_calib_hist_bins": (I64, []),
         "vq_calib_static_scale": (I, [P, I, I64, I64, I64, I, P, I32, P, P, P, P, P, P, P]),
         "vq_status_string": (ctypes.c_char_p, [I]),
@@ -363,6 +364,32 @@ def _workspace(need, device):
         t = torch.zeros(need, dtype=torch.uint8, device=device)
         _GEMM_WS[key] = t
     return t
+
+
+def vq_gemm_dense(x: torch.Tensor, w: torch.Tensor, out_dtype=None, y=None):
+    """Unquantized FP16/BF16 layer Y = X . W^T (float32 accumulation), for the layers the
+    precision override runs at 16 bits.  x [M x K] and w [N x K] share one 16-bit dtype;
+    out_dtype defaults to it.  Returns y."""
+    _dev(x, "x")
+    _dev(w, "w")
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-D")
+    m, k = x.shape
+    n = w.shape[0]
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    if w.dtype != x.dtype or w.device != x.device:
+        raise TypeError(f"w must be a {x.dtype} tensor on {x.device}")
+    if w.shape[1] != k:
+        raise ValueError(f"w must be [N x {k}]")
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _out2d(y, "y", m, n, x.device)
+    _check("vq_gemm_dense", _lib.vq_gemm_dense(
+        _ptr(x), _ptr(w), _DT[x.dtype], m, n, k, x.stride(0), w.stride(0), _ptr(y), _DT.get(y.dtype, -1),
+        y.stride(0), _stream(x)))
+    return y
 
 
 def vq_route_rel_l1(x: torch.Tensor, y: torch.Tensor, threshold: float = 0.1, bits_hi: int = 8, bits_lo: int = 4,

@@ -16,6 +16,24 @@ namespace vqk {
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz32(int r) { return (r >> 3) & 1; }
 
+// Swizzle and direct-load lane mapping of a row width: a 1 KB load covers 1024/W rows,
+// lane -> (row, 16-byte position), the position holding chunk position ^ swz(row).
+// A 16-lane group of 16-byte fragment reads covers the 64 banks once when the chunks of
+// its 16 rows land on distinct 16-byte bank groups: with 128-byte rows, rows r and r+1
+// start half a bank line apart, so the eight chunk positions are spread over r >> 1.
+template <int W>
+__device__ __forceinline__ int swz_row(int r) {
+  if constexpr (W == 32) return swz32(r);
+  else if constexpr (W == 64) return swz64(r);
+  else return (r >> 1) & 7;
+}
+template <int W>
+__device__ __forceinline__ void dma_lane(int q, int lane, int& row, int& col) {
+  constexpr int LPR = W / 16;  // lanes per row
+  row = (1024 / W) * q + lane / LPR;
+  col = 16 * ((lane % LPR) ^ swz_row<W>(row));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -401,6 +401,21 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
   return hip_status(vq_internal::launch_mx_gemm(a, sa, (int)fa, b, sb, m, n, k, y, (int)out_dt, ldy, ws, stream));
 }
 
+// ------------------------------------------------------------------ unquantized layer
+
+vq_status vq_gemm_dense(const void* x, const void* w, vq_dtype dt, int64_t m, int64_t n, int64_t k,
+                        int64_t ldx, int64_t ldw, void* y, vq_dtype out_dt, int64_t ldy, hipStream_t stream) {
+  if (!x || !w || !y) return VQ_ERR_INVALID_ARG;
+  if (!is_16bit(dt) || !valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
+  if (m < 1 || n < 1 || k < 1 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return VQ_ERR_INVALID_ARG;
+  if (ldx < k || ldw < k || ldy < n) return VQ_ERR_INVALID_ARG;
+  if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || ldx % 8 || ldw % 8) return VQ_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
+  vq_internal::DenseParams p{x, w, dt == VQ_BF16 ? 1 : 0, m, n, k, ldx, ldw, y, (int)out_dt, ldy};
+  return hip_status(vq_internal::launch_gemm_dense(p, stream));
+}
+
 // ------------------------------------------------------------------ calibration
 
 int64_t vq_calib_hist_bins(void) { return vq_internal::calib_hist_bins(); }

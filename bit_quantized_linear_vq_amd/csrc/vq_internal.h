@@ -80,6 +80,17 @@ int64_t mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uint8_t* b, const uint8_t* sb, int64_t m,
                           int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, void* ws, hipStream_t st);
 
+struct DenseParams {
+  const void* x;
+  const void* w;
+  int in_dt;  // 0 f16, 1 bf16
+  int64_t m, n, k, ldx, ldw;
+  void* y;
+  int out_dt;
+  int64_t ldy;
+};
+hipError_t launch_gemm_dense(const DenseParams& p, hipStream_t st);
+
 int calib_hist_bins();
 constexpr int CALIB_MAX_CAND = 64;
 hipError_t launch_calib(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int bits,

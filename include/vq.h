@@ -317,6 +317,25 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
                      vq_dtype out_dt, int64_t ldy, void* ws, hipStream_t stream);
 
 /*
+ * Unquantized FP16/BF16 layer for the precision override (6Bit-Diffusion, Methodology
+ * B.3, PDR: a layer whose input has a high outlier ratio is computed in FP16/BF16; the
+ * step control reports it as precision code 16).
+ *   y[i, j] = sum_k x[i, k] * w[j, k], accumulated in float32 on the matrix cores (the
+ *   products of 16-bit values are exact), then rounded once to out_dt (round to nearest
+ *   even).  The sum is the exact one only up to the float32 accumulation's rounding:
+ *   |y - exact| <= (k + 2) * 2^-24 * sum_k |x_k w_k| before the output rounding.
+ *   x      device, dt in {F16, BF16}, [m x k], row stride ldx elements
+ *   w      device, same dt, [n x k], row stride ldw elements
+ *   y      device, out_dt in {F16, BF16, F32}, [m x n], row stride ldy elements; aligned
+ *          to its element size (16-byte rows store faster)
+ *   k % 64 == 0; x and w 16-byte aligned, ldx % 8 == 0, ldw % 8 == 0.
+ * Asynchronous on `stream`; nothing is allocated.  Errors: INVALID_ARG (null pointers,
+ * dtypes, sizes, strides), SHAPE (k % 64, alignment).
+ */
+vq_status vq_gemm_dense(const void* x, const void* w, vq_dtype dt, int64_t m, int64_t n, int64_t k,
+                        int64_t ldx, int64_t ldw, void* y, vq_dtype out_dt, int64_t ldy, hipStream_t stream);
+
+/*
  * Static per-tensor activation scale by clipping-percentile search (Q-ARVD, Technical
  * details: per-tensor activations with a clipping percentile and a scale learned during
  * reconstruction).  One pass builds the histogram of |x| over its 32768 16-bit magnitude
@@ -379,7 +398,7 @@ vq_status vq_route_rel_l1(const void* x, const void* y, vq_dtype dt, int64_t n, 
  * The readings (delta definition, the form of E, the accumulated error, the precedence)
  * are this library's: the page states the rules without formulas.  bits_dev feeds
  * vq_quant_act's bits_dev directly (it quantizes a 16 as 8: a caller that honours the
- * flag runs the layer unquantized instead).
+ * flag runs the layer unquantized instead, with vq_gemm_dense).
  *   delta_new, delta_old  device [n_delta] of delta_dt (F16/BF16/F32), or both NULL
  *   x_prev, y_prev        device [n_xy] of xy_dt, or both NULL
  *   n_out_dev             device int32 [1] (e.g. vq_detect_outliers' n_out_dev) or NULL;

@@ -353,6 +353,24 @@ def test_mx_gemm_workspace_sizes(lib):
     assert lib.vq_mx_gemm_workspace_bytes(300, 320, 6100) == 0  # K not a multiple of 64
 
 
+def test_gemm_dense_validation(lib):
+    def call(x=FAKE, w=FAKE, dt=BF16, m=64, n=64, k=128, ldx=128, ldw=128, y=FAKE, out=BF16, ldy=64):
+        return lib.vq_gemm_dense(x, w, dt, m, n, k, ldx, ldw, y, out, ldy, NULL)
+    assert call(x=NULL) == INVALID
+    assert call(w=NULL) == INVALID
+    assert call(y=NULL) == INVALID
+    assert call(dt=F32) == INVALID       # inputs are 16-bit
+    assert call(out=7) == INVALID
+    assert call(m=0) == INVALID
+    assert call(ldx=64) == INVALID
+    assert call(ldw=96) == INVALID
+    assert call(ldy=32) == INVALID
+    assert call(k=96, ldx=96, ldw=96) == SHAPE  # K a multiple of 64
+    assert call(x=ctypes.c_void_p(0x10008)) == SHAPE
+    assert call(ldw=132) == SHAPE         # row pitch not a multiple of 8 elements
+    assert call(y=ctypes.c_void_p(0x10001)) == SHAPE
+
+
 def test_calib_validation(lib):
     assert lib.vq_calib_hist_bins() == 32768
     pct = (ctypes.c_double * 2)(100.0, 99.9)
