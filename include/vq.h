@@ -140,6 +140,11 @@ vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int6
  *   static_scale_dev  device float [1 or 2] (static granularity only), else NULL
  *   codes      device int8 [m x kp], row stride kp = vq_packed_k(k, n_out)
  *   scales     device float: per token [m] or [m x 2]; per tensor [1] or [2]
+ * Launches: per token, one kernel; dynamic per tensor, one kernel for at most 2^18
+ * elements without outlier partition or rotation (every workgroup reduces the whole
+ * maximum itself), else a fill kernel that clears the maximum, a maximum pass, the code
+ * pass and a one-thread finalize; static per tensor, the code pass and the finalize.  No
+ * memset is enqueued, so a call may be captured in a graph.
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED as for vq_pack_weights.
  */
 vq_status vq_quant_act(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t ldx, int bits,
