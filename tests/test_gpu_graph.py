@@ -3,9 +3,10 @@
 A step (activation quantization and the GEMM with its epilogue) is captured once and
 replayed several times, with eager work on the same buffers between the replays; every
 replay must reproduce the eager output bit for bit.  Cases: per-token and dynamic
-per-tensor quantization (the latter clears its maxima with a fill kernel, no memset), and
-a GEMM whose leftover tiles are split along K through a workspace that every call must
-leave zeroed for the next replay.
+per-tensor quantization (the latter clears its maxima with a fill kernel, no memset), a
+GEMM whose leftover tiles are split along K through a workspace that every call must
+leave zeroed for the next replay, the tiny per-tensor layer (one-launch quantizer,
+few-tile GEMM) with the unquantized bf16 layer, and split GEMMs on two streams at once.
 """
 import pytest
 import torch
@@ -110,3 +111,73 @@ def test_default_workspace_under_capture(vq, monkeypatch):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), f"replay {rep}"
+
+
+def test_small_layer_and_dense_layer_in_one_graph(vq):
+    """The 256 x 512 x 512 per-tensor layer (one-launch quantizer, few-tile GEMM) and the
+    unquantized bf16 layer, captured together and replayed with eager work on the same
+    buffers between replays: every replay equals the eager results."""
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn(256, 512, generator=g, device=DEV).to(torch.float16)
+    x2 = torch.randn(256, 512, generator=g, device=DEV).to(torch.float16)
+    w = (torch.randn(512, 512, generator=g, device=DEV) * 0.02).to(torch.float16)
+    wc, wsc = vq.vq_pack_weights(w, 8)
+    codes = torch.empty((256, 512), dtype=torch.int8, device=DEV)
+    scales = torch.empty(1, dtype=torch.float32, device=DEV)
+    y = torch.empty((256, 512), dtype=torch.float16, device=DEV)
+    yd = torch.empty((256, 512), dtype=torch.float16, device=DEV)
+
+    def step(src):
+        vq.vq_quant_act(src, 8, "tensor", codes=codes, scales=scales)
+        vq.vq_qgemm_dequant(codes, scales, wc, wsc, 8, 512, torch.float16, False, y=y, ws=False)
+        vq.vq_gemm_dense(src, w, y=yd)
+
+    step(x)
+    torch.cuda.synchronize()
+    ref = (y.clone(), yd.clone(), scales.clone())
+    step(x2)
+    torch.cuda.synchronize()
+    ref2 = (y.clone(), yd.clone(), scales.clone())
+    assert not torch.equal(ref[0], ref2[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(x)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        y.zero_()
+        yd.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]) and torch.equal(yd, ref[1]) and torch.equal(scales, ref[2]), f"replay {rep}"
+        step(x2)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref2[0]) and torch.equal(yd, ref2[1]), f"eager after replay {rep}"
+
+
+def test_two_streams_keep_separate_workspaces(vq):
+    """Split GEMMs on two streams at once, each with the binding's default workspace (one
+    per device and stream): both results equal the unsplit GEMM."""
+    m, n, k = 300, 4400, 6144  # 36 tiles, two K ranges each
+    g = torch.Generator(device=DEV).manual_seed(8)
+    xs = [torch.randn(m, k, generator=g, device=DEV).to(torch.bfloat16) for _ in range(2)]
+    w = (torch.randn(n, k, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    wc, wsc = vq.vq_pack_weights(w, 8)
+    ops = [vq.vq_quant_act(x, 8) for x in xs]
+    want = [vq.vq_qgemm_dequant(a, s, wc, wsc, 8, ws=False) for a, s in ops]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = [None, None]
+    for rep in range(3):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                outs[i] = vq.vq_qgemm_dequant(ops[i][0], ops[i][1], wc, wsc, 8)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], want[i]), f"stream {i}, call {rep}"
+    keys = [key for key in vq._GEMM_WS if key[1] in (streams[0].cuda_stream, streams[1].cuda_stream)]
+    assert len(keys) == 2
