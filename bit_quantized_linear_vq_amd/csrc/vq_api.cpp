@@ -33,6 +33,9 @@ bool valid_dt(vq_dtype dt) { return dt == VQ_F16 || dt == VQ_BF16 || dt == VQ_F3
 int64_t part_len(int32_t n_out) { return n_out > 0 ? ((int64_t)n_out + VQ_K_ALIGN - 1) / VQ_K_ALIGN * VQ_K_ALIGN : 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// The GEMM kernels count 256 x 256 tiles (and split items, at most twice as many) in
+// 32-bit integers.
+bool too_many_tiles(int64_t m, int64_t n) { return ((m + 255) / 256) * ((n + 255) / 256) > ((int64_t)1 << 28); }
 
 // Shared checks of the row-quantization entry points.
 vq_status check_rows(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, const int32_t* idx,
@@ -225,7 +228,7 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
 // ------------------------------------------------------------------ GEMM
 
 int64_t vq_qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0) {
-  if (m < 1 || n < 1 || k0 < 1 || m >= kMaxDim || n >= kMaxDim || k0 >= kMaxDim) return 0;
+  if (m < 1 || n < 1 || k0 < 1 || m >= kMaxDim || n >= kMaxDim || k0 >= kMaxDim || too_many_tiles(m, n)) return 0;
   return vq_internal::qgemm_workspace_bytes(m, n, k0);
 }
 
@@ -238,6 +241,7 @@ vq_status check_gemm(const int8_t* a, const float* sa, int sa_per_token, const v
   if (m < 1 || n < 1 || kp < 1 || k0 < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || kp >= kMaxDim)
     return VQ_ERR_INVALID_ARG;
   if (b_bits != 4 && b_bits != 8) return VQ_ERR_UNSUPPORTED;
+  if (too_many_tiles(m, n)) return VQ_ERR_UNSUPPORTED;
   if (kp % VQ_K_ALIGN || k0 % VQ_K_ALIGN || k0 > kp || kp - k0 > VQ_MAX_OUTLIERS) return VQ_ERR_SHAPE;
   // The int32 accumulators must hold any sum of the longer partition (partition 0): 127
   // per activation code times 127 per int8 weight code, or 112 = 16 * 7 per 4-bit weight
@@ -383,7 +387,9 @@ vq_status vq_mx_quant_rotated(const void* x, vq_dtype dt, int64_t rows, int64_t 
 }
 
 int64_t vq_mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m < 1 || n < 1 || k < 1 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % VQ_K_ALIGN) return 0;
+  if (m < 1 || n < 1 || k < 1 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % VQ_K_ALIGN ||
+      too_many_tiles(m, n))
+    return 0;
   return vq_internal::mx_gemm_workspace_bytes(m, n, k);
 }
 
@@ -394,6 +400,7 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
   if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
   if (m < 1 || n < 1 || k < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return VQ_ERR_INVALID_ARG;
   if (!mx_fmt_ok(fa) || fb != VQ_MXFP4) return VQ_ERR_UNSUPPORTED;
+  if (too_many_tiles(m, n)) return VQ_ERR_UNSUPPORTED;
   if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b) || !aligned16(sa) || !aligned16(sb)) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
@@ -409,6 +416,7 @@ vq_status vq_gemm_dense(const void* x, const void* w, vq_dtype dt, int64_t m, in
   if (!is_16bit(dt) || !valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
   if (m < 1 || n < 1 || k < 1 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return VQ_ERR_INVALID_ARG;
   if (ldx < k || ldw < k || ldy < n) return VQ_ERR_INVALID_ARG;
+  if (too_many_tiles(m, n)) return VQ_ERR_UNSUPPORTED;
   if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || ldx % 8 || ldw % 8) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;

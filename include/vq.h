@@ -193,7 +193,8 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
  *            bit-identical to the unsplit GEMM.  Every call leaves the workspace
  *            zero-filled; calls that share one must not overlap.  A size of 0 means the
  *            shape gains nothing from the split (ws is then not used).
- * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8, out_dt).
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8, out_dt, or more than 2^28
+ * output tiles of 256 x 256, which the kernels' 32-bit tile counts cannot hold).
  */
 int64_t vq_qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0);
 vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b,
@@ -297,7 +298,7 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
  *   one rounding, within the same bound, and does not depend on the order the ranges
  *   finish).  Every call leaves the workspace zeroed; calls sharing one must not
  *   overlap.  Errors: INVALID_ARG, SHAPE (k % 64, alignment), UNSUPPORTED (fa, fb other
- *   than MXFP4).
+ *   than MXFP4, or more than 2^28 output tiles of 256 x 256).
  */
 int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt);
 int64_t vq_mx_scale_bytes(int64_t rows, int64_t k);
@@ -335,7 +336,8 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
  *          to its element size (16-byte rows store faster)
  *   k % 64 == 0; x and w 16-byte aligned, ldx % 8 == 0, ldw % 8 == 0.
  * Asynchronous on `stream`; nothing is allocated.  Errors: INVALID_ARG (null pointers,
- * dtypes, sizes, strides), SHAPE (k % 64, alignment).
+ * dtypes, sizes, strides), SHAPE (k % 64, alignment), UNSUPPORTED (more than 2^28 output
+ * tiles of 256 x 256).
  */
 vq_status vq_gemm_dense(const void* x, const void* w, vq_dtype dt, int64_t m, int64_t n, int64_t k,
                         int64_t ldx, int64_t ldw, void* y, vq_dtype out_dt, int64_t ldy, hipStream_t stream);

@@ -353,6 +353,20 @@ def test_mx_gemm_workspace_sizes(lib):
     assert lib.vq_mx_gemm_workspace_bytes(300, 320, 6100) == 0  # K not a multiple of 64
 
 
+def test_gemm_tile_count_bound(lib):
+    """Output shapes whose 256 x 256 tile count exceeds 2^28 are refused (the kernels
+    count tiles in 32 bits), and their workspace size is reported as 0."""
+    big = 1 << 30  # 2^22 x 2^22 tiles
+    assert lib.vq_qgemm_workspace_bytes(big, big, 6144) == 0
+    assert lib.vq_mx_gemm_workspace_bytes(big, big, 6144) == 0
+    assert lib.vq_qgemm_dequant(FAKE, FAKE, 1, FAKE, 8, FAKE, big, big, 64, 64, FAKE, BF16, big, NULL, NULL,
+                                NULL) == UNSUP
+    assert lib.vq_mx_gemm(FAKE, FAKE, MXFP4, FAKE, FAKE, MXFP4, big, big, 64, FAKE, BF16, big, NULL, NULL) == UNSUP
+    assert lib.vq_gemm_dense(FAKE, FAKE, BF16, big, big, 64, 64, 64, FAKE, BF16, big, NULL) == UNSUP
+    # the largest accepted count: 2^14 x 2^14 tiles
+    assert lib.vq_gemm_dense(FAKE, FAKE, BF16, 1 << 22, 1 << 22, 96, 96, 96, FAKE, BF16, 1 << 22, NULL) == SHAPE
+
+
 def test_gemm_dense_validation(lib):
     def call(x=FAKE, w=FAKE, dt=BF16, m=64, n=64, k=128, ldx=128, ldw=128, y=FAKE, out=BF16, ldy=64):
         return lib.vq_gemm_dense(x, w, dt, m, n, k, ldx, ldw, y, out, ldy, NULL)
