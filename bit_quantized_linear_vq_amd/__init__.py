@@ -609,3 +609,69 @@ def vq_step_control(state: torch.Tensor, params: ControlParams, delta_new=None, 
         _ptr(n_out_dev), channels, ctypes.byref(params), _ptr(state), _ptr(ws), _ptr(skip), _ptr(bits), _ptr(e),
         _ptr(gamma), _stream(state)))
     return skip, bits, e, gamma
+
+
+# ------------------------------------------------------------------ prepared calls
+
+# Entry points that only enqueue work on a stream (their last argument).
+_LAUNCHES = frozenset((
+    "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant", "vq_qgemm_dequant_noalloc",
+    "vq_route_rel_l1", "vq_quant_residual", "vq_qgemm_dequant_residual", "vq_mx_quant", "vq_mx_quant_rotated",
+    "vq_mx_gemm", "vq_gemm_dense", "vq_calib_static_scale", "vq_step_control",
+))
+
+
+class _Recorder:
+    """Stands in for the library while a binding function runs under prepare(): the
+    launch entry points are recorded instead of called; everything else passes through."""
+
+    def __init__(self, lib):
+        self._lib = lib
+        self.calls = []
+
+    def __getattr__(self, name):
+        f = getattr(self._lib, name)
+        if name not in _LAUNCHES:
+            return f
+
+        def record(*args):
+            self.calls.append((name, f, args))
+            return VQ_OK
+        return record
+
+
+def prepare(fn, *args, **kwargs):
+    """Validate and marshal a binding call once, for loops that repeat it on the same
+    tensors (the binding's checks cost more host time than the kernels of a small layer).
+
+    Runs fn(*args, **kwargs) with the library's launches recorded instead of enqueued, and
+    returns (launch, result): result is what fn returned (its outputs, allocated now if
+    not given), and launch() enqueues the recorded launches again, unchanged, on torch's
+    current stream of the device at that time (the device of fn's first device-tensor
+    argument, else the current device).  fn may also be a caller's function that makes
+    binding calls: all their launches are recorded, in order.  The tensors involved must stay alive and
+    keep their storage and shape (launch() holds references to them; it reads their data
+    anew at each call).  fn must be one of the binding's asynchronous entry points;
+    prepare() is not thread-safe (it swaps the library handle for the duration of fn).
+    """
+    global _lib
+    real = _lib
+    rec = _Recorder(real)
+    _lib = rec
+    try:
+        result = fn(*args, **kwargs)
+    finally:
+        _lib = real
+    if not rec.calls:
+        raise ValueError(f"{getattr(fn, '__name__', fn)} enqueues nothing through the library")
+    tensors = [a for a in list(args) + list(kwargs.values()) if isinstance(a, torch.Tensor) and a.is_cuda]
+    device = tensors[0].get_device() if tensors else torch.cuda.current_device()
+    calls = rec.calls
+    keep = (args, kwargs, result)
+
+    def launch():
+        st = torch._C._cuda_getCurrentRawStream(device)
+        for name, f, a in calls:
+            _check(name, f(*a[:-1], st))
+    launch.keep = keep
+    return launch, result
