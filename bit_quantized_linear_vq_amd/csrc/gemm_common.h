@@ -42,6 +42,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
+// The same barrier with no instruction moved across it by the scheduler: the ping-pong
+// schedules rely on the phases staying where they are written.
+__device__ __forceinline__ void sched_barrier_all() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 16 bytes per lane from global memory straight into LDS at ldst + 16 * lane (ldst is
@@ -86,6 +94,33 @@ __device__ __forceinline__ void store4_f32(void* y, int64_t off, const float v[4
   } else {
     for (int i = 0; i < cnt; ++i) p[i] = v[i];
   }
+}
+
+// Work item w of a persistent GEMM with the remainder split: items [0, dp_items) are
+// whole tiles, the rest are `split` consecutive K ranges of each remaining tile.  Written
+// with selects only: with an if/else that assigns the fields on both sides, the compiler
+// merged the stores into a store through a selected address and kept the fields in
+// scratch memory, whose reload at every tile start drained all outstanding loads.
+struct WorkItem {
+  int tile;   // tile index for tile_of
+  int kb0;    // first K stage
+  int nks;    // K stages of the item
+  int part;   // K range (-1: whole tile)
+  int rslot;  // index among the remaining tiles (0 for a whole tile)
+};
+__device__ __forceinline__ WorkItem item_of(int w, int dp_items, int split, int nk) {
+  const bool whole = w < dp_items;
+  const int j = whole ? 0 : w - dp_items;
+  const int rs = j / split;
+  const int pt = j - rs * split;
+  const int b0 = pt * nk / split;
+  WorkItem it;
+  it.tile = whole ? w : dp_items + rs;
+  it.kb0 = whole ? 0 : b0;
+  it.nks = whole ? nk : (pt + 1) * nk / split - b0;
+  it.part = whole ? -1 : pt;
+  it.rslot = rs;
+  return it;
 }
 
 // Block b -> tile (tm, tn): contiguous tile ranges per XCD, grouped order inside.

@@ -318,9 +318,20 @@ struct MxArgs {
   uint64_t* ws_part;
 };
 
-template <int FA, int S, int OUT_DT>
+// Two schedules of the same K loop.  Interleaved (PP false): every wave reads the next
+// sub-step's fragments while the MFMAs of the current one run, one barrier per stage.
+// Ping-pong (PP true, S = 2): the two waves of a SIMD (w and w + 4) alternate between a
+// memory phase (the fragment reads of a whole stage and this wave's share of the refill
+// loads) and a compute phase (the stage's MFMAs from registers), waves 0-3 one phase
+// ahead of waves 4-7, two barriers per stage; the refill of stage p + 2 is issued in the
+// memory phase of stage p into the slot read at stage p + 2 - NST, whose readers passed
+// a barrier before.
+template <int FA, int S, int OUT_DT, bool PP>
 __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mxgemm(MxArgs g) {
   using C = MxCfg<FA, S>;
+  static_assert(!PP || (S == 2 && C::NST >= 3), "ping-pong: two sub-steps, three stages");
+  constexpr int PD = 2;                         // ping-pong refill distance (stages)
+  constexpr int PRO = PP ? PD : C::NST - 1;     // stages requested ahead of a tile
   constexpr bool HALF_OUT = OUT_DT != DT_F32;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::STAGE];
 
@@ -387,21 +398,13 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   int kb0 = 0, nks = nk;     // the item's first stage and stage count
   int part = -1, rslot = 0;  // K range of a split tile (-1: whole tile) and its remainder index
   auto set_tile = [&](int w) {
-    int ti = w;
-    if (w < g.dp_items) {
-      kb0 = 0;
-      nks = nk;
-      part = -1;
-    } else {
-      const int j = w - g.dp_items;
-      rslot = j / g.split;
-      part = j - rslot * g.split;
-      ti = g.dp_items + rslot;
-      kb0 = part * nk / g.split;
-      nks = (part + 1) * nk / g.split - kb0;
-    }
+    const WorkItem it = item_of(w, g.dp_items, g.split, nk);
+    kb0 = it.kb0;
+    nks = it.nks;
+    part = it.part;
+    rslot = it.rslot;
     int tm, tn;
-    tile_of(ti, g.tiles_m, g.tiles_n, tm, tn);
+    tile_of(it.tile, g.tiles_m, g.tiles_n, tm, tn);
     m0 = tm * MX_BM;
     n0 = tn * MX_BN;
 #pragma unroll
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   };
   auto issue_prologue = [&]() {
 #pragma unroll
-    for (int s = 0; s < C::NST - 1; ++s)
+    for (int s = 0; s < PRO; ++s)
       if (s < nks) issue(kb0 + s, s);
   };
 
@@ -515,12 +518,72 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   if (vt >= g.items) return;
   set_tile(vt);
   issue_prologue();
+  // pend (ping-pong): the previous tile's 16 output stores were issued after this tile's
+  // first loads, so the first waits of this tile leave them in flight (vmcnt is in order).
+  bool pend = false;
   for (;;) {
 #pragma unroll
     for (int i = 0; i < MX_MBLK; ++i)
 #pragma unroll
       for (int j = 0; j < MX_NBLK; ++j) acc[i][j] = v16f{};
 
+    if constexpr (PP) {
+      const int grp = wave >> 2;
+      auto reads_done = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };  // lgkmcnt(0)
+      if (nks >= 2) {
+        if (pend) wait_vmcnt<C::L + 16>();
+        else wait_vmcnt<C::L>();
+      } else {
+        if (pend) wait_vmcnt<16>();
+        else wait_vmcnt<0>();
+      }
+      sched_barrier_all();
+      if (grp == 1) sched_barrier_all();
+      Frag f[S];
+      int p = 0, slot = 0;
+      for (; p + PD < nks; ++p) {
+        // memory phase (waves 0-3: while waves 4-7 compute stage p - 1)
+#pragma unroll
+        for (int u = 0; u < S; ++u) load_sub(slot, u, f[u]);
+        const int fill = slot + PD >= C::NST ? slot + PD - C::NST : slot + PD;
+        issue(kb0 + p + PD, fill);
+        const bool early = pend && p == 0;  // stage 1 was requested before the stores
+        if (grp == 1) {
+          if (early) wait_vmcnt<C::L + 16>();
+          else wait_vmcnt<C::L>();
+        }
+        reads_done();
+        sched_barrier_all();
+        // compute phase
+#pragma unroll
+        for (int u = 0; u < S; ++u) mma_sub(f[u]);
+        if (grp == 0) {
+          if (early) wait_vmcnt<C::L + 16>();
+          else wait_vmcnt<C::L>();
+        }
+        sched_barrier_all();
+        slot = slot + 1 == C::NST ? 0 : slot + 1;
+      }
+      for (; p < nks; ++p) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) load_sub(slot, u, f[u]);
+        if (grp == 1) {
+          if (pend && p == 0) wait_vmcnt<16>();
+          else wait_vmcnt<0>();
+        }
+        reads_done();
+        sched_barrier_all();
+#pragma unroll
+        for (int u = 0; u < S; ++u) mma_sub(f[u]);
+        if (grp == 0) {
+          if (pend && p == 0) wait_vmcnt<16>();
+          else wait_vmcnt<0>();
+        }
+        sched_barrier_all();
+        slot = slot + 1 == C::NST ? 0 : slot + 1;
+      }
+      if (grp == 0) sched_barrier_all();
+    } else {
     Frag f0, f1;
     wait_loads(min(C::NST - 2, nks - 1));
     barrier_nofence();
@@ -585,6 +648,7 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         slot = next;
       }
     }
+    }  // interleaved schedule
 
     // ------------------------------------------------------------ remainder split
     if (part >= 0) {  // the block's last item: nothing is in flight
@@ -606,6 +670,8 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       set_tile(nvt);
       issue_prologue();
     }
+    // A whole tile with aligned rows stores exactly MBLK * NBLK * 2 = 16 times per wave.
+    pend = PP && HALF_OUT && has_next && g.vec_store && cm0 + MX_BM <= g.m && cn0 + MX_BN <= g.n;
     // Output layout of a 32 x 32 block: lane holds column m = lane & 31 (activation row)
     // and, for group q = 0..3, rows n = 8q + 4 * (lane >> 5) + 0..3 (weight rows); the
     // block scales are already applied by the matrix cores.
@@ -743,10 +809,11 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uin
   g.ws_cnt = g.split > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
   g.ws_part = g.split > 1 ? reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(ws) + 4096) : nullptr;
   const int grid = g.items < pb ? g.items : pb;
-  // Two 64-deep sub-steps per ring stage for FP4 activations when K allows it (with FP6
-  // the doubled operand registers do not fit).
+  // FP4 activations: two 64-deep sub-steps per ring stage on the ping-pong schedule when K
+  // allows it.  FP6 activations stay at one sub-step on the interleaved schedule: with two
+  // sub-steps (42 KB stages, three in the ring) the ping-pong form measured 19% slower.
   const bool two = fa == MX_FP4 && k % 128 == 0;
-#define MXG(F, SS, O) hipLaunchKernelGGL((k_mxgemm<F, SS, O>), dim3(grid), dim3(MX_NT), 0, st, g)
+#define MXG(F, SS, O) hipLaunchKernelGGL((k_mxgemm<F, SS, O, SS == 2>), dim3(grid), dim3(MX_NT), 0, st, g)
 #define MXO(F, SS)                \
   if (out_dt == DT_F16)           \
     MXG(F, SS, DT_F16);           \

@@ -143,21 +143,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   int kb0 = 0, nks = nk;    // the item's first stage and stage count
   int part = -1, rslot = 0;  // K range of a split tile (-1: whole tile) and its remainder index
   auto set_tile = [&](int w) {
-    int ti = w;
-    if (w < g.dp_items) {
-      kb0 = 0;
-      nks = nk;
-      part = -1;
-    } else {
-      const int j = w - g.dp_items;
-      rslot = j / g.split;
-      part = j - rslot * g.split;
-      ti = g.dp_items + rslot;
-      kb0 = part * nk / g.split;
-      nks = (part + 1) * nk / g.split - kb0;
-    }
+    const WorkItem it = item_of(w, g.dp_items, g.split, nk);
+    kb0 = it.kb0;
+    nks = it.nks;
+    part = it.part;
+    rslot = it.rslot;
     int tm, tn;
-    tile_of(ti, g.tiles_m, g.tiles_n, tm, tn);
+    tile_of(it.tile, g.tiles_m, g.tiles_n, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
 #pragma unroll
@@ -195,7 +187,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // registers are spoken for by their wider ring, load them into registers early and write
   // them to LDS late.
   constexpr bool SC_DMA = H == 2;
-  float sc_a[P], sc_b[P];
+  // Register path: threads below BM hold a row scale, the others a column scale, both in
+  // sc[] (one array: conditional stores to two arrays were merged through a selected
+  // address and kept in scratch memory).
+  float sc[P];
   const int srow = tid & (BM - 1);  // register path: each thread loads one row or column scale
   auto load_scales = [&](int buf) {
     if constexpr (SC_DMA) {
@@ -210,13 +205,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
       }
     } else {
+      const float* src = tid < BM ? (g.sa_tok ? g.sa + (int64_t)min(m0 + srow, g.m - 1) * P : g.sa)
+                                  : g.sb + (int64_t)min(n0 + srow, g.n - 1) * P;
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (tid < BM)
-          sc_a[p] = g.sa_tok ? g.sa[(int64_t)min(m0 + srow, g.m - 1) * P + p] : g.sa[p];
-        else
-          sc_b[p] = g.sb[(int64_t)min(n0 + srow, g.n - 1) * P + p];
-      }
+      for (int p = 0; p < P; ++p) sc[p] = src[p];
     }
   };
   auto store_scales = [&](int buf) {
@@ -224,9 +216,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         if (tid < BM)
-          s_sa[buf][p][srow] = sc_a[p];
+          s_sa[buf][p][srow] = sc[p];
         else
-          s_sb[buf][p][srow] = sc_b[p];
+          s_sb[buf][p][srow] = sc[p];
       }
     }
   };
@@ -562,12 +554,6 @@ constexpr int STAGE = A_BYTES + BN * ROW;
 constexpr int LA = A_BYTES / (NT * 16);  // direct loads per wave per operand and stage (2)
 constexpr int L = 2 * LA;
 }  // namespace ppc
-
-__device__ __forceinline__ void sched_barrier_all() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int OUT_DT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm_pp(GArgs g) {
