@@ -87,7 +87,8 @@ def test_layer_matches_oracle(vq, case):
         assert np.array_equal(acc[p].cpu().numpy(), want), f"accumulators of partition {p}"
     want = np.asarray(r["y_store"])
     got = y.cpu().numpy() if case["out"] == "fp32" else gen.as_numpy_bits(y.cpu())
-    bad = np.flatnonzero(got.reshape(-1).view(want.dtype) != want.reshape(-1))
+    u = np.uint32 if case["out"] == "fp32" else np.uint16  # compare bit patterns (signed zeros too)
+    bad = np.flatnonzero(got.reshape(-1).view(u) != want.reshape(-1).view(u))
     assert bad.size == 0, f"outputs: {bad.size} mismatches, first at {bad[:5]}"
 
 
