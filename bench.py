@@ -380,13 +380,13 @@ def side_kernels(vq, gen, torch, dev, stream, head):
     codes = torch.empty((m, k), dtype=torch.int8, device=dev)
     scales = torch.empty(1, dtype=torch.float32, device=dev)
     us = launches_us(lambda: vq.vq_quant_act(x, 8, "tensor", codes=codes, scales=scales), torch, stream)
-    out["per_tensor_quant_c2"] = hbm_entry("k_fill_u32 + k_rowquant (maximum pass) + k_rowquant (codes) + "
+    out["per_tensor_quant_c2"] = hbm_entry("k_fill_u32 + k_tensor_absmax (maximum pass) + k_rowquant (codes) + "
                                            "k_tensor_finalize", f"c2 activations {m} x {k} bf16, dynamic per tensor",
                                            5 * m * k + 4, us)
     static = vq.vq_calib_static_scale(x, 8)["scale"]
     us = launches_us(lambda: vq.vq_quant_act(x, 8, "static", static_scale=static, codes=codes, scales=scales),
                      torch, stream)
-    out["static_quant_c2"] = hbm_entry("k_rowquant (static scale) + k_tensor_finalize",
+    out["static_quant_c2"] = hbm_entry("k_rowquant (static scale, one launch)",
                                        f"c2 activations {m} x {k} bf16, static per tensor", 3 * m * k + 4, us)
     del codes, scales
 
@@ -770,10 +770,10 @@ def main():
         out["roofline"]["kernel"] = "k_qgemm over all rows + k_qgemm over the stacked residual rows + k_residual_merge"
         out["act_quant"]["kernel"] = "k_rowquant + k_residual_quant"
     if L.gran == "tensor":
-        out["act_quant"]["kernel"] = ("k_fill_u32 + k_rowquant (maximum pass) + k_rowquant (codes) + k_tensor_finalize"
-                                      if L.M * L.K > 1 << 18 else "k_tensorquant_small (one launch)")
+        out["act_quant"]["kernel"] = ("k_fill_u32 + k_tensor_absmax (maximum pass) + k_rowquant (codes) + "
+                                      "k_tensor_finalize" if L.M * L.K > 1 << 18 else "k_tensorquant_small (one launch)")
     elif L.gran == "static":
-        out["act_quant"]["kernel"] = "k_rowquant (static scale) + k_tensor_finalize"
+        out["act_quant"]["kernel"] = "k_rowquant (static scale, one launch)"
     if not L.mx and not L.R and args.config != 5 and L.gran == "token":
         out["act_quant"]["stream_ref"] = stream_reference(L, torch, stream)
     if args.config == 5:

@@ -134,6 +134,12 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
     for (int p = 0; p < (DUAL ? 2 : 1); ++p) dyn_scale(a.gsrc[p], qf, r_g[p], s_g[p]);
   } else if constexpr (MODE == MODE_STATIC && !MAXONLY) {
     for (int p = 0; p < (DUAL ? 2 : 1); ++p) static_scale(a.gsrc[p], r_g[p], s_g[p]);
+    // The stored scale is the given one, bit for bit (so even an output that aliases the
+    // input keeps its value while other workgroups read it): no finalizing launch.
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      a.scales[0] = s_g[0];
+      if constexpr (DUAL) a.scales[1] = s_g[1];
+    }
   }
 
   float run_max[2] = {0.0f, 0.0f};  // MAXONLY running maxima
@@ -341,20 +347,16 @@ __global__ void k_fill_u32(unsigned* p, int n, unsigned v) {
   if (i < n) p[i] = v;
 }
 
-// Per-tensor scales after the codes: dynamic s = fl32(amax / Q), static s = given.
-__global__ void k_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
-                                  const int32_t* bits_dev) {
+// Dynamic per-tensor scales after the codes: the maxima the code pass read are replaced
+// by s = fl32(amax / Q).
+__global__ void k_tensor_finalize(float* scales, int parts, int qbits, const int32_t* bits_dev) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int b = bits_dev ? *bits_dev : qbits;
   b = (b == 4 || b == 6) ? b : 8;
   const float qf = (float)((1 << (b - 1)) - 1);
   for (int p = 0; p < parts; ++p) {
     float r, s;
-    if (static_src) {
-      static_scale(static_src[p], r, s);
-    } else {
-      dyn_scale(scales[p], qf, r, s);
-    }
+    dyn_scale(scales[p], qf, r, s);
     scales[p] = s;
   }
 }
@@ -653,9 +655,8 @@ hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
-                                  const int32_t* bits_dev, hipStream_t st) {
-  hipLaunchKernelGGL(k_tensor_finalize, dim3(1), dim3(64), 0, st, scales, static_src, parts, qbits, bits_dev);
+hipError_t launch_tensor_finalize(float* scales, int parts, int qbits, const int32_t* bits_dev, hipStream_t st) {
+  hipLaunchKernelGGL(k_tensor_finalize, dim3(1), dim3(64), 0, st, scales, parts, qbits, bits_dev);
   return hipGetLastError();
 }
 

@@ -198,13 +198,11 @@ vq_status vq_quant_act(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t
     p.gsrc = scales;
     e = vq_internal::launch_row_quant(p, stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(vq_internal::launch_tensor_finalize(scales, nullptr, parts, bits, bits_dev, stream));
+    return hip_status(vq_internal::launch_tensor_finalize(scales, parts, bits, bits_dev, stream));
   }
   p.mode = 2;
   p.gsrc = static_scale_dev;
-  e = vq_internal::launch_row_quant(p, stream);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(vq_internal::launch_tensor_finalize(scales, static_scale_dev, parts, bits, bits_dev, stream));
+  return hip_status(vq_internal::launch_row_quant(p, stream));
 }
 
 // ------------------------------------------------------------------ Hadamard

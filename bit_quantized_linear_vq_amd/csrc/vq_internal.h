@@ -41,8 +41,7 @@ hipError_t launch_tensor_absmax(const void* x, int dtype, int64_t ldx, int64_t r
                                 hipStream_t st);
 hipError_t launch_tensor_small(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int bits,
                                const int32_t* bits_dev, int8_t* codes, float* scales, hipStream_t st);
-hipError_t launch_tensor_finalize(float* scales, const float* static_src, int parts, int qbits,
-                                  const int32_t* bits_dev, hipStream_t st);
+hipError_t launch_tensor_finalize(float* scales, int parts, int qbits, const int32_t* bits_dev, hipStream_t st);
 
 hipError_t launch_hadamard(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, int64_t ldy,
                            int64_t rows, int64_t cols, int normalize, hipStream_t st);

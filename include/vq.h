@@ -143,8 +143,9 @@ vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int6
  * Launches: per token, one kernel; dynamic per tensor, one kernel for at most 2^18
  * elements without outlier partition or rotation (every workgroup reduces the whole
  * maximum itself), else a fill kernel that clears the maximum, a maximum pass, the code
- * pass and a one-thread finalize; static per tensor, the code pass and the finalize.  No
- * memset is enqueued, so a call may be captured in a graph.
+ * pass and a one-thread finalize; static per tensor, the code pass alone (it also copies
+ * the given scales to scales).  No memset is enqueued, so a call may be captured in a
+ * graph.
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED as for vq_pack_weights.
  */
 vq_status vq_quant_act(const void* x, vq_dtype dt, int64_t m, int64_t k, int64_t ldx, int bits,
