@@ -365,6 +365,9 @@ def side_kernels(vq, gen, torch, dev, stream, head):
     * the dual-scale quantizer of the 17776 x 3072 FFN-up activations (outlier channels
       from the weights' detection): 2 B read per element, 1 B per packed code (the outlier
       partition padded to 64 codes), 8 B of scales per row;
+    * the outlier detection on the 12288 x 3072 FFN-up weights (column norms, median, MAD,
+      flags), an offline step: 2 B read per element, whole calls including the copy of
+      the results to the host;
     * per-tensor activation scales on the 17776 x 1920 fused-QKV activations: dynamic (a
       maximum pass, then the code pass: 2 B read twice, 1 B written per element) and
       static (the clipping-percentile scale found offline: 2 B read, 1 B written);
@@ -407,7 +410,14 @@ def side_kernels(vq, gen, torch, dev, stream, head):
     m, k = x.shape
     w = gen.make_w(3).to(dev)
     _, idx, _ = vq.vq_detect_outliers(w)
-    del w
+    nw, kw = w.shape
+    ws = torch.empty(vq.vq_detect_workspace_elems(nw, kw), dtype=torch.float64, device=dev)
+    us = launches_us(lambda: vq.vq_detect_outliers(w, ws=ws), torch, stream, reps=20, warm=20)
+    out["detect_c3_weights"] = hbm_entry(
+        "k_colsumsq_partial + k_colsumsq_final + k_detect_flags", f"c3 weights {nw} x {kw} bf16, {int(idx.numel())} "
+        "outliers found", 2 * nw * kw, us, note="offline (once per weight tensor); each call copies its results to "
+        "the host and so waits for the device")
+    del w, ws
     idx = idx.to(dev)
     kp = vq.vq_packed_k(k, int(idx.numel()))
     codes = torch.empty((m, kp), dtype=torch.int8, device=dev)

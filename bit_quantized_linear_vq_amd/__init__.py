@@ -184,15 +184,21 @@ def _mx_ws_bytes(m: int, n: int, k: int) -> int:
     return int(_lib.vq_mx_gemm_workspace_bytes(m, n, k))
 
 
+def vq_detect_workspace_elems(rows: int, cols: int) -> int:
+    """Float64 elements of the device workspace vq_detect_outliers needs for x [rows x cols]."""
+    return int(_lib.vq_detect_workspace_elems(rows, cols))
+
+
 def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kfac: float = 1.0, ws=None,
                        n_out_dev=None):
     """Outlier input channels (columns) of x.  Returns (mask uint8 [K], idx int32 [n_out], norms f64 [K]) on the host;
     n_out_dev (device int32 [1]), if given, receives the count for vq_step_control."""
     _dev(x, "x")
     rows, cols = x.shape
+    need = vq_detect_workspace_elems(rows, cols)
     if ws is None:
-        ws = torch.empty(int(_lib.vq_detect_workspace_elems(rows, cols)), dtype=torch.float64, device=x.device)
-    _buf(ws, "ws", 8 * int(_lib.vq_detect_workspace_elems(rows, cols)), x.device)
+        ws = torch.empty(need, dtype=torch.float64, device=x.device)
+    _buf(ws, "ws", 8 * need, x.device)
     if n_out_dev is not None:
         _in(n_out_dev, "n_out_dev", _I32, 1, x.device)
     norms = torch.empty(cols, dtype=torch.float64)

@@ -17,6 +17,8 @@
 namespace vqk {
 
 constexpr int DET_MAX_CHUNKS = 256;
+constexpr int COLSUM_BATCH = 16;  // rows loaded together per thread in the column sums
+constexpr int COLFIN_BATCH = 32;  // chunk partials loaded together per thread in the final sums
 
 // Grid (column groups of 8 per thread, row chunks).  ws[chunk * cols + col].
 template <int DT>
@@ -30,20 +32,34 @@ __global__ __launch_bounds__(256) void k_colsumsq_partial(const void* __restrict
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const unsigned short* xs = reinterpret_cast<const unsigned short*>(x);
   const bool full = c0 + 8 <= cols;
-  for (int64_t r = r0; r < r1; ++r) {
+  auto add_row = [&](const u4v& w) {
+    float f[8];
+    decode2<DT>(w.x, f[0], f[1]);
+    decode2<DT>(w.y, f[2], f[3]);
+    decode2<DT>(w.z, f[4], f[5]);
+    decode2<DT>(w.w, f[6], f[7]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double d = (double)f[i];
+      acc[i] = __builtin_fma(d, d, acc[i]);  // d*d is exact in float64
+    }
+  };
+  int64_t r = r0;
+  if (full) {
+    // Rows in groups of COLSUM_BATCH: all loads of a group are issued before the first
+    // addition, which still runs in ascending row order.
+    for (; r + COLSUM_BATCH <= r1; r += COLSUM_BATCH) {
+      u4v w[COLSUM_BATCH];
+#pragma unroll
+      for (int j = 0; j < COLSUM_BATCH; ++j) w[j] = *reinterpret_cast<const u4v*>(xs + (r + j) * ldx + c0);
+#pragma unroll
+      for (int j = 0; j < COLSUM_BATCH; ++j) add_row(w[j]);
+    }
+  }
+  for (; r < r1; ++r) {
     const unsigned short* p = xs + r * ldx + c0;
     if (full) {
-      u4v w = *reinterpret_cast<const u4v*>(p);
-      float f[8];
-      decode2<DT>(w.x, f[0], f[1]);
-      decode2<DT>(w.y, f[2], f[3]);
-      decode2<DT>(w.z, f[4], f[5]);
-      decode2<DT>(w.w, f[6], f[7]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double d = (double)f[i];
-        acc[i] = __builtin_fma(d, d, acc[i]);  // d*d is exact in float64
-      }
+      add_row(*reinterpret_cast<const u4v*>(p));
     } else {
       for (int i = 0; i < 8 && c0 + i < cols; ++i) {
         const double d = (double)load1<DT>(x, r * ldx + c0 + i);
@@ -58,7 +74,16 @@ __global__ __launch_bounds__(256) void k_colsumsq_final(double* ws, int64_t cols
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   double s = 0.0;
-  for (int i = 0; i < chunks; ++i) s += ws[(int64_t)i * cols + c];
+  int i = 0;
+  // Loads in groups of COLFIN_BATCH (issued together), added in ascending chunk order.
+  for (; i + COLFIN_BATCH <= chunks; i += COLFIN_BATCH) {
+    double v[COLFIN_BATCH];
+#pragma unroll
+    for (int j = 0; j < COLFIN_BATCH; ++j) v[j] = ws[(int64_t)(i + j) * cols + c];
+#pragma unroll
+    for (int j = 0; j < COLFIN_BATCH; ++j) s += v[j];
+  }
+  for (; i < chunks; ++i) s += ws[(int64_t)i * cols + c];
   ws[(int64_t)chunks * cols + c] = s;
 }
 
@@ -77,26 +102,51 @@ struct DetectOut {
   uint8_t* mask;  // [cols]
 };
 
-// The rank-th smallest (0-based) of val(0..n-1), all non-negative and finite.
+// The rank0-th and rank1-th smallest (0-based) of val(0..n-1), all non-negative and
+// finite, found together: eight passes over 8-bit digits from the top, each building one
+// 256-bin histogram per rank of the values that share that rank's prefix so far (the two
+// middle ranks of an even count share most of their digits).  hist holds 512 bins,
+// s_sel and s_rem two entries.
 template <class F>
-__device__ double select_rank(F val, int n, int rank, unsigned* hist, int* s_sel, int* s_rem) {
+__device__ void select_ranks(F val, int n, int rank0, int rank1, unsigned* hist, int* s_sel, int* s_rem,
+                             double& out0, double& out1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t prefix = 0;
-  int rem = rank;
+  uint64_t prefix[2] = {0ull, 0ull};
+  int rem[2] = {rank0, rank1};
   for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0u;
+    for (int i = tid; i < 512; i += SEL_THREADS) hist[i] = 0u;
     __syncthreads();
     const uint64_t hi = shift == 56 ? 0ull : (~0ull << (shift + 8));
-    for (int i = tid; i < n; i += SEL_THREADS) {
-      const uint64_t b = (uint64_t)__double_as_longlong(val(i));
-      if ((b & hi) == prefix) atomicAdd(&hist[(b >> shift) & 255u], 1u);
+    // The leading digits of the norms mostly agree, and one LDS atomic per lane on a single
+    // bin serializes the pass: the lanes holding the digit of the wave's first active lane
+    // add their count with one atomic, the others (diverse digits) one each.
+    for (int base = 0; base < n; base += SEL_THREADS) {
+      const int i = base + tid;
+      uint64_t b = 0;
+      if (i < n) b = (uint64_t)__double_as_longlong(val(i));
+      const unsigned dig = (unsigned)(b >> shift) & 255u;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const bool act = i < n && (b & hi) == prefix[q];
+        const uint64_t am = __ballot(act);
+        if (am) {
+          const int leader = __ffsll((unsigned long long)am) - 1;
+          const unsigned d = __shfl(dig, leader, 64);
+          const bool mine = act && dig == d;
+          const uint64_t same = __ballot(mine);
+          if (lane == leader) atomicAdd(&hist[256 * q + d], (unsigned)__popcll(same));
+          if (act && !mine) atomicAdd(&hist[256 * q + dig], 1u);
+        }
+      }
     }
     __syncthreads();
-    if (wave == 0) {  // the digit whose cumulative count passes rem: lane l holds digits 4l..4l+3
+    if (wave < 2) {  // wave q: the digit whose cumulative count passes rem[q]; lane l holds digits 4l..4l+3
+      const int q = wave;
+      const int r = rem[q];
       unsigned c[4], own = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = hist[4 * lane + j];
+        c[j] = hist[256 * q + 4 * lane + j];
         own += c[j];
       }
       unsigned incl = own;
@@ -106,12 +156,12 @@ __device__ double select_rank(F val, int n, int rank, unsigned* hist, int* s_sel
         if (lane >= d) incl += v;
       }
       const unsigned excl = incl - own;
-      if (excl <= (unsigned)rem && (unsigned)rem < incl) {
+      if (excl <= (unsigned)r && (unsigned)r < incl) {
         unsigned cum = excl;
         for (int j = 0; j < 4; ++j) {
-          if (cum + c[j] > (unsigned)rem) {
-            *s_sel = 4 * lane + j;
-            *s_rem = rem - (int)cum;
+          if (cum + c[j] > (unsigned)r) {
+            s_sel[q] = 4 * lane + j;
+            s_rem[q] = r - (int)cum;
             break;
           }
           cum += c[j];
@@ -119,26 +169,30 @@ __device__ double select_rank(F val, int n, int rank, unsigned* hist, int* s_sel
       }
     }
     __syncthreads();
-    prefix |= (uint64_t)*s_sel << shift;
-    rem = *s_rem;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      prefix[q] |= (uint64_t)s_sel[q] << shift;
+      rem[q] = s_rem[q];
+    }
     __syncthreads();
   }
-  return __longlong_as_double((long long)prefix);
+  out0 = __longlong_as_double((long long)prefix[0]);
+  out1 = __longlong_as_double((long long)prefix[1]);
 }
 
+// Median: the middle value of an odd count, the mean of the two middle values of an even one.
 template <class F>
 __device__ double median_of(F val, int n, unsigned* hist, int* s_sel, int* s_rem) {
-  if (n & 1) return select_rank(val, n, n / 2, hist, s_sel, s_rem);
-  const double a = select_rank(val, n, n / 2 - 1, hist, s_sel, s_rem);
-  const double b = select_rank(val, n, n / 2, hist, s_sel, s_rem);
-  return 0.5 * (a + b);
+  double a, b;
+  select_ranks(val, n, (n - 1) / 2, n / 2, hist, s_sel, s_rem, a, b);
+  return (n & 1) ? b : 0.5 * (a + b);
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void k_detect_flags(const double* sums, int cols, double tau, double alpha,
                                                               double kfac, DetectOut o) {
   __shared__ double sv[SEL_LDS_VALUES];
-  __shared__ unsigned hist[256];
-  __shared__ int s_sel, s_rem;
+  __shared__ unsigned hist[512];
+  __shared__ int s_sel[2], s_rem[2];
   __shared__ int s_wcnt[SEL_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool in_lds = cols <= SEL_LDS_VALUES;
@@ -150,9 +204,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_detect_flags(const double* sums
   __syncthreads();
   const double* vg = o.norms;
   auto V = [&](int i) { return in_lds ? sv[i] : vg[i]; };
-  const double med = median_of(V, cols, hist, &s_sel, &s_rem);
+  const double med = median_of(V, cols, hist, s_sel, s_rem);
   auto D = [&](int i) { return fabs(V(i) - med); };
-  const double mad = median_of(D, cols, hist, &s_sel, &s_rem);
+  const double mad = median_of(D, cols, hist, s_sel, s_rem);
   const double amin = alpha * med;
 
   // Outliers in ascending order, then the normal channels in ascending order.
