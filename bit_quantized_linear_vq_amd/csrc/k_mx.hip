@@ -318,8 +318,8 @@ struct MxArgs {
   uint64_t* ws_part;
 };
 
-// Two schedules of the same K loop.  Interleaved (PP false): every wave reads the next
-// sub-step's fragments while the MFMAs of the current one run, one barrier per stage.
+// Two schedules of the same K loop.  Interleaved (PP false, S = 1): every wave reads the
+// next stage's fragments while the MFMAs of the current one run, one barrier per stage.
 // Ping-pong (PP true, S = 2): the two waves of a SIMD (w and w + 4) alternate between a
 // memory phase (the fragment reads of a whole stage and this wave's share of the refill
 // loads) and a compute phase (the stage's MFMAs from registers), waves 0-3 one phase
@@ -329,7 +329,8 @@ struct MxArgs {
 template <int FA, int S, int OUT_DT, bool PP>
 __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mxgemm(MxArgs g) {
   using C = MxCfg<FA, S>;
-  static_assert(!PP || (S == 2 && C::NST >= 3), "ping-pong: two sub-steps, three stages");
+  static_assert(PP ? (S == 2 && C::NST >= 3) : S == 1,
+                "ping-pong: two sub-steps, three stages; interleaved: one sub-step");
   constexpr int PD = 2;                         // ping-pong refill distance (stages)
   constexpr int PRO = PP ? PD : C::NST - 1;     // stages requested ahead of a tile
   constexpr bool HALF_OUT = OUT_DT != DT_F32;
@@ -584,44 +585,15 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       }
       if (grp == 0) sched_barrier_all();
     } else {
-    Frag f0, f1;
-    wait_loads(min(C::NST - 2, nks - 1));
-    barrier_nofence();
-    load_sub(0, 0, f0);
-    int kt = 0, slot = 0;
-    if constexpr (S == 2) {
-      // Stage kt holds two sub-steps.  The second sub-step's operands are read while the
-      // first one's MFMAs run; in the middle of the stage every wave waits for its loads
-      // of stage kt+1 and meets the others at a barrier, which publishes stage kt+1 and
-      // certifies that stage kt-1 is no longer read; that stage receives stage kt+NST-1,
-      // and the first sub-step of stage kt+1 is read while the second one's MFMAs run.
-      for (; kt < nks - (C::NST - 1); ++kt) {
-        const int next = slot + 1 == C::NST ? 0 : slot + 1;
-        const int refill = slot == 0 ? C::NST - 1 : slot - 1;
-        load_sub(slot, 1, f1);
-        mma_sub(f0);
-        wait_vmcnt<(C::NST - 3) * C::L>();
-        barrier_nofence();
-        issue(kb0 + kt + C::NST - 1, refill);
-        load_sub(next, 0, f0);
-        mma_sub(f1);
-        slot = next;
-      }
-      for (; kt < nks; ++kt) {
-        const int next = slot + 1 == C::NST ? 0 : slot + 1;
-        load_sub(slot, 1, f1);
-        mma_sub(f0);
-        if (kt + 1 < nks) {
-          wait_loads(nks - 2 - kt);
-          barrier_nofence();
-          load_sub(next, 0, f0);
-        }
-        mma_sub(f1);
-        slot = next;
-      }
-    } else {
+      Frag f0, f1;
+      wait_loads(min(C::NST - 2, nks - 1));
+      barrier_nofence();
+      load_sub(0, 0, f0);
+      int kt = 0, slot = 0;
       // One sub-step per stage: the MFMAs of weight block 0 run on operands read during
-      // stage kt-1, then the barrier as above, then the operands of stage kt+1 are read
+      // stage kt-1; then every wave waits for its loads of stage kt+1 and meets the others
+      // at a barrier, which publishes stage kt+1 and certifies that stage kt-1 is no longer
+      // read (that slot receives stage kt+NST-1); then the operands of stage kt+1 are read
       // while the MFMAs of weight block 1 run.
       for (; kt < nks - (C::NST - 1); ++kt) {
         const int next = slot + 1 == C::NST ? 0 : slot + 1;
@@ -647,7 +619,6 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         f0 = f1;
         slot = next;
       }
-    }
     }  // interleaved schedule
 
     // ------------------------------------------------------------ remainder split
