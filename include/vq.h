@@ -144,7 +144,7 @@ vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int6
  * elements without outlier partition or rotation (every workgroup reduces the whole
  * maximum itself), else a fill kernel that clears the maximum, a maximum pass, the code
  * pass and a one-thread finalize; static per tensor, the code pass alone (it also copies
- * the given scales to scales).  No memset is enqueued, so a call may be captured in a
+ * the given scales to scales, which may alias static_scale_dev).  No memset is enqueued, so a call may be captured in a
  * graph.
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED as for vq_pack_weights.
  */

@@ -129,6 +129,28 @@ def test_quant_static_scale(vq):
     assert np.abs(rc).max() == 127  # the static scale clips
 
 
+@pytest.mark.parametrize("dual", [False, True])
+def test_quant_static_scale_one_launch(vq, dual):
+    """Static per-tensor scales in one launch (the code pass also stores the given scales):
+    codes and stored scales against the oracle over many workgroups, with the outlier
+    partition's second scale, and with the scale output aliasing the given scales."""
+    x = gen.make_x(3, m=700)
+    idx = gen.w_outlier_channels(3).astype(np.int32) if dual else None
+    idx_d = None if idx is None else torch.from_numpy(idx).to(DEV)
+    s = torch.tensor([0.03, 0.6][: 2 if dual else 1], dtype=torch.float32)
+    codes, scales = vq.vq_quant_act(x.to(DEV), 8, "static", idx=idx_d, static_scale=s.to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oq.quant_act(npb(x), "bf16", 8, "static", 0, idx, static_scale=s.numpy())
+    assert_same(codes.cpu().numpy(), rc, "codes")
+    assert_same(scales.cpu().numpy(), rs, "scales")
+    same = s.to(DEV)
+    codes2, out = vq.vq_quant_act(x.to(DEV), 8, "static", idx=idx_d, static_scale=same, scales=same)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == same.data_ptr()
+    assert torch.equal(codes2, codes), "codes with the scales aliased"
+    assert_same(same.cpu().numpy(), rs, "aliased scales")
+
+
 @pytest.mark.parametrize("gran", ["token", "tensor"])
 def test_quant_dual_c3_small(vq, gran):
     x = gen.make_x(3, m=300)
