@@ -511,6 +511,28 @@ def test_detect_order_statistics_exact(vq, cols):
     np.testing.assert_allclose(norms.numpy(), r["norms"], rtol=1e-12)
 
 
+@pytest.mark.parametrize("cols", [3000, 5001])
+def test_detect_norms_over_many_binades(vq, cols):
+    """Column norms spread over sixty binades: the leading digits of the float64 patterns
+    differ between columns, so the selection's histograms take the per-lane path as well as
+    the wave-aggregated one; median, MAD and flags still match the rule on the device norms
+    and the oracle's own decision."""
+    g = np.random.default_rng(cols)
+    x = g.standard_normal((16, cols)).astype(np.float32)
+    x *= np.exp2(g.integers(-30, 30, cols)).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    pad = torch.zeros((16, (cols + 7) // 8 * 8), dtype=torch.bfloat16)
+    pad[:, :cols] = t
+    mask, idx, norms = vq.vq_detect_outliers(pad.to(DEV)[:, :cols])
+    fm, fidx, _, _, _ = odetect.flag_outliers(norms.numpy())
+    assert_same(mask.numpy().astype(bool), fm, "mask")
+    assert_same(idx.numpy(), fidx, "indices")
+    r = oracle.linear.detect_on(npb(t), "bf16")
+    np.testing.assert_allclose(norms.numpy(), r["norms"], rtol=1e-12)
+    assert_same(idx.numpy(), r["idx"], "indices against the oracle")
+    assert idx.numel() > 0
+
+
 def test_detect_zero_mad(vq):
     """More than half of the norms equal: MAD = 0, so every larger norm above alpha * median is flagged."""
     x = torch.ones((4, 64), dtype=torch.float32)
