@@ -65,6 +65,9 @@ def parse():
                         "from graphs of G launches.  Default: 10 for the 256 x 512 x 512 workload, whose "
                         "kernels take less time than the binding's host work per call, else 1 with --graph "
                         "and host launches without it")
+    p.add_argument("--w-layout", choices=["kblock", "row"], default="kblock",
+                   help="layout of the packed integer weights: 64-byte K pieces (each GEMM stage of a weight "
+                        "tile whole cache lines) or row-major")
     p.add_argument("--residual-frac", type=float, default=0.0, metavar="F",
                    help="decompose a seeded fraction F of the tokens (residual re-quantization added back "
                         "in the epilogue); per-token workloads without dual scale or rotation only")
@@ -126,7 +129,7 @@ def load_traffic(workload):
 class Layer:
     """Device buffers and launch closures for one configuration."""
 
-    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0, mx=None, gran=None):
+    def __init__(self, cfg, vq, gen, torch, dev, residual_frac=0.0, mx=None, gran=None, w_layout="kblock"):
         c = gen.CONFIGS[cfg]
         self.mx = mx
         self.cfg, self.c = cfg, c
@@ -149,7 +152,7 @@ class Layer:
             self.bits_dev = []
             for l in range(self.layers):
                 w = gen.make_w(cfg, layer=l).to(dev)
-                self.w.append(vq.vq_pack_weights(w, c["w_bits"]))
+                self.w.append(vq.vq_pack_weights(w, c["w_bits"], kblock=w_layout == "kblock"))
                 del w
                 xp, yp, _ = gen.make_route_pair(cfg, l)
                 bits, _ = vq.vq_route_rel_l1(xp.to(dev), yp.to(dev), c["route_threshold"],
@@ -179,7 +182,7 @@ class Layer:
             if c["dual"]:
                 _, idx, _ = vq.vq_detect_outliers(w)
                 self.idx = idx.to(dev)
-            self.w = [vq.vq_pack_weights(w, c["w_bits"], self.idx, self.had)]
+            self.w = [vq.vq_pack_weights(w, c["w_bits"], self.idx, self.had, kblock=w_layout == "kblock")]
             self.bits_dev = [None]
             del w
         n_out = 0 if self.idx is None else int(self.idx.numel())
@@ -642,7 +645,7 @@ def main():
     if args.dense:
         dense(args, vq, gen, torch, dev)
         return
-    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx, args.act_gran)
+    L = Layer(args.config, vq, gen, torch, dev, args.residual_frac, args.mx, args.act_gran, args.w_layout)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -757,6 +760,7 @@ def main():
                    "w_bits": L.c["w_bits"], "a_bits": L.c["a_bits"] if L.c["a_bits"] else "routed 8/4",
                    "act_granularity": L.gran, "hadamard_block": L.had,
                    "outlier_channels": 0 if L.idx is None else int(L.idx.numel()),
+                   "weight_layout": "64-byte K pieces" if args.w_layout == "kblock" else "row-major",
                    "out_dtype": str(L.y.dtype).replace("torch.", "")},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,

@@ -24,9 +24,10 @@ VQ_MXFP6, VQ_MXFP4 = 2, 4
 VQ_K_ALIGN = 64
 VQ_HAD_BLOCK = 128
 VQ_MAX_OUTLIERS = 128
+VQ_W_KBLOCK = 0x100  # weight layout flag: 64-byte K pieces, piece j of every row together
 
 EXPORTS = (
-    "vq_outlier_part_len", "vq_packed_k", "vq_detect_workspace_elems", "vq_detect_outliers",
+    "vq_outlier_part_len", "vq_packed_k", "vq_weight_bytes", "vq_detect_workspace_elems", "vq_detect_outliers",
     "vq_pack_weights", "vq_quant_act", "vq_hadamard_block", "vq_qgemm_dequant", "vq_qgemm_workspace_bytes",
     "vq_qgemm_scratch_bytes", "vq_qgemm_dequant_noalloc",
     "vq_route_workspace_elems", "vq_route_rel_l1", "vq_quant_residual", "vq_residual_workspace_bytes",
@@ -60,6 +61,7 @@ def _load():
     sig = {
         "vq_outlier_part_len": (I64, [I32]),
         "vq_packed_k": (I64, [I64, I32]),
+        "vq_weight_bytes": (I64, [I64, I64, I]),
         "vq_detect_workspace_elems": (I64, [I64, I64]),
         "vq_detect_outliers": (I, [P, I, I64, I64, I64, D, D, D, P, P, P, P, P, P, P]),
         "vq_control_workspace_elems": (I64, []),
@@ -211,26 +213,42 @@ def vq_detect_outliers(x: torch.Tensor, tau: float = 3.5, alpha: float = 2.0, kf
     return mask, idx[: n_out.value].clone(), norms
 
 
+def vq_weight_bytes(n: int, kp: int, wfmt: int) -> int:
+    return int(_lib.vq_weight_bytes(n, kp, wfmt))
+
+
 def vq_pack_weights(w: torch.Tensor, bits: int, idx: torch.Tensor | None = None, had_block: int = 0,
-                    codes=None, scales=None):
-    """Per-output-channel codes of W [N x K].  Returns (codes, scales)."""
+                    codes=None, scales=None, kblock: bool = False):
+    """Per-output-channel codes of W [N x K].  Returns (codes, scales).
+
+    codes are int8 [N x kp] (8-bit) or uint8 [N x kp/2] (4-bit, two per byte); with
+    kblock=True the same codes in 64-byte K pieces, [pieces x N x 64] (the GEMM calls take
+    either form and tell them apart by the tensor's rank)."""
     _dev(w, "w")
     n, k = w.shape
     n_out = 0 if idx is None else int(idx.numel())
     if idx is not None:
         _in(idx, "idx", _I32, n_out, w.device)
     kp = vq_packed_k(k, n_out)
+    wfmt = bits | (VQ_W_KBLOCK if kblock else 0)
+    dt = torch.int8 if bits == 8 else torch.uint8
+    row_bytes = kp if bits == 8 else kp // 2
     if codes is None:
-        codes = (torch.empty((n, kp), dtype=torch.int8, device=w.device) if bits == 8
-                 else torch.empty((n, kp // 2), dtype=torch.uint8, device=w.device))
+        shape = ((row_bytes + 63) // 64, n, 64) if kblock else (n, row_bytes)
+        codes = torch.empty(shape, dtype=dt, device=w.device)
     if scales is None:
         scales = torch.empty((n, 2) if n_out else (n,), dtype=torch.float32, device=w.device)
-    _buf(codes, "codes", n * (kp if bits == 8 else kp // 2), w.device)
+    _buf(codes, "codes", vq_weight_bytes(n, kp, wfmt) if bits in (4, 8) else 0, w.device)
     _buf(scales, "scales", 4 * n * (2 if n_out else 1), w.device)
     _check("vq_pack_weights", _lib.vq_pack_weights(
-        _ptr(w), _DT.get(w.dtype, -1), n, k, w.stride(0), bits, _ptr(idx), n_out, had_block,
+        _ptr(w), _DT.get(w.dtype, -1), n, k, w.stride(0), wfmt, _ptr(idx), n_out, had_block,
         _ptr(codes), _ptr(scales), _stream(w)))
     return codes, scales
+
+
+def vq_kblock_to_rows(codes: torch.Tensor, n: int, row_bytes: int) -> torch.Tensor:
+    """The row-major [N x row_bytes] view of weight codes in 64-byte K pieces (a copy)."""
+    return codes.reshape(-1, n, 64).permute(1, 0, 2).reshape(n, -1)[:, :row_bytes].contiguous()
 
 
 def vq_quant_act(x: torch.Tensor, bits: int, gran: str = "token", had_block: int = 0,
@@ -285,9 +303,8 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
     given, False runs without the remainder split."""
     _dev(a, "a")
     m, kp = a.shape
-    n = b.shape[0]
     k0 = kp if k0 is None else k0
-    _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token)
+    n, wfmt = _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token)
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if acc_debug and acc is None:
@@ -299,7 +316,7 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
     if ws is not False:
         _buf(ws, "ws", _qgemm_ws_bytes(m, n, k0), a.device)
     _check("vq_qgemm_dequant", _lib.vq_qgemm_dequant(
-        _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
+        _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), wfmt, _ptr(sb), m, n, kp, k0,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(acc if acc_debug else None),
         None if ws is False else _ptr(ws), _stream(a)))
     return (y, acc) if acc_debug else y
@@ -307,25 +324,32 @@ def vq_qgemm_dequant(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: tor
 
 def _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token=True):
     """The GEMM's codes and scales as the kernels read them: A int8 [M x kp] dense; B int8
-    [N x kp] (8-bit weights) or uint8 [N x kp/2] (4-bit); scales float32 with one or two
-    partitions (k0 < kp: two per row, column and tensor)."""
+    [N x kp] (8-bit weights) or uint8 [N x kp/2] (4-bit), or those codes in 64-byte K
+    pieces [pieces x N x 64] (vq_pack_weights(..., kblock=True)); scales float32 with one
+    or two partitions (k0 < kp: two per row, column and tensor).  Returns (N, the weight
+    format for the library: b_bits, with VQ_W_KBLOCK for the pieces)."""
     dev = a.device
     m = a.shape[0]
     parts = 2 if k0 < kp else 1
     _in(a, "a", (torch.int8,), m * kp, dev)
-    if not (isinstance(b, torch.Tensor) and b.dim() == 2):
-        raise TypeError("b must be a 2-D CUDA (HIP) tensor of packed weight codes")
-    n = b.shape[0]
-    if b_bits == 8:
-        _in(b, "b", (torch.int8,), n * kp, dev)
-        if b.shape[1] != kp:
-            raise ValueError(f"b must be [N x {kp}] int8 codes for 8-bit weights")
-    elif b_bits == 4:
-        _in(b, "b", _U8, n * kp // 2, dev)
-        if b.shape[1] != kp // 2:
-            raise ValueError(f"b must be [N x {kp // 2}] packed nibbles for 4-bit weights")
+    if not (isinstance(b, torch.Tensor) and b.dim() in (2, 3)):
+        raise TypeError("b must be a 2-D (row-major) or 3-D (K pieces) CUDA (HIP) tensor of packed weight codes")
+    kblock = b.dim() == 3
+    n = b.shape[1] if kblock else b.shape[0]
+    if b_bits in (4, 8):
+        row_bytes = kp if b_bits == 8 else kp // 2
+        dts = (torch.int8,) if b_bits == 8 else _U8
+        what = "int8 codes for 8-bit weights" if b_bits == 8 else "packed nibbles for 4-bit weights"
+        _in(b, "b", dts, 0, dev)  # device, dtype and density first; then the shape fixes the size
+        if kblock:
+            pieces = (row_bytes + 63) // 64
+            if tuple(b.shape) != (pieces, n, 64):
+                raise ValueError(f"b in K pieces must be [{pieces} x N x 64] {what}")
+        elif b.shape[1] != row_bytes:
+            raise ValueError(f"b must be [N x {row_bytes}] {what}")
     _in(sa, "sa", _F32, (m if sa_per_token else 1) * parts, dev)
     _in(sb, "sb", _F32, n * parts, dev)
+    return n, b_bits | (VQ_W_KBLOCK if kblock else 0)
 
 
 def vq_qgemm_dequant_noalloc(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor, b_bits: int,
@@ -334,12 +358,11 @@ def vq_qgemm_dequant_noalloc(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
     split uses the library's static scratch; overlapping calls on one GPU race)."""
     _dev(a, "a")
     m, kp = a.shape
-    n = b.shape[0]
     k0 = kp if k0 is None else k0
-    _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token)
+    n, wfmt = _check_gemm_operands(a, sa, b, sb, b_bits, kp, k0, sa_per_token)
     _out2d(y, "y", m, n, a.device)
     _check("vq_qgemm_dequant_noalloc", _lib.vq_qgemm_dequant_noalloc(
-        _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), b_bits, _ptr(sb), m, n, kp, k0,
+        _ptr(a), _ptr(sa), int(bool(sa_per_token)), _ptr(b), wfmt, _ptr(sb), m, n, kp, k0,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _stream(a)))
     return y
 
@@ -453,21 +476,20 @@ def vq_qgemm_dequant_residual(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor
     """Y = dequant(A . B^T); listed rows get both terms of the stacked operand (a2, sa2) added before rounding."""
     _dev(a, "a")
     m, kp = a.shape
-    n = b.shape[0]
+    n, wfmt = _check_gemm_operands(a, sa, b, sb, b_bits, kp, kp)
     n_rows = int(rows.numel())
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if ws is None and n_rows:
         ws = torch.empty(vq_residual_workspace_bytes(m, n_rows, n), dtype=torch.uint8, device=a.device)
     _out2d(y, "y", m, n, a.device)
-    _check_gemm_operands(a, sa, b, sb, b_bits, kp, kp)
     if n_rows:
         _in(rows, "rows", _I32, n_rows, a.device)
         _in(a2, "a2", (torch.int8,), 2 * n_rows * kp, a.device)
         _in(sa2, "sa2", _F32, 2 * n_rows, a.device)
         _buf(ws, "ws", vq_residual_workspace_bytes(m, n_rows, n), a.device)
     _check("vq_qgemm_dequant_residual", _lib.vq_qgemm_dequant_residual(
-        _ptr(a), _ptr(sa), _ptr(b), b_bits, _ptr(sb), m, n, kp, _ptr(a2), _ptr(sa2), _ptr(rows), n_rows,
+        _ptr(a), _ptr(sa), _ptr(b), wfmt, _ptr(sb), m, n, kp, _ptr(a2), _ptr(sa2), _ptr(rows), n_rows,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), _ptr(ws), _stream(a)))
     return y
 

@@ -89,7 +89,21 @@ struct GArgs {
   int items;         // dp_items + (tiles - dp_items) * split
   int32_t* ws_cnt;   // [tiles - dp_items] arrival counters (zero between calls)
   uint64_t* ws_part;  // [(tiles - dp_items) * split][64][NT] partial accumulators (int32 pairs)
+  int64_t b_kp;  // weights in 64-byte K pieces: bytes from one piece to the next (64 n)
 };
+
+// Weight addressing, fixed per kernel instance (KB: the layout of 64-byte K pieces, piece
+// j of every row stored together).  Bytes from one row to the next, and the offset of byte
+// c of a row from the row's first byte.
+template <bool KB>
+__device__ __forceinline__ int64_t wrow(const GArgs& g, int bbits) {
+  return KB ? 64 : (bbits == 8 ? g.kp : g.kp / 2);
+}
+template <bool KB>
+__device__ __forceinline__ int64_t wofs(const GArgs& g, int c) {
+  if constexpr (KB) return (int64_t)(c >> 6) * g.b_kp + (c & 63);
+  else return c;
+}
 
 __device__ __forceinline__ v4i unpack_int4x16(u2v w) {
   const unsigned h0 = w.x & 0xF0F0F0F0u, l0 = (w.x << 4) & 0xF0F0F0F0u;
@@ -102,7 +116,7 @@ __device__ __forceinline__ v4i unpack_int4x16(u2v w) {
   return r;
 }
 
-template <int BBITS, int OUT_DT, bool DUAL, int H>
+template <int BBITS, int OUT_DT, bool DUAL, int H, bool KB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm(GArgs g) {
   static_assert(!DUAL || H == 2 || (H == 4 && BBITS == 4),
                 "the outlier partition is staged in 64-code stages, or in one 128-code stage");
@@ -136,7 +150,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     dma_lane<C::B_ROW>(q, lane, rb[i], cb[i]);
     lb_off[i] = C::A_BYTES + q * 1024;
   }
-  const int64_t ldb = BBITS == 8 ? g.kp : g.kp / 2;
   const int8_t* ga[C::LA];
   const uint8_t* gb[C::LB];
   int m0 = 0, n0 = 0;
@@ -155,7 +168,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) ga[i] = g.a + (int64_t)min(m0 + ra[i], g.m - 1) * g.kp + ca[i];
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * ldb + cb[i];
+    for (int i = 0; i < C::LB; ++i) gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * wrow<KB>(g, BBITS) + cb[i];
   };
   auto issue = [&](int k, int slot) {
     uint8_t* base = lds + slot * C::STAGE;
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int i = 0; i < C::LA; ++i) dma16(ga[i] + k, base + la_off[i]);
     const int kb = BBITS == 8 ? k : k / 2;
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) dma16(gb[i] + kb, base + lb_off[i]);
+    for (int i = 0; i < C::LB; ++i) dma16(gb[i] + wofs<KB>(g, kb), base + lb_off[i]);
   };
   // The outlier partition [k0, kp) of 64 or 128 codes as one 128-code stage: columns past
   // the partition wrap to its start (mask), so every load stays inside the row's
@@ -172,7 +185,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) dma16(ga[i] - ca[i] + (ca[i] & amask) + g.k0, lds + la_off[i]);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) dma16(gb[i] - cb[i] + (cb[i] & bmask) + g.k0 / 2, lds + lb_off[i]);
+    for (int i = 0; i < C::LB; ++i) dma16(gb[i] - cb[i] + (cb[i] & bmask) + wofs<KB>(g, g.k0 / 2), lds + lb_off[i]);
   };
   auto issue_prologue = [&]() {
 #pragma unroll
@@ -555,7 +568,7 @@ constexpr int LA = A_BYTES / (NT * 16);  // direct loads per wave per operand an
 constexpr int L = 2 * LA;
 }  // namespace ppc
 
-template <int OUT_DT>
+template <int OUT_DT, bool KB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qgemm_pp(GArgs g) {
   using namespace ppc;
   constexpr bool HALF_OUT = OUT_DT != DT_F32;
@@ -585,7 +598,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       ga[i] = g.a + (int64_t)min(m0 + ra[i], g.m - 1) * g.kp + ca[i];
-      gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * g.kp + cb[i];
+      gb[i] = g.b + (int64_t)min(n0 + rb[i], g.n - 1) * wrow<KB>(g, 8) + cb[i];
     }
   };
   auto issue = [&](int k, int slot) {
@@ -593,7 +606,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int i = 0; i < LA; ++i) dma16(ga[i] + k, base + (wave * LA + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < LA; ++i) dma16(gb[i] + k, base + A_BYTES + (wave * LA + i) * 1024);
+    for (int i = 0; i < LA; ++i) dma16(gb[i] + wofs<KB>(g, k), base + A_BYTES + (wave * LA + i) * 1024);
   };
   // Scales straight to LDS, one direct load per wave, ahead of the tile's first stage.
   auto load_scales = [&](int buf) {
@@ -772,7 +785,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 constexpr int SMALL_KB = 8;           // 32-deep steps per load batch
 constexpr int SMALL_MAX_TILES = 16;   // 256 x 256 tiles up to which this kernel is taken
 
-template <int OUT_DT>
+template <int OUT_DT, bool KB>
 __global__ __launch_bounds__(64) void k_qgemm_small(GArgs g) {
   const int lane = threadIdx.x;
   const int m0 = blockIdx.x * 32;
@@ -787,7 +800,7 @@ __global__ __launch_bounds__(64) void k_qgemm_small(GArgs g) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sbv[q][r] = g.sb[min(n0 + 8 * q + 4 * kc + r, g.n - 1)];
   const int8_t* pa = g.a + (int64_t)min(m0 + rl, g.m - 1) * g.kp + 16 * kc;
-  const uint8_t* pb = g.b + (int64_t)min(n0 + rl, g.n - 1) * g.kp + 16 * kc;
+  const uint8_t* pb = g.b + (int64_t)min(n0 + rl, g.n - 1) * wrow<KB>(g, 8) + 16 * kc;
   const int nks = g.k0 / 32;
   v16i acc = v16i{};
   v4i fa[2][SMALL_KB], fb[2][SMALL_KB];
@@ -796,7 +809,7 @@ __global__ __launch_bounds__(64) void k_qgemm_small(GArgs g) {
     for (int u = 0; u < SMALL_KB; ++u) {
       const int ks = min(kb * SMALL_KB + u, nks - 1);  // past the end: a valid step, not used
       fa[set][u] = *reinterpret_cast<const v4i*>(pa + 32 * ks);
-      fb[set][u] = *reinterpret_cast<const v4i*>(pb + 32 * ks);
+      fb[set][u] = *reinterpret_cast<const v4i*>(pb + wofs<KB>(g, 32 * ks));
     }
   };
   auto mma = [&](int set, int kb) {
@@ -843,27 +856,47 @@ __global__ __launch_bounds__(64) void k_qgemm_small(GArgs g) {
   }
 }
 
-template <int BBITS, int OUT_DT>
+template <int BBITS, int OUT_DT, bool KB>
 static hipError_t launch_dual(const GArgs& a, bool dual, int grid, hipStream_t st) {
   const int part = a.kp - a.k0;
   if (dual && BBITS == 4 && a.k0 % 128 == 0 && (part == 64 || part == 128))  // 128-code stages
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, BBITS == 4 ? 4 : 2>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, BBITS == 4 ? 4 : 2, KB>), dim3(grid), dim3(NT), 0, st, a);
   else if (dual)
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, 2>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, true, 2, KB>), dim3(grid), dim3(NT), 0, st, a);
   else if (BBITS == 4 && a.k0 % 128 == 0)  // 4-bit weights: 128-code stages
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, BBITS == 4 ? 4 : 2>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, BBITS == 4 ? 4 : 2, KB>), dim3(grid), dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, 2>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_qgemm<BBITS, OUT_DT, false, 2, KB>), dim3(grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
-template <int BBITS>
+template <int BBITS, bool KB>
 static hipError_t launch_out(const GArgs& a, int out_dt, bool dual, int grid, hipStream_t st) {
   switch (out_dt) {
-    case DT_F16: return launch_dual<BBITS, DT_F16>(a, dual, grid, st);
-    case DT_BF16: return launch_dual<BBITS, DT_BF16>(a, dual, grid, st);
-    default: return launch_dual<BBITS, DT_F32>(a, dual, grid, st);
+    case DT_F16: return launch_dual<BBITS, DT_F16, KB>(a, dual, grid, st);
+    case DT_BF16: return launch_dual<BBITS, DT_BF16, KB>(a, dual, grid, st);
+    default: return launch_dual<BBITS, DT_F32, KB>(a, dual, grid, st);
   }
+}
+
+template <bool KB>
+static hipError_t launch_small(const GArgs& a, int out_dt, dim3 sg, hipStream_t st) {
+  switch (out_dt) {
+    case DT_F16: hipLaunchKernelGGL((k_qgemm_small<DT_F16, KB>), sg, dim3(64), 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL((k_qgemm_small<DT_BF16, KB>), sg, dim3(64), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_qgemm_small<DT_F32, KB>), sg, dim3(64), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool KB>
+static hipError_t launch_pp(const GArgs& a, int out_dt, int grid, hipStream_t st) {
+  switch (out_dt) {
+    case DT_F16: hipLaunchKernelGGL((k_qgemm_pp<DT_F16, KB>), dim3(grid), dim3(NT), 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL((k_qgemm_pp<DT_BF16, KB>), dim3(grid), dim3(NT), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_qgemm_pp<DT_F32, KB>), dim3(grid), dim3(NT), 0, st, a); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace vqk
@@ -907,6 +940,7 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.k0 = (int)p.k0;
   a.ldy = p.ldy;
   a.sa_tok = p.sa_per_token;
+  a.b_kp = 64 * p.n;
   const int64_t esize = p.out_dt == DT_F32 ? 4 : 2;
   a.vec_store = ((reinterpret_cast<uintptr_t>(p.y) & 15u) == 0 && (p.ldy * esize) % 16 == 0) ? 1 : 0;
   a.tiles_m = (int)((p.m + BM - 1) / BM);
@@ -923,25 +957,16 @@ hipError_t launch_qgemm(const GemmParams& p, hipStream_t st) {
   a.ws_part = split > 1 ? reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(p.ws) + QGEMM_WS_COUNTERS) : nullptr;
   const int grid = a.items < pb ? a.items : pb;
   const bool dual = p.k0 < p.kp;
+  const bool kb = p.b_kblock != 0;
   if (p.b_bits == 8 && !dual && tiles <= SMALL_MAX_TILES) {
     const dim3 sg((unsigned)((p.m + 31) / 32), (unsigned)((p.n + 31) / 32));
-    switch (p.out_dt) {
-      case DT_F16: hipLaunchKernelGGL(k_qgemm_small<DT_F16>, sg, dim3(64), 0, st, a); break;
-      case DT_BF16: hipLaunchKernelGGL(k_qgemm_small<DT_BF16>, sg, dim3(64), 0, st, a); break;
-      default: hipLaunchKernelGGL(k_qgemm_small<DT_F32>, sg, dim3(64), 0, st, a); break;
-    }
-    return hipGetLastError();
+    return kb ? launch_small<true>(a, p.out_dt, sg, st) : launch_small<false>(a, p.out_dt, sg, st);
   }
-  if (p.b_bits == 8 && !dual && split == 1) {
-    switch (p.out_dt) {
-      case DT_F16: hipLaunchKernelGGL(k_qgemm_pp<DT_F16>, dim3(grid), dim3(NT), 0, st, a); break;
-      case DT_BF16: hipLaunchKernelGGL(k_qgemm_pp<DT_BF16>, dim3(grid), dim3(NT), 0, st, a); break;
-      default: hipLaunchKernelGGL(k_qgemm_pp<DT_F32>, dim3(grid), dim3(NT), 0, st, a); break;
-    }
-    return hipGetLastError();
-  }
-  if (p.b_bits == 8) return launch_out<8>(a, p.out_dt, dual, grid, st);
-  return launch_out<4>(a, p.out_dt, dual, grid, st);
+  if (p.b_bits == 8 && !dual && split == 1)
+    return kb ? launch_pp<true>(a, p.out_dt, grid, st) : launch_pp<false>(a, p.out_dt, grid, st);
+  if (p.b_bits == 8)
+    return kb ? launch_out<8, true>(a, p.out_dt, dual, grid, st) : launch_out<8, false>(a, p.out_dt, dual, grid, st);
+  return kb ? launch_out<4, true>(a, p.out_dt, dual, grid, st) : launch_out<4, false>(a, p.out_dt, dual, grid, st);
 }
 
 // ---- scratch-free entry: the remainder split's workspace in a static device array.

@@ -45,6 +45,7 @@ struct RowArgs {
   float scale_mul;     // exact factor folded into the stored scale (1/128 after rotation)
   void* codes;         // int8 [rows x kp] or packed uint8 [rows x kp/2]
   float* scales;       // MODE_ROW: [rows] or [rows x 2]; MAXONLY: absmax target [P]
+  int64_t c_kp;        // KBLK: bytes between 64-byte K pieces (64 rows)
 };
 
 __device__ __forceinline__ float qmax_f(const RowArgs& a) {
@@ -68,7 +69,9 @@ __device__ __forceinline__ void decode8(const u4v& w, float* v) {
   decode2<DT>(w.w, v[6], v[7]);
 }
 
-template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY, int NP>
+// KBLK: the codes go out in 64-byte K pieces (byte c of row r at (c / 64) * c_kp +
+// 64 r + c % 64), the weight layout whose GEMM stages are whole cache lines.
+template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY, int NP, bool KBLK>
 __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   static_assert(!(HAD && DUAL), "the rotation and the outlier partition are not combined");
   __shared__ float s_red[8][2];
@@ -143,6 +146,13 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
   }
 
   float run_max[2] = {0.0f, 0.0f};  // MAXONLY running maxima
+
+  // Byte c of row `row`'s codes.
+  auto code_at = [&](int64_t row, int c) -> uint8_t* {
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.codes);
+    if constexpr (KBLK) return base + (int64_t)(c >> 6) * a.c_kp + row * 64 + (c & 63);
+    else return base + row * (OUT4 ? a.kp / 2 : a.kp) + c;
+  };
 
   for (int64_t rowbase = (int64_t)blockIdx.x * rpb; rowbase < a.rows; rowbase += (int64_t)gridDim.x * rpb) {
     const int64_t row = rowbase + rib;
@@ -282,10 +292,9 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) u[t] = qbyte(v[j][8 * h + t], rr, qf);
             if constexpr (OUT4) {
-              reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(a.codes) + row * (a.kp / 2) + e / 2)[0] =
-                  pack8_nibbles(u);
+              reinterpret_cast<unsigned*>(code_at(row, e / 2))[0] = pack8_nibbles(u);
             } else {
-              *reinterpret_cast<u2v*>(reinterpret_cast<int8_t*>(a.codes) + row * a.kp + e) =
+              *reinterpret_cast<u2v*>(code_at(row, e)) =
                   u2v{pack4_lo(u[0], u[1], u[2], u[3]), pack4_lo(u[4], u[5], u[6], u[7])};
             }
           }
@@ -299,10 +308,9 @@ __global__ __launch_bounds__(512) void k_rowquant(RowArgs a) {
             if constexpr (OUT4) {
               const unsigned nb = __shfl_down(c, 1, 64);
               if (jj < a.p1 && (jj & 1) == 0)
-                reinterpret_cast<uint8_t*>(a.codes)[row * (a.kp / 2) + (a.k + jj) / 2] =
-                    (uint8_t)((c & 0xFu) | ((nb & 0xFu) << 4));
+                *code_at(row, (a.k + jj) / 2) = (uint8_t)((c & 0xFu) | ((nb & 0xFu) << 4));
             } else {
-              if (jj < a.p1) reinterpret_cast<int8_t*>(a.codes)[row * a.kp + a.k + jj] = (int8_t)c;
+              if (jj < a.p1) *code_at(row, a.k + jj) = (uint8_t)c;
             }
           }
         }
@@ -508,23 +516,27 @@ __global__ __launch_bounds__(AMAX_THREADS) void k_tensor_absmax(const void* x, i
   }
 }
 
-template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY>
+template <int DT, bool HAD, bool DUAL, int MODE, bool OUT4, bool MAXONLY, bool KBLK = false>
 static hipError_t launch_row(const RowArgs& a, int grid, int block, hipStream_t st) {
   // The pass count is a compile-time constant so that a lane holds exactly its passes.
   const size_t shm = (DUAL && a.W == 1) ? (size_t)(block / 64) * a.k * 2 : 0;  // rows per block x K words
   switch (a.np) {
-    case 1: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 1>), dim3(grid), dim3(block), shm, st, a); break;
-    case 2: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 2>), dim3(grid), dim3(block), shm, st, a); break;
-    case 3: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 3>), dim3(grid), dim3(block), shm, st, a); break;
-    default: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, NPMAX>), dim3(grid), dim3(block), shm, st, a); break;
+    case 1: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 1, KBLK>), dim3(grid), dim3(block), shm, st, a); break;
+    case 2: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 2, KBLK>), dim3(grid), dim3(block), shm, st, a); break;
+    case 3: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, 3, KBLK>), dim3(grid), dim3(block), shm, st, a); break;
+    default: hipLaunchKernelGGL((k_rowquant<DT, HAD, DUAL, MODE, OUT4, MAXONLY, NPMAX, KBLK>), dim3(grid), dim3(block), shm, st, a); break;
   }
   return hipGetLastError();
 }
 
 template <int DT, bool HAD, bool DUAL>
-static hipError_t dispatch_mode(const RowArgs& a, int mode, bool out4, bool maxonly, int grid, int block,
-                                hipStream_t st) {
+static hipError_t dispatch_mode(const RowArgs& a, int mode, bool out4, bool maxonly, bool kblock, int grid,
+                                int block, hipStream_t st) {
   if (maxonly) return launch_row<DT, HAD, DUAL, MODE_ROW, false, true>(a, grid, block, st);
+  if (kblock) {  // weights: per-row (output-channel) scales
+    if (out4) return launch_row<DT, HAD, DUAL, MODE_ROW, true, false, true>(a, grid, block, st);
+    return launch_row<DT, HAD, DUAL, MODE_ROW, false, false, true>(a, grid, block, st);
+  }
   if (out4) return launch_row<DT, HAD, DUAL, MODE_ROW, true, false>(a, grid, block, st);
   switch (mode) {
     case MODE_ROW: return launch_row<DT, HAD, DUAL, MODE_ROW, false, false>(a, grid, block, st);
@@ -534,11 +546,11 @@ static hipError_t dispatch_mode(const RowArgs& a, int mode, bool out4, bool maxo
 }
 
 template <int DT>
-static hipError_t dispatch_dt(const RowArgs& a, bool had, bool dual, int mode, bool out4, bool maxonly, int grid,
-                              int block, hipStream_t st) {
-  if (had) return dispatch_mode<DT, true, false>(a, mode, out4, maxonly, grid, block, st);
-  if (dual) return dispatch_mode<DT, false, true>(a, mode, out4, maxonly, grid, block, st);
-  return dispatch_mode<DT, false, false>(a, mode, out4, maxonly, grid, block, st);
+static hipError_t dispatch_dt(const RowArgs& a, bool had, bool dual, int mode, bool out4, bool maxonly, bool kblock,
+                              int grid, int block, hipStream_t st) {
+  if (had) return dispatch_mode<DT, true, false>(a, mode, out4, maxonly, kblock, grid, block, st);
+  if (dual) return dispatch_mode<DT, false, true>(a, mode, out4, maxonly, kblock, grid, block, st);
+  return dispatch_mode<DT, false, false>(a, mode, out4, maxonly, kblock, grid, block, st);
 }
 
 }  // namespace vqk
@@ -572,10 +584,12 @@ static RowArgs make_args(const RowQuantParams& p) {
   a.scale_mul = p.scale_mul;
   a.codes = p.codes;
   a.scales = p.scales;
+  a.c_kp = p.kblock ? 64 * p.rows : 64;
   return a;
 }
 
 hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st) {
+  if (p.kblock && (p.mode != 0 || p.maxonly)) return hipErrorInvalidValue;  // a weight layout
   RowArgs a = make_args(p);
   int W, np, block;
   row_geometry(a.k, W, np, block);
@@ -592,8 +606,8 @@ hipError_t launch_row_quant(const RowQuantParams& p, hipStream_t st) {
   const int grid = (int)blocks;
   const int mode = p.mode;
   switch (p.dtype) {
-    case DT_F16: return dispatch_dt<DT_F16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, grid, block, st);
-    case DT_BF16: return dispatch_dt<DT_BF16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, grid, block, st);
+    case DT_F16: return dispatch_dt<DT_F16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, p.kblock, grid, block, st);
+    case DT_BF16: return dispatch_dt<DT_BF16>(a, p.had, p.n_out > 0, mode, p.out4, p.maxonly, p.kblock, grid, block, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -62,6 +62,21 @@ int64_t vq_outlier_part_len(int32_t n_out) { return part_len(n_out); }
 
 int64_t vq_packed_k(int64_t k, int32_t n_out) { return k + part_len(n_out); }
 
+namespace {
+// A weight format: the width (4 or 8) with or without VQ_W_KBLOCK.
+bool wfmt_ok(int wfmt) {
+  const int bits = wfmt & ~VQ_W_KBLOCK;
+  return bits == 4 || bits == 8;
+}
+int64_t weight_row_bytes(int64_t kp, int wfmt) { return (wfmt & ~VQ_W_KBLOCK) == 8 ? kp : kp / 2; }
+}  // namespace
+
+int64_t vq_weight_bytes(int64_t n, int64_t kp, int wfmt) {
+  if (n < 1 || kp < 1 || n >= kMaxDim || kp >= kMaxDim || kp % VQ_K_ALIGN || !wfmt_ok(wfmt)) return 0;
+  const int64_t rb = weight_row_bytes(kp, wfmt);
+  return (wfmt & VQ_W_KBLOCK) ? (rb + 63) / 64 * 64 * n : rb * n;
+}
+
 const char* vq_status_string(vq_status s) {
   switch (s) {
     case VQ_OK: return "ok";
@@ -124,7 +139,9 @@ vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int6
                           hipStream_t stream) {
   vq_status s = check_rows(w, dt, n, k, ldw, idx_dev, n_out, had_block, codes, scales);
   if (s != VQ_OK) return s;
-  if (bits != 4 && bits != 8) return VQ_ERR_UNSUPPORTED;
+  if (!wfmt_ok(bits)) return VQ_ERR_UNSUPPORTED;
+  const bool kblock = (bits & VQ_W_KBLOCK) != 0;
+  bits &= ~VQ_W_KBLOCK;
   vq_internal::RowQuantParams p{};
   p.x = w;
   p.dtype = (int)dt;
@@ -142,6 +159,7 @@ vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int6
   p.mode = 0;
   p.had = had_block != 0;
   p.out4 = bits == 4;
+  p.kblock = kblock;
   return hip_status(vq_internal::launch_row_quant(p, stream));
 }
 
@@ -238,13 +256,13 @@ vq_status check_gemm(const int8_t* a, const float* sa, int sa_per_token, const v
   if (sa_per_token != 0 && sa_per_token != 1) return VQ_ERR_INVALID_ARG;
   if (m < 1 || n < 1 || kp < 1 || k0 < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || kp >= kMaxDim)
     return VQ_ERR_INVALID_ARG;
-  if (b_bits != 4 && b_bits != 8) return VQ_ERR_UNSUPPORTED;
+  if (!wfmt_ok(b_bits)) return VQ_ERR_UNSUPPORTED;
   if (too_many_tiles(m, n)) return VQ_ERR_UNSUPPORTED;
   if (kp % VQ_K_ALIGN || k0 % VQ_K_ALIGN || k0 > kp || kp - k0 > VQ_MAX_OUTLIERS) return VQ_ERR_SHAPE;
   // The int32 accumulators must hold any sum of the longer partition (partition 0): 127
   // per activation code times 127 per int8 weight code, or 112 = 16 * 7 per 4-bit weight
   // code, which enters the MFMA as 16 times its value.
-  if ((double)k0 * 127.0 * (b_bits == 8 ? 127.0 : 112.0) >= 2147483648.0) return VQ_ERR_SHAPE;
+  if ((double)k0 * 127.0 * ((b_bits & ~VQ_W_KBLOCK) == 8 ? 127.0 : 112.0) >= 2147483648.0) return VQ_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b)) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
   return VQ_OK;
@@ -258,7 +276,8 @@ vq_internal::GemmParams gemm_params(const int8_t* a, const float* sa, int sa_per
   p.sa = sa;
   p.sa_per_token = sa_per_token;
   p.b = b;
-  p.b_bits = b_bits;
+  p.b_bits = b_bits & ~VQ_W_KBLOCK;
+  p.b_kblock = (b_bits & VQ_W_KBLOCK) != 0;
   p.sb = sb;
   p.m = m;
   p.n = n;

@@ -26,6 +26,7 @@ struct RowQuantParams {
   bool had;
   bool out4;
   bool maxonly;
+  bool kblock;  // codes in the 64-byte K-piece layout (weights, MODE_ROW only)
 };
 
 int row_quant_max_k();
@@ -51,7 +52,8 @@ struct GemmParams {
   const float* sa;
   int sa_per_token;
   const void* b;
-  int b_bits;
+  int b_bits;    // 8 or 4
+  int b_kblock;  // b in the 64-byte K-piece layout (VQ_W_KBLOCK)
   const float* sb;
   int64_t m, n, kp, k0;
   void* y;

@@ -78,6 +78,23 @@ int64_t vq_outlier_part_len(int32_t n_out);
 int64_t vq_packed_k(int64_t k, int32_t n_out);
 
 /*
+ * Weight layout flag, OR'ed into the weight width (bits of vq_pack_weights, b_bits of the
+ * GEMM entry points; the same value goes to both).  A row of packed weight codes has
+ * row_bytes = kp (8-bit weights) or kp / 2 (4-bit).  Without the flag the codes are
+ * [n x row_bytes] row-major.  With it they are cut into 64-byte K pieces (64 int8 codes
+ * or 128 4-bit codes) and piece j of every row is stored together: byte c of row r is at
+ * (c / 64) * n * 64 + r * 64 + c % 64, for ceil(row_bytes / 64) pieces (the last one
+ * padded to 64 bytes when row_bytes % 64 == 32; its padding is never read).  A GEMM stage
+ * of a 256-row weight tile is then one contiguous block of whole 128-byte lines, where
+ * the row-major layout gives it half lines at the row pitch.
+ */
+#define VQ_W_KBLOCK 0x100
+
+/* Bytes of packed weights [n rows, kp codes] in format wfmt (4 or 8, optionally OR
+ * VQ_W_KBLOCK); 0 for invalid arguments. */
+int64_t vq_weight_bytes(int64_t n, int64_t kp, int wfmt);
+
+/*
  * Outlier input-channel detection (Q-ARVD, Methodology: outlier-aware adaptive
  * dual-scale quantization).  For each column k of x [rows x cols]:
  *   v_k = sqrt(sum_r x[r,k]^2)                       (float64 accumulation)
@@ -110,16 +127,18 @@ vq_status vq_detect_outliers(const void* x, vq_dtype dt, int64_t rows, int64_t c
  * details: per-channel weights, dual scale; 6Bit-Diffusion, Methodology B.1: weights
  * quantized offline to 4 bits and activations rotated by an online block Hadamard).
  *   w          device, dt in {F16, BF16}, [n x k], stride ldw; k % 64 == 0
- *   bits       8 (codes int8 [n x kp]) or 4 (codes uint8 [n x kp/2], two per byte)
+ *   bits       8 (codes int8 [n x kp]) or 4 (codes uint8 [n x kp/2], two per byte),
+ *              optionally OR VQ_W_KBLOCK for the K-piece layout
  *   idx_dev    device int32 [n_out] outlier channels (ascending, < k), or NULL with n_out = 0
  *   had_block  0, or 128: each row is first rotated by the unnormalized 128-point
  *              Sylvester Hadamard butterflies; the scale then carries the exact 1/128
  *              so that products with rotated activations equal the normalized rotation.
  *              Not combined with n_out > 0.
- *   codes      device, kp = vq_packed_k(k, n_out)
+ *   codes      device, vq_weight_bytes(n, kp, bits) bytes, kp = vq_packed_k(k, n_out)
  *   scales     device float [n] (n_out = 0) or [n x 2] (partition 0, partition 1)
- * Errors: INVALID_ARG, SHAPE (k % 64, k % 128 with had_block), UNSUPPORTED (bits,
- * had_block other than 0/128, had_block with n_out, n_out > VQ_MAX_OUTLIERS or >= k).
+ * Errors: INVALID_ARG, SHAPE (k % 64, k % 128 with had_block), UNSUPPORTED (bits other
+ * than 4/8 with or without VQ_W_KBLOCK, had_block other than 0/128, had_block with
+ * n_out, n_out > VQ_MAX_OUTLIERS or >= k).
  */
 vq_status vq_pack_weights(const void* w, vq_dtype dt, int64_t n, int64_t k, int64_t ldw, int bits,
                           const int32_t* idx_dev, int32_t n_out, int had_block, void* codes,
@@ -176,7 +195,9 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
  * y = y_0 (+ y_1 when dual, added in float32), RNE to out_dt.
  *   a        device int8 [m x kp] (row stride kp)
  *   sa       device float: sa_per_token ? [m] or [m x 2] : [1] or [2]
- *   b        device: b_bits 8 -> int8 [n x kp]; b_bits 4 -> uint8 [n x kp/2] packed nibbles
+ *   b        device: b_bits 8 -> int8 [n x kp]; b_bits 4 -> uint8 [n x kp/2] packed nibbles;
+ *            with VQ_W_KBLOCK OR'ed into b_bits, the K-piece layout of those codes
+ *            (vq_weight_bytes bytes), as vq_pack_weights wrote it with the same flag
  *   sb       device float [n] or [n x 2]
  *   kp, k0   kp % 64 == 0, k0 % 64 == 0, 0 < k0 <= kp, kp - k0 <= 128; the int32
  *            accumulators bound k0: k0 * 127 * 127 < 2^31 (int8 weights, k0 <= 133120) or
@@ -194,8 +215,9 @@ vq_status vq_hadamard_block(const void* x, vq_dtype in_dt, int64_t ldx, void* y,
  *            bit-identical to the unsplit GEMM.  Every call leaves the workspace
  *            zero-filled; calls that share one must not overlap.  A size of 0 means the
  *            shape gains nothing from the split (ws is then not used).
- * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8, out_dt, or more than 2^28
- * output tiles of 256 x 256, which the kernels' 32-bit tile counts cannot hold).
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED (b_bits not 4/8 with or without VQ_W_KBLOCK,
+ * out_dt, or more than 2^28 output tiles of 256 x 256, which the kernels' 32-bit tile
+ * counts cannot hold).
  */
 int64_t vq_qgemm_workspace_bytes(int64_t m, int64_t n, int64_t k0);
 vq_status vq_qgemm_dequant(const int8_t* a, const float* sa, int sa_per_token, const void* b,
@@ -252,7 +274,8 @@ vq_status vq_quant_residual(const void* x, vq_dtype dt, int64_t m, int64_t k, in
  * with acc1 and acc2 taken from the stacked operand of vq_quant_residual (one small GEMM
  * over its 2 n_rows rows, float32 results in ws, then a merge kernel).
  *   a, sa     the per-token codes [m x kp] and scales [m] of vq_quant_act (kp % 64 == 0)
- *   b, sb     packed weights as for vq_qgemm_dequant (b_bits 8 or 4), scales [n]
+ *   b, sb     packed weights as for vq_qgemm_dequant (b_bits 8 or 4, optionally OR
+ *             VQ_W_KBLOCK), scales [n]
  *   a2, sa2   the stacked codes [2 n_rows x kp] and scales [2 n_rows] of vq_quant_residual
  *   rows_dev  device int32 [n_rows], distinct, the same list as for vq_quant_residual
  *   y         as for vq_qgemm_dequant

@@ -67,6 +67,21 @@ def test_layout_helpers(lib):
     assert lib.vq_detect_workspace_elems(0, 5) == 0
 
 
+def test_weight_bytes(lib):
+    """Packed weight sizes: row-major n * row_bytes; 64-byte K pieces ceil(row_bytes / 64)
+    pieces of n * 64 bytes (a 4-bit row of kp % 128 == 64 codes pads its last piece)."""
+    KB = 0x100
+    assert lib.vq_weight_bytes(5760, 1920, 8) == 5760 * 1920
+    assert lib.vq_weight_bytes(5760, 1920, 8 | KB) == 5760 * 1920
+    assert lib.vq_weight_bytes(3072, 12288, 4) == 3072 * 6144
+    assert lib.vq_weight_bytes(3072, 12288, 4 | KB) == 3072 * 6144
+    assert lib.vq_weight_bytes(7, 192, 4) == 7 * 96
+    assert lib.vq_weight_bytes(7, 192, 4 | KB) == 2 * 7 * 64
+    assert lib.vq_weight_bytes(12288, 3136, 4 | KB) == 25 * 12288 * 64
+    for bad in ((0, 64, 8), (4, 0, 8), (4, 100, 8), (4, 64, 6), (4, 64, 6 | KB), (4, 64, 8 | 0x200)):
+        assert lib.vq_weight_bytes(*bad) == 0, bad
+
+
 def quant(lib, **kw):
     a = dict(x=FAKE, dt=BF16, m=64, k=1920, ldx=1920, bits=8, bits_dev=NULL, gran=1, had=0, idx=NULL,
              n_out=0, static=NULL, codes=FAKE, scales=FAKE, stream=NULL)
@@ -120,6 +135,10 @@ def pack(lib, **kw):
     (dict(had=128, idx=FAKE, n_out=4), UNSUP),
     (dict(n=0), INVALID),
     (dict(idx=FAKE, n_out=3072), UNSUP),
+    (dict(bits=6 | 0x100), UNSUP),
+    (dict(bits=8 | 0x200), UNSUP),
+    (dict(bits=4 | 0x100, k=100, ldw=100), SHAPE),  # the layout flag passes to the other checks
+    (dict(bits=8 | 0x100, w=NULL), INVALID),
 ])
 def test_pack_weights_validation(lib, kw, want):
     assert pack(lib, **kw) == want
@@ -154,6 +173,13 @@ def gemm(lib, **kw):
     (dict(kp=133184, k0=133184), SHAPE),
     (dict(kp=133248, k0=133184), SHAPE),
     (dict(bb=4, kp=151040, k0=151040), SHAPE),
+    # the weight layout flag: accepted with both widths, then the same checks
+    (dict(bb=6 | 0x100), UNSUP),
+    (dict(bb=8 | 0x400), UNSUP),
+    (dict(bb=8 | 0x100, kp=133184, k0=133184), SHAPE),
+    (dict(bb=4 | 0x100, kp=151040, k0=151040), SHAPE),
+    (dict(bb=8 | 0x100, y=ctypes.c_void_p(0x10001)), SHAPE),
+    (dict(bb=4 | 0x100, b=NULL), INVALID),
 ])
 def test_qgemm_validation(lib, kw, want):
     assert gemm(lib, **kw) == want
