@@ -66,8 +66,8 @@ def parse():
                         "kernels take less time than the binding's host work per call, else 1 with --graph "
                         "and host launches without it")
     p.add_argument("--w-layout", choices=["kblock", "row"], default="kblock",
-                   help="layout of the packed integer weights: 64-byte K pieces (each GEMM stage of a weight "
-                        "tile whole cache lines) or row-major")
+                   help="layout of the packed weights (integer, and MXFP4 on the MX route): 64-byte K pieces "
+                        "(each GEMM stage of a weight tile whole cache lines) or row-major")
     p.add_argument("--residual-frac", type=float, default=0.0, metavar="F",
                    help="decompose a seeded fraction F of the tokens (residual re-quantization added back "
                         "in the epilogue); per-token workloads without dual scale or rotation only")
@@ -165,7 +165,7 @@ class Layer:
                 for l in range(self.layers):
                     if self.routes[l] == 4:
                         w = gen.make_w(cfg, layer=l).to(dev)
-                        self.mx_w[l] = vq.vq_mx_quant(w, "fp4")
+                        self.mx_w[l] = vq.vq_mx_quant(w, "fp4", kblock=w_layout == "kblock")
                         del w
         elif mx:
             if c["dual"] or self.gran != "token":
@@ -173,7 +173,8 @@ class Layer:
             w = gen.make_w(cfg).to(dev)
             # With the workload's block Hadamard, the activations are rotated online and the
             # weights offline (their block exponents 7 lower, so the GEMM needs no 1/128).
-            self.mx_w = [vq.vq_mx_quant(w, "fp4", had_block=self.had, exp_offset=-7 if self.had else 0)]
+            self.mx_w = [vq.vq_mx_quant(w, "fp4", had_block=self.had, exp_offset=-7 if self.had else 0,
+                                        kblock=w_layout == "kblock")]
             self.w = [None]
             self.bits_dev = [None]
             del w

@@ -21,6 +21,7 @@ VQ_OK, VQ_ERR_INVALID_ARG, VQ_ERR_SHAPE, VQ_ERR_UNSUPPORTED, VQ_ERR_HIP = range(
 VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 VQ_PER_TENSOR, VQ_PER_TOKEN, VQ_PER_TENSOR_STATIC = 0, 1, 2
 VQ_MXFP6, VQ_MXFP4 = 2, 4
+VQ_MXFP4_KBLOCK = VQ_MXFP4 | 0x100  # FP4 codes in 64-byte K pieces (weights)
 VQ_K_ALIGN = 64
 VQ_HAD_BLOCK = 128
 VQ_MAX_OUTLIERS = 128
@@ -503,56 +504,72 @@ def vq_mx_scale_bytes(rows: int, k: int) -> int:
 
 
 def vq_mx_quant(x: torch.Tensor, fmt: str = "fp4", codes=None, scales=None, had_block: int = 0,
-                exp_offset: int = 0):
+                exp_offset: int = 0, kblock: bool = False):
     """MX codes of X [rows x K].  Returns (codes uint8 [rows x K*w/8], scales uint8 E8M0 in step-major order).
 
     had_block=128 rotates each row by the unnormalized 128-point block Hadamard transform
-    first (vq_mx_quant_rotated), scaled by 2^exp_offset (-7 for weights rotated offline)."""
+    first (vq_mx_quant_rotated), scaled by 2^exp_offset (-7 for weights rotated offline).
+    kblock=True (FP4 only, for weights): the codes in 64-byte K pieces, [pieces x rows x 64]
+    (vq_mx_gemm tells the layouts apart by the tensor's rank)."""
     _dev(x, "x")
     rows, k = x.shape
+    if kblock and fmt != "fp4":
+        raise ValueError("K pieces hold FP4 codes only")
+    code = (VQ_MXFP4_KBLOCK if kblock else _MX[fmt]) if fmt in _MX else -1
     if codes is None:
-        codes = torch.empty((rows, k * _MX_BITS.get(fmt, 8) // 8), dtype=torch.uint8, device=x.device)
+        row_bytes = k * _MX_BITS.get(fmt, 8) // 8
+        shape = ((row_bytes + 63) // 64, rows, 64) if kblock else (rows, row_bytes)
+        codes = torch.empty(shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(max(vq_mx_scale_bytes(rows, k), 1), dtype=torch.uint8, device=x.device)
     if fmt in _MX:
-        _buf(codes, "codes", vq_mx_code_bytes(rows, k, fmt), x.device)
+        _buf(codes, "codes", int(_lib.vq_mx_code_bytes(rows, k, code)), x.device)
         _buf(scales, "scales", vq_mx_scale_bytes(rows, k), x.device)
     if had_block:
         if had_block != VQ_HAD_BLOCK:
             raise ValueError(f"had_block must be 0 or {VQ_HAD_BLOCK}")
         _check("vq_mx_quant_rotated", _lib.vq_mx_quant_rotated(
-            _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), _MX.get(fmt, -1), exp_offset, _ptr(codes),
+            _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), code, exp_offset, _ptr(codes),
             _ptr(scales), _stream(x)))
         return codes, scales
     _check("vq_mx_quant", _lib.vq_mx_quant(
-        _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), _MX.get(fmt, -1), _ptr(codes), _ptr(scales), _stream(x)))
+        _ptr(x), _DT.get(x.dtype, -1), rows, k, x.stride(0), code, _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales
 
 
 def vq_mx_gemm(a: torch.Tensor, sa: torch.Tensor, fa: str, b: torch.Tensor, sb: torch.Tensor, fb: str = "fp4",
                out_dtype=torch.bfloat16, y=None, ws=None):
-    """Y = dec(A) . dec(B)^T on the scaled MFMA; a, b are the MX code buffers of vq_mx_quant.
+    """Y = dec(A) . dec(B)^T on the scaled MFMA; a, b are the MX code buffers of vq_mx_quant
+    (b row-major [N x K/2], or in 64-byte K pieces [pieces x N x 64]).
 
     ws: None uses the zero-filled workspace kept per device and stream, a tensor of
     vq_mx_gemm_workspace_bytes() bytes is used as given, False runs without the split."""
     _dev(a, "a")
     m = a.shape[0]
-    n = b.shape[0]
+    if not (isinstance(b, torch.Tensor) and b.dim() in (2, 3)):
+        raise TypeError("b must be a 2-D (row-major) or 3-D (K pieces) CUDA (HIP) tensor of MX codes")
+    kblock = b.dim() == 3
+    n = b.shape[1] if kblock else b.shape[0]
     k = a.shape[1] * 8 // _MX_BITS[fa]
+    if kblock and fb != "fp4":
+        raise ValueError("K pieces hold FP4 codes only")
+    fb_code = (VQ_MXFP4_KBLOCK if kblock else _MX[fb]) if fb in _MX else -1
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=a.device)
     _out2d(y, "y", m, n, a.device)
     if fa in _MX and fb in _MX:
         _in(a, "a", _U8, vq_mx_code_bytes(m, k, fa), a.device)
         _in(sa, "sa", _U8, vq_mx_scale_bytes(m, k), a.device)
-        _in(b, "b", _U8, vq_mx_code_bytes(n, k, fb), a.device)
+        _in(b, "b", _U8, int(_lib.vq_mx_code_bytes(n, k, fb_code)), a.device)
+        if kblock and tuple(b.shape) != ((k // 2 + 63) // 64, n, 64):
+            raise ValueError(f"b in K pieces must be [{(k // 2 + 63) // 64} x N x 64] FP4 codes")
         _in(sb, "sb", _U8, vq_mx_scale_bytes(n, k), a.device)
     need = _mx_ws_bytes(m, n, k)
     ws = _workspace(need, a.device) if ws is None else ws
     if ws is not False:
         _buf(ws, "ws", need, a.device)
     _check("vq_mx_gemm", _lib.vq_mx_gemm(
-        _ptr(a), _ptr(sa), _MX.get(fa, -1), _ptr(b), _ptr(sb), _MX.get(fb, -1), m, n, k,
+        _ptr(a), _ptr(sa), _MX.get(fa, -1), _ptr(b), _ptr(sb), fb_code, m, n, k,
         _ptr(y), _DT.get(y.dtype, -1), y.stride(0), None if ws is False else _ptr(ws), _stream(a)))
     return y
 

@@ -63,7 +63,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // One block: E8M0 exponent from its largest magnitude, scale byte, element codes.
 template <int DT, int FMT>
 __device__ __forceinline__ void mxq_block(const unsigned (&d)[16], int64_t row, int blk, int64_t rows8,
-                                          uint8_t* codes_row, uint8_t* scales) {
+                                          uint8_t* codes_blk, uint8_t* scales) {
   using F = MxFmt<FMT>;
   // Largest magnitude: with the sign bit cleared, bf16 and fp16 magnitudes order like their
   // 16-bit patterns (finite inputs), so a packed 16-bit integer maximum finds it.
@@ -82,7 +82,7 @@ __device__ __forceinline__ void mxq_block(const unsigned (&d)[16], int64_t row, 
   e = e < -127 ? -127 : e;
   scales[((int64_t)(blk >> 1) * rows8 + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
   const float sc = bits_f((unsigned)(e + 127) << 23);  // 2^e (bit pattern 0 for 2^-127)
-  u2v* dst = reinterpret_cast<u2v*>(codes_row + (int64_t)blk * (32 * F::W / 8));
+  u2v* dst = reinterpret_cast<u2v*>(codes_blk);
   if constexpr (FMT == MX_FP4) {
     unsigned o[4];
 #pragma unroll
@@ -122,7 +122,7 @@ __device__ __forceinline__ void mxq_block(const unsigned (&d)[16], int64_t row, 
 // (v_cvt_scalef32_pk_fp4_f32: two elements; v_cvt_scalef32_2xpk16_fp6_f32: the block).
 template <int FMT>
 __device__ __forceinline__ void mxq_block_f32(const float (&v)[32], int64_t row, int blk, int64_t rows8,
-                                              uint8_t* codes_row, uint8_t* scales) {
+                                              uint8_t* codes_blk, uint8_t* scales) {
   using F = MxFmt<FMT>;
   float m = 0.0f;
 #pragma unroll
@@ -132,7 +132,7 @@ __device__ __forceinline__ void mxq_block_f32(const float (&v)[32], int64_t row,
   e = e < -127 ? -127 : e;
   scales[((int64_t)(blk >> 1) * rows8 + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
   const float sc = bits_f((unsigned)(e + 127) << 23);
-  u2v* dst = reinterpret_cast<u2v*>(codes_row + (int64_t)blk * (32 * F::W / 8));
+  u2v* dst = reinterpret_cast<u2v*>(codes_blk);
   if constexpr (FMT == MX_FP4) {
     unsigned o[4];
 #pragma unroll
@@ -205,10 +205,14 @@ __device__ __forceinline__ void fwht128_quad(float (&v)[32], int q) {
 // HAD: the rows are first rotated by 128-point Hadamard blocks (each a lane quad, K a
 // multiple of 128) and scaled by pscale (an exact power of two); the block scales then
 // come from the float32 rotated values.
-template <int DT, int FMT, bool HAD>
+// KB (FP4 codes only): the codes go out in 64-byte K pieces, four blocks of a row per
+// piece and piece j of every row together (byte c of row r at (c / 64) * 64 rows + 64 r +
+// c % 64), the weight layout whose GEMM stages read whole cache lines.
+template <int DT, int FMT, bool HAD, bool KB>
 __global__ __launch_bounds__(256) void k_mxquant(const void* x, int64_t ldx, int64_t rows, int k, int64_t rows8,
                                                  uint8_t* codes, uint8_t* scales, float pscale) {
   using F = MxFmt<FMT>;
+  static_assert(!KB || FMT == MX_FP4, "K pieces hold whole FP4 blocks only");
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 4096];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the tile index stays scalar
@@ -217,6 +221,11 @@ __global__ __launch_bounds__(256) void k_mxquant(const void* x, int64_t ldx, int
   const int nbg = (nb + 7) / 8;
   const int64_t tiles = (rows + 7) / 8 * nbg;
   const int64_t row_bytes = (int64_t)k * F::W / 8;
+  // Destination of block blk of row `row`.
+  auto block_at = [&](int64_t row, int blk) -> uint8_t* {
+    if constexpr (KB) return codes + (int64_t)(blk >> 2) * rows * 64 + row * 64 + (blk & 3) * 16;
+    else return codes + row * row_bytes + (int64_t)blk * (32 * F::W / 8);
+  };
   const int64_t step = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < tiles; t += step) {
     const int64_t row0 = t / nbg * 8;  // wave-uniform
@@ -263,9 +272,9 @@ __global__ __launch_bounds__(256) void k_mxquant(const void* x, int64_t ldx, int
 #pragma unroll
         for (int i = 0; i < 32; ++i) v[i] *= pscale;
       }
-      if (row < rows && blk < nb) mxq_block_f32<FMT>(v, row, blk, rows8, codes + row * row_bytes, scales);
+      if (row < rows && blk < nb) mxq_block_f32<FMT>(v, row, blk, rows8, block_at(row, blk), scales);
     } else {
-      if (row < rows && blk < nb) mxq_block<DT, FMT>(d, row, blk, rows8, codes + row * row_bytes, scales);
+      if (row < rows && blk < nb) mxq_block<DT, FMT>(d, row, blk, rows8, block_at(row, blk), scales);
     }
     // LDS operations of one wave complete in order, so the next pass's writes cannot pass
     // these reads; this only keeps the compiler from moving them across.
@@ -316,6 +325,7 @@ struct MxArgs {
   int dp_items, split, items;
   int32_t* ws_cnt;
   uint64_t* ws_part;
+  int64_t b_kp;  // weights in 64-byte K pieces: bytes from one piece to the next (64 n)
 };
 
 // Two schedules of the same K loop.  Interleaved (PP false, S = 1): every wave reads the
@@ -326,7 +336,9 @@ struct MxArgs {
 // ahead of waves 4-7, two barriers per stage; the refill of stage p + 2 is issued in the
 // memory phase of stage p into the slot read at stage p + 2 - NST, whose readers passed
 // a barrier before.
-template <int FA, int S, int OUT_DT, bool PP>
+// KB: the weights in 64-byte K pieces (vq_mx_quant with VQ_W_KBLOCK); a stage's weight
+// bytes of a row (32 or 64) then lie in one piece, and a tile's rows are consecutive.
+template <int FA, int S, int OUT_DT, bool PP, bool KB>
 __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mxgemm(MxArgs g) {
   using C = MxCfg<FA, S>;
   static_assert(PP ? (S == 2 && C::NST >= 3) : S == 1,
@@ -343,7 +355,9 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int nk = g.k / (MX_BK * S);  // ring stages along K
   __shared__ int s_last;
   const int64_t a_rowb = (int64_t)g.k * MxFmt<FA>::W / 8;
-  const int64_t b_rowb = g.k / 2;
+  const int64_t b_rowb = KB ? 64 : g.k / 2;
+  // Offset of byte c of a weight row from the row's first byte.
+  auto bofs = [&](int64_t c) -> int64_t { return KB ? (c >> 6) * g.b_kp + (c & 63) : c; };
 
   // ---- direct-load assignment (per lane, per stage).
   // 64-byte rows (FP4, S = 2): 1 KB slot = 16 rows, lane -> row lane/4, chunk (lane & 3)
@@ -429,7 +443,7 @@ __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int i = 0; i < C::LA; ++i)
       if (a_on[i]) dma16(ga[i] + (int64_t)kt * C::A_ROW, base + la_off[i]);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) dma16(gb[i] + (int64_t)kt * C::B_ROW, base + lb_off[i]);
+    for (int i = 0; i < C::LB; ++i) dma16(gb[i] + bofs((int64_t)kt * C::B_ROW), base + lb_off[i]);
 #pragma unroll
     for (int sub = 0; sub < S; ++sub)
       if (s_on) dma16(gs + (int64_t)(kt * S + sub) * s_pitch, base + ls_off + sub * 1024);
@@ -712,28 +726,32 @@ using namespace vqk;
 int64_t mx_rows8(int64_t rows) { return (rows + 7) / 8 * 8; }
 
 hipError_t launch_mx_quant(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int fmt, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st, bool had, int exp_offset) {
+                           uint8_t* scales, hipStream_t st, bool had, int exp_offset, bool kblock) {
+  if (kblock && fmt != MX_FP4) return hipErrorInvalidValue;
   const int64_t tiles = (rows + 7) / 8 * ((k / 32 + 7) / 8);
   const int64_t wgs = (tiles + 3) / 4;  // four waves, one 8 x 8-block tile each, per workgroup and pass
   const unsigned grid = (unsigned)(wgs < 8192 ? wgs : 8192);
   const int64_t r8 = mx_rows8(rows);
   const float pscale = ldexpf(1.0f, exp_offset);  // exact: |exp_offset| <= 64
-#define MXQ(DTV, FV, H)                                                                                       \
-  hipLaunchKernelGGL((k_mxquant<DTV, FV, H>), dim3(grid), dim3(256), 0, st, x, ldx, rows, (int)k, r8, codes, \
+#define MXQ(DTV, FV, H, KBV)                                                                                  \
+  hipLaunchKernelGGL((k_mxquant<DTV, FV, H, KBV>), dim3(grid), dim3(256), 0, st, x, ldx, rows, (int)k, r8, codes, \
                      scales, pscale)
+#define MXQ4(DTV, H) \
+  if (kblock) MXQ(DTV, MX_FP4, H, true); else MXQ(DTV, MX_FP4, H, false)
   if (dtype == DT_F16) {
     if (fmt == MX_FP4) {
-      if (had) MXQ(DT_F16, MX_FP4, true); else MXQ(DT_F16, MX_FP4, false);
+      if (had) { MXQ4(DT_F16, true); } else { MXQ4(DT_F16, false); }
     } else {
-      if (had) MXQ(DT_F16, MX_FP6, true); else MXQ(DT_F16, MX_FP6, false);
+      if (had) MXQ(DT_F16, MX_FP6, true, false); else MXQ(DT_F16, MX_FP6, false, false);
     }
   } else {
     if (fmt == MX_FP4) {
-      if (had) MXQ(DT_BF16, MX_FP4, true); else MXQ(DT_BF16, MX_FP4, false);
+      if (had) { MXQ4(DT_BF16, true); } else { MXQ4(DT_BF16, false); }
     } else {
-      if (had) MXQ(DT_BF16, MX_FP6, true); else MXQ(DT_BF16, MX_FP6, false);
+      if (had) MXQ(DT_BF16, MX_FP6, true, false); else MXQ(DT_BF16, MX_FP6, false, false);
     }
   }
+#undef MXQ4
 #undef MXQ
   return hipGetLastError();
 }
@@ -755,7 +773,8 @@ int64_t mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 }
 
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uint8_t* b, const uint8_t* sb, int64_t m,
-                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, void* ws, hipStream_t st) {
+                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, void* ws, hipStream_t st,
+                          bool b_kblock) {
   MxArgs g{};
   g.a = a;
   g.sa = sa;
@@ -768,6 +787,7 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uin
   g.m8 = mx_rows8(m);
   g.n8 = mx_rows8(n);
   g.ldy = ldy;
+  g.b_kp = 64 * n;
   const int64_t esize = out_dt == DT_F32 ? 4 : 2;
   g.vec_store = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * esize) % 16 == 0) ? 1 : 0;
   g.tiles_m = (int)((m + MX_BM - 1) / MX_BM);
@@ -784,14 +804,19 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uin
   // allows it.  FP6 activations stay at one sub-step on the interleaved schedule: with two
   // sub-steps (42 KB stages, three in the ring) the ping-pong form measured 19% slower.
   const bool two = fa == MX_FP4 && k % 128 == 0;
-#define MXG(F, SS, O) hipLaunchKernelGGL((k_mxgemm<F, SS, O, SS == 2>), dim3(grid), dim3(MX_NT), 0, st, g)
-#define MXO(F, SS)                \
-  if (out_dt == DT_F16)           \
-    MXG(F, SS, DT_F16);           \
-  else if (out_dt == DT_BF16)     \
-    MXG(F, SS, DT_BF16);          \
-  else                            \
-    MXG(F, SS, DT_F32)
+#define MXG(F, SS, O)                                                                          \
+  if (b_kblock)                                                                                \
+    hipLaunchKernelGGL((k_mxgemm<F, SS, O, SS == 2, true>), dim3(grid), dim3(MX_NT), 0, st, g); \
+  else                                                                                         \
+    hipLaunchKernelGGL((k_mxgemm<F, SS, O, SS == 2, false>), dim3(grid), dim3(MX_NT), 0, st, g)
+#define MXO(F, SS)              \
+  if (out_dt == DT_F16) {       \
+    MXG(F, SS, DT_F16);         \
+  } else if (out_dt == DT_BF16) { \
+    MXG(F, SS, DT_BF16);        \
+  } else {                      \
+    MXG(F, SS, DT_F32);         \
+  }
   if (fa == MX_FP4) {
     if (two) { MXO(MX_FP4, 2); } else { MXO(MX_FP4, 1); }
   } else {

@@ -365,13 +365,16 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
 // ------------------------------------------------------------------ MX formats
 
 namespace {
-bool mx_fmt_ok(vq_mx_fmt f) { return f == VQ_MXFP4 || f == VQ_MXFP6; }
-int mx_bits(vq_mx_fmt f) { return f == VQ_MXFP4 ? 4 : 6; }
+bool mx_fmt_ok(vq_mx_fmt f) { return f == VQ_MXFP4 || f == VQ_MXFP6 || f == VQ_MXFP4_KBLOCK; }
+bool mx_kblock(vq_mx_fmt f) { return f == VQ_MXFP4_KBLOCK; }
+int mx_base(vq_mx_fmt f) { return (int)f & ~VQ_W_KBLOCK; }  // the element format (MFMA code)
+int mx_bits(vq_mx_fmt f) { return mx_base(f) == VQ_MXFP4 ? 4 : 6; }
 }  // namespace
 
 int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt) {
   if (rows < 1 || k < 1 || k % VQ_K_ALIGN || !mx_fmt_ok(fmt)) return 0;
-  return rows * (k * mx_bits(fmt) / 8);
+  const int64_t row_bytes = k * mx_bits(fmt) / 8;
+  return mx_kblock(fmt) ? (row_bytes + 63) / 64 * 64 * rows : rows * row_bytes;
 }
 
 int64_t vq_mx_scale_bytes(int64_t rows, int64_t k) {
@@ -387,7 +390,8 @@ vq_status vq_mx_quant(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64
   if (!mx_fmt_ok(fmt)) return VQ_ERR_UNSUPPORTED;
   if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
   if (!aligned16(x) || ldx % 8 || reinterpret_cast<uintptr_t>(codes) % 8) return VQ_ERR_SHAPE;
-  return hip_status(vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream));
+  return hip_status(vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, mx_base(fmt), codes, scales, stream, false,
+                                                 0, mx_kblock(fmt)));
 }
 
 vq_status vq_mx_quant_rotated(const void* x, vq_dtype dt, int64_t rows, int64_t k, int64_t ldx, vq_mx_fmt fmt,
@@ -400,7 +404,8 @@ vq_status vq_mx_quant_rotated(const void* x, vq_dtype dt, int64_t rows, int64_t 
   if (k % VQ_HAD_BLOCK) return VQ_ERR_SHAPE;
   if (!aligned16(x) || ldx % 8 || reinterpret_cast<uintptr_t>(codes) % 8) return VQ_ERR_SHAPE;
   return hip_status(
-      vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, (int)fmt, codes, scales, stream, true, exp_offset));
+      vq_internal::launch_mx_quant(x, (int)dt, ldx, rows, k, mx_base(fmt), codes, scales, stream, true, exp_offset,
+                                   mx_kblock(fmt)));
 }
 
 int64_t vq_mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
@@ -416,13 +421,14 @@ vq_status vq_mx_gemm(const uint8_t* a, const uint8_t* sa, vq_mx_fmt fa, const ui
   if (!a || !sa || !b || !sb || !y) return VQ_ERR_INVALID_ARG;
   if (!valid_dt(out_dt)) return VQ_ERR_INVALID_ARG;
   if (m < 1 || n < 1 || k < 1 || ldy < n || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return VQ_ERR_INVALID_ARG;
-  if (!mx_fmt_ok(fa) || fb != VQ_MXFP4) return VQ_ERR_UNSUPPORTED;
+  if ((fa != VQ_MXFP4 && fa != VQ_MXFP6) || (fb != VQ_MXFP4 && fb != VQ_MXFP4_KBLOCK)) return VQ_ERR_UNSUPPORTED;
   if (too_many_tiles(m, n)) return VQ_ERR_UNSUPPORTED;
   if (k % VQ_K_ALIGN) return VQ_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b) || !aligned16(sa) || !aligned16(sb)) return VQ_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_size(out_dt)) return VQ_ERR_SHAPE;
   if (ws && !aligned16(ws)) return VQ_ERR_SHAPE;
-  return hip_status(vq_internal::launch_mx_gemm(a, sa, (int)fa, b, sb, m, n, k, y, (int)out_dt, ldy, ws, stream));
+  return hip_status(
+      vq_internal::launch_mx_gemm(a, sa, (int)fa, b, sb, m, n, k, y, (int)out_dt, ldy, ws, stream, mx_kblock(fb)));
 }
 
 // ------------------------------------------------------------------ unquantized layer

@@ -76,10 +76,12 @@ hipError_t launch_residual_merge(const float* y12, int64_t n_rows, int64_t n, co
 
 int64_t mx_rows8(int64_t rows);
 hipError_t launch_mx_quant(const void* x, int dtype, int64_t ldx, int64_t rows, int64_t k, int fmt, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st, bool had = false, int exp_offset = 0);
+                           uint8_t* scales, hipStream_t st, bool had = false, int exp_offset = 0,
+                           bool kblock = false);
 int64_t mx_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* sa, int fa, const uint8_t* b, const uint8_t* sb, int64_t m,
-                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, void* ws, hipStream_t st);
+                          int64_t n, int64_t k, void* y, int out_dt, int64_t ldy, void* ws, hipStream_t st,
+                          bool b_kblock);
 
 struct DenseParams {
   const void* x;

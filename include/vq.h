@@ -64,7 +64,10 @@ typedef enum vq_gran {
 /* MX element formats: the codes of the scaled MFMA's operand formats. */
 typedef enum vq_mx_fmt {
   VQ_MXFP6 = 2, /* FP6 E2M3: sign, 2 exponent bits (bias 1), 3 mantissa bits; largest 7.5 */
-  VQ_MXFP4 = 4  /* FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; largest 6 */
+  VQ_MXFP4 = 4, /* FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; largest 6 */
+  /* FP4 codes in 64-byte K pieces (weights): the layout of VQ_W_KBLOCK below, four MX
+   * blocks of a row per piece. */
+  VQ_MXFP4_KBLOCK = 4 | 0x100
 } vq_mx_fmt;
 
 #define VQ_K_ALIGN 64        /* K and each K partition are multiples of this */
@@ -300,7 +303,9 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
  * e = -127); each element is v / 2^e rounded to nearest even and clamped to +-6 (FP4)
  * or +-7.5 (FP6); a negative value that rounds to zero keeps its sign bit.
  *   codes   row-major [rows x k*w/8] bytes, w = 4 or 6; element p of a row at bits
- *           [w*p, w*p+w) of the row's little-endian bit string
+ *           [w*p, w*p+w) of the row's little-endian bit string.  VQ_MXFP4_KBLOCK: the
+ *           same FP4 bytes in 64-byte K pieces (byte c of row r at (c / 64) * rows * 64 +
+ *           r * 64 + c % 64, the last piece padded when k % 128 == 64), for weights
  *   scales  E8M0 bytes in step-major order [k/64][rows8][2], rows8 = rows rounded up to a
  *           multiple of 8 (byte (t * rows8 + r) * 2 + h = block 2t + h of row r); bytes
  *           of the padding rows are not written
@@ -312,7 +317,7 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
  *   Errors: INVALID_ARG, SHAPE, UNSUPPORTED (fmt).
  * vq_mx_gemm: y[i,j] = sum_k dec(a[i,k]) * dec(b[j,k]) on the matrix cores (block scales
  *   applied there, float32 accumulation), then RNE to out_dt.  a: activations [m x k]
- *   in fa (MXFP4 or MXFP6); b: weights [n x k], MXFP4 only (fb); codes and scales
+ *   in fa (MXFP4 or MXFP6); b: weights [n x k], fb MXFP4 or MXFP4_KBLOCK; codes and scales
  *   16-byte aligned; y as for vq_qgemm_dequant.  The sums are accumulated in float32 by
  *   the hardware, so y equals the exact sum rounded to float32 only up to the
  *   accumulation's rounding.  ws: device workspace of vq_mx_gemm_workspace_bytes(m, n,
@@ -321,8 +326,9 @@ vq_status vq_qgemm_dequant_residual(const int8_t* a, const float* sa, const void
  *   whose float32 partials are added once (y then differs from the unsplit GEMM by that
  *   one rounding, within the same bound, and does not depend on the order the ranges
  *   finish).  Every call leaves the workspace zeroed; calls sharing one must not
- *   overlap.  Errors: INVALID_ARG, SHAPE (k % 64, alignment), UNSUPPORTED (fa, fb other
- *   than MXFP4, or more than 2^28 output tiles of 256 x 256).
+ *   overlap.  Errors: INVALID_ARG, SHAPE (k % 64, alignment), UNSUPPORTED (fa other than
+ *   MXFP4/MXFP6, fb other than MXFP4/MXFP4_KBLOCK, or more than 2^28 output tiles of
+ *   256 x 256).
  */
 int64_t vq_mx_code_bytes(int64_t rows, int64_t k, vq_mx_fmt fmt);
 int64_t vq_mx_scale_bytes(int64_t rows, int64_t k);

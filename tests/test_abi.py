@@ -308,6 +308,10 @@ def test_mx_size_helpers(lib):
     assert lib.vq_mx_code_bytes(10, 128, MXFP6) == 10 * 96
     assert lib.vq_mx_code_bytes(10, 100, MXFP4) == 0
     assert lib.vq_mx_code_bytes(10, 128, 3) == 0
+    # FP4 codes in 64-byte K pieces: ceil(k / 2 / 64) pieces of rows * 64 bytes
+    assert lib.vq_mx_code_bytes(3072, 12288, MXFP4 | 0x100) == 96 * 3072 * 64
+    assert lib.vq_mx_code_bytes(10, 192, MXFP4 | 0x100) == 2 * 10 * 64
+    assert lib.vq_mx_code_bytes(10, 192, MXFP6 | 0x100) == 0
     # step-major E8M0 scales: [k/64][rows rounded up to 8][2]
     assert lib.vq_mx_scale_bytes(17776, 12288) == 192 * 17776 * 2
     assert lib.vq_mx_scale_bytes(3, 128) == 2 * 8 * 2
@@ -322,6 +326,8 @@ def test_mx_size_helpers(lib):
     (dict(rows=0), INVALID),
     (dict(ldx=100), INVALID),
     (dict(fmt=3), UNSUP),
+    (dict(fmt=MXFP6 | 0x100), UNSUP),  # K pieces hold FP4 codes only
+    (dict(fmt=MXFP4 | 0x100, k=96, ldx=96), SHAPE),
     (dict(k=96, ldx=96), SHAPE),
     (dict(ldx=132), SHAPE),
     (dict(x=ctypes.c_void_p(0x10008)), SHAPE),
@@ -343,6 +349,8 @@ def test_mx_quant_rotated_validation(lib):
     assert call(ldx=128) == INVALID
     assert call(off=65) == INVALID
     assert call(fmt=3) == UNSUP
+    assert call(fmt=MXFP6 | 0x100) == UNSUP
+    assert call(fmt=MXFP4 | 0x100, k=192, ldx=192) == SHAPE
     assert call(k=192, ldx=192) == SHAPE  # not a multiple of the 128-point block
     assert call(codes=ctypes.c_void_p(0x10004)) == SHAPE
 
@@ -356,6 +364,10 @@ def test_mx_quant_rotated_validation(lib):
     (dict(ldy=10), INVALID),
     (dict(fa=3), UNSUP),
     (dict(fb=MXFP6), UNSUP),
+    (dict(fa=MXFP4 | 0x100), UNSUP),  # activations are not taken in K pieces
+    (dict(fb=MXFP6 | 0x100), UNSUP),
+    (dict(fb=MXFP4 | 0x100, k=96), SHAPE),
+    (dict(fb=MXFP4 | 0x100, b=ctypes.c_void_p(0x10004)), SHAPE),
     (dict(k=96), SHAPE),
     (dict(sa=ctypes.c_void_p(0x10008)), SHAPE),
     (dict(b=ctypes.c_void_p(0x10004)), SHAPE),

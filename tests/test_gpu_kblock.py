@@ -170,3 +170,59 @@ def test_kblock_binding_checks(vq):
     r4, rs4 = vq.vq_pack_weights(w, 4)
     assert torch.equal(y8, vq.vq_qgemm_dequant(ac, as_, r8, rs8, 8))
     assert torch.equal(y4, vq.vq_qgemm_dequant(ac, as_, r4, rs4, 4))
+
+
+# ------------------------------------------------------------------ MX weights in K pieces
+
+MX_CASES = [
+    # name, m, n, k, activation format, rotated operands
+    ("fp4_two_substeps", 300, 320, 640, "fp4", False),   # K % 128 == 0: 128-deep stages, ping-pong
+    ("fp4_one_substep", 257, 520, 192, "fp4", False),    # K % 128 == 64: 64-deep stages, last piece half used
+    ("fp6", 300, 320, 640, "fp6", False),                # FP6 activations: 64-deep stages
+    ("fp6_ragged", 257, 520, 192, "fp6", False),
+    ("fp4_rotated", 257, 320, 1024, "fp4", True),
+    ("fp6_rotated", 257, 320, 1024, "fp6", True),
+    ("fp4_split", 300, 320, 6144, "fp4", False),         # remainder split through the workspace
+    ("fp6_split", 300, 320, 6144, "fp6", False),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_mx_kblock_weights_match_oracle_and_row_major(vq, case):
+    """MXFP4 weights in 64-byte K pieces: the pieces read back into rows are the oracle's
+    packed codes, the scales are unchanged, and the GEMM gives the row-major layout's
+    output bit for bit, within the float32 summation bound of the oracle's exact sum."""
+    from oracle import mx, numerics
+    name, m, n, k, fa, rot = case
+    print(f"mx kblock case: {case}", flush=True)
+    g = np.random.default_rng(m + n + k)
+    x32 = g.standard_normal((m, k)).astype(np.float32)
+    x32 *= np.exp2(g.integers(-8, 9, size=(m, k // 32))).repeat(32, axis=1).astype(np.float32)
+    x = gen.to_storage(x32, "bf16")
+    w = gen.to_storage(g.standard_normal((n, k)).astype(np.float32), "bf16")
+    kw_a = dict(had_block=128) if rot else {}
+    kw_b = dict(had_block=128, exp_offset=-7) if rot else {}
+    ac_d, as_d = vq.vq_mx_quant(x.to(DEV), fa, **kw_a)
+    bc_r, bs_r = vq.vq_mx_quant(w.to(DEV), "fp4", **kw_b)
+    bc_b, bs_b = vq.vq_mx_quant(w.to(DEV), "fp4", kblock=True, **kw_b)
+    y_r = vq.vq_mx_gemm(ac_d, as_d, fa, bc_r, bs_r, "fp4", torch.float32)
+    y_b = vq.vq_mx_gemm(ac_d, as_d, fa, bc_b, bs_b, "fp4", torch.float32)
+    y16 = vq.vq_mx_gemm(ac_d, as_d, fa, bc_b, bs_b, "fp4", torch.bfloat16)
+    torch.cuda.synchronize()
+    assert tuple(bc_b.shape) == ((k // 2 + 63) // 64, n, 64)
+    xf, wf = numerics.to_f32(npb(x), "bf16"), numerics.to_f32(npb(w), "bf16")
+    if rot:
+        ac, asc = mx.quantize_rotated(xf, fa)
+        bc, bsc = mx.quantize_rotated(wf, "fp4", exp_offset=-7)
+    else:
+        ac, asc = mx.quantize(xf, fa)
+        bc, bsc = mx.quantize(wf, "fp4")
+    assert_same(rows_of_pieces(bc_b.cpu().numpy().reshape(-1), n, k // 2), mx.pack(bc, "fp4"), "codes in pieces")
+    assert torch.equal(bs_b, bs_r), "scales"
+    assert torch.equal(y_b, y_r), "outputs of the two layouts"
+    assert torch.equal(y16, y_b.to(torch.bfloat16)), "16-bit output = float32 output rounded once"
+    exact = mx.gemm(ac, asc, fa, bc, bsc, "fp4")
+    mag = np.abs(mx.dequantize(ac, asc, fa)) @ np.abs(mx.dequantize(bc, bsc, "fp4")).T
+    bound = (k / 32 + 2) * 2.0 ** -24 * mag
+    err = np.abs(y_b.cpu().numpy().astype(np.float64) - exact)
+    assert np.all(err <= bound + 1e-300), float((err / np.maximum(bound, 1e-300)).max())
