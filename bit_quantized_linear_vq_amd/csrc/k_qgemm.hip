@@ -448,6 +448,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // A tile inside the output with aligned rows stores without per-lane guards.
     const bool full = g.vec_store && cm0 + BM <= g.m && cn0 + BN <= g.n && !g.accd;
 
+    if (!DUAL && g.accd) {  // test hook: the int32 accumulators (with the 4-bit shift), before any scaling
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = cm0 + mrow + mb * 32;
+            const int n = cn0 + ncol + nb * 32 + 8 * (e >> 2) + (e & 3);
+            int a0 = acc[mb][nb][e];
+            if constexpr (BBITS == 4) a0 >>= 4;
+            if (m < g.m && n < g.n) g.accd[(int64_t)m * g.n + n] = a0;
+          }
+    }
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
       const int ml = mrow + mb * 32;
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
               yv = yv + y1;
               if (g.accd && m < g.m && n + r < g.n) g.accd[mn + (int64_t)m * g.n + n + r] = a1;
             }
-            if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
+            if (DUAL && g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
             out[r] = yv;
           }
           if constexpr (HALF_OUT) {
@@ -715,11 +729,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bool full = g.vec_store && cm0 + BM <= g.m && cn0 + BN <= g.n && !g.accd;
     pend = HALF_OUT && has_next && full;
     typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+    // The lane's row and column scales, read once per tile and waited for once: its
+    // columns are the same for every row block.
+    float sa_r[MBLK];
+    v4f sb_r[NBLK][4];
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) sa_r[mb] = s_sa[buf][wm * WTM + rl + mb * 32];
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sb_r[nb][q] = *reinterpret_cast<const v4f*>(&s_sb[buf][wn * WTN + 4 * kc + nb * 32 + 8 * q]);
+    if (g.accd) {  // test hook: the int32 accumulators, before any scaling
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = cm0 + wm * WTM + rl + mb * 32;
+            const int n = cn0 + wn * WTN + 4 * kc + nb * 32 + 8 * (e >> 2) + (e & 3);
+            if (m < g.m && n < g.n) g.accd[(int64_t)m * g.n + n] = acc[mb][nb][e];
+          }
+    }
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
       const int ml = wm * WTM + rl + mb * 32;
       const int m = cm0 + ml;
-      const float sa0 = s_sa[buf][ml];
+      const float sa0 = sa_r[mb];
 #pragma unroll
       for (int nb = 0; nb < NBLK; ++nb) {
         unsigned pk[8];
@@ -727,14 +763,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int q = 0; q < 4; ++q) {
           const int nl = wn * WTN + 4 * kc + nb * 32 + 8 * q;
           const int n = cn0 + nl;
-          const v4f sb0 = *reinterpret_cast<const v4f*>(&s_sb[buf][nl]);
+          const v4f sb0 = sb_r[nb][q];
           float out[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int a0 = acc[mb][nb][4 * q + r];
             const float t0 = sa0 * sb0[r];
             out[r] = (float)a0 * t0;
-            if (g.accd && m < g.m && n + r < g.n) g.accd[(int64_t)m * g.n + n + r] = a0;
           }
           if constexpr (HALF_OUT) {
             pk[2 * q] = cvt_pair<OUT_DT>(out[0], out[1]);
