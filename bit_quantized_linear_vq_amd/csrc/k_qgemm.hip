@@ -671,39 +671,73 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
   for (int s = 0; s < D; ++s)
     if (s < nk) issue(s * ROW, s);
+  typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
   int buf = 0;
-  // pend: the previous tile issued exactly 16 vector stores after this tile's first loads,
-  // so waits for this tile's first stages leave those stores in flight (vmcnt is in order).
-  bool pend = false;
+  // pend: the number of output stores (16, PD or 0) the previous tile issued after this
+  // tile's first loads, so that waits for this tile's first stages leave them in flight
+  // (vmcnt retires in order).
+  int pend = 0;
+  // The stores of the last NDEF / 4 row blocks of a whole 16-bit tile are deferred into the next
+  // tile's first NDEF stages, one per stage after that stage's own loads: all CUs finish
+  // their tiles together, and storing a whole tile at once made every CU's tile change
+  // wait for the same burst of writes.  dq holds their payloads, dptr the first one's
+  // address; dcnt is NDEF while they are pending, else 0.
+  constexpr int NDEF = 4;
+  constexpr int MB_DEF = MBLK - NDEF / 4;  // first deferred row block
+  constexpr int PD = 4 * NBLK * MBLK / 2 - NDEF;  // stores issued at a tile change that defers (of 16)
+  u4v dq[NDEF];
+  h_t* dptr = nullptr;
+  int dcnt = 0;
+  const int64_t d_mb = (int64_t)32 * g.ldy;  // elements from one row block to the next
+  auto def_store = [&](int j) {  // deferred store j = 4 * (mb - MB_DEF) + 2 * nb + pr
+    *reinterpret_cast<u4v*>(dptr + (j >> 2) * d_mb + ((j >> 1) & 1) * 32 + (j & 1) * 16) = dq[j];
+  };
+  // One K stage of the ping-pong loop.  wsel: loads and stores allowed in flight beyond
+  // the next stage's own loads (0; 1: a deferred store issued in the previous stage;
+  // PD or 16: the previous tile's last stores).
+  auto stage = [&](int p, int wsel, int dj) {
+    // memory phase (leaders: while the followers compute stage p - 1)
+    read_stage(p % NST);
+    issue((p + D) * ROW, (p + D) % NST);
+    auto wait_next = [&]() {
+      if (wsel == 16) wait_vmcnt<(D - 1) * L + 16>();
+      else if (wsel == PD) wait_vmcnt<(D - 1) * L + PD>();
+      else if (wsel == 1) wait_vmcnt<(D - 1) * L + 1>();
+      else wait_vmcnt<(D - 1) * L>();
+    };
+    if (grp == 1) wait_next();
+    lds_reads_done();
+    sched_barrier_all();
+    // compute phase
+    compute();
+    if (grp == 0) wait_next();
+    if (dj >= 0) def_store(dj);
+    sched_barrier_all();
+  };
   for (;;) {
 #pragma unroll
     for (int i = 0; i < MBLK; ++i)
 #pragma unroll
       for (int j = 0; j < NBLK; ++j) acc[i][j] = v16i{};
-    if (pend && nk > D) wait_vmcnt<(D - 1) * L + 16>();
+    if (pend == 16 && nk > D) wait_vmcnt<(D - 1) * L + 16>();
+    else if (pend == PD && nk > D) wait_vmcnt<(D - 1) * L + PD>();
     else wait_groups(min(D, nk) - 1);
     sched_barrier_all();
     if (grp == 1) sched_barrier_all();
     int p = 0;
-    for (; p + D < nk; ++p) {
-      // memory phase (leaders: while the followers compute stage p - 1)
-      read_stage(p % NST);
-      issue((p + D) * ROW, (p + D) % NST);
-      const bool early = pend && p < D - 1;  // stage p + 1 was loaded before the stores
-      if (grp == 1) {
-        if (early) wait_vmcnt<(D - 1) * L + 16>();
-        else wait_vmcnt<(D - 1) * L>();
-      }
-      lds_reads_done();
-      sched_barrier_all();
-      // compute phase
-      compute();
-      if (grp == 0) {
-        if (early) wait_vmcnt<(D - 1) * L + 16>();
-        else wait_vmcnt<(D - 1) * L>();
-      }
-      sched_barrier_all();
+    // stage 0 waits past the previous tile's last stores (pend); stages 1 .. NDEF past the
+    // deferred store of the stage before
+    if (dcnt) {
+#pragma unroll
+      for (int j = 0; j < NDEF; ++j) stage(j, j == 0 ? pend : 1, j);
+      p = NDEF;
+      stage(p, 1, -1);
+      ++p;
+    } else if (p + D < nk) {
+      stage(0, pend, -1);
+      ++p;
     }
+    for (; p + D < nk; ++p) stage(p, 0, -1);
     for (; p < nk; ++p) {
       read_stage(p % NST);
       const int later = nk - p - 2;
@@ -727,8 +761,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         if (s < nk) issue(s * ROW, s);
     }
     const bool full = g.vec_store && cm0 + BM <= g.m && cn0 + BN <= g.n && !g.accd;
-    pend = HALF_OUT && has_next && full;
-    typedef typename std::conditional<OUT_DT == DT_BF16, __bf16, _Float16>::type h_t;
+    // deferral needs the next tile's loop to have more than NDEF + 1 stages before its tail
+    const bool defer = HALF_OUT && has_next && full && nk > NDEF + 1 + D;
+    pend = HALF_OUT && has_next && full ? (defer ? PD : 16) : 0;
+    dcnt = defer ? NDEF : 0;
+    if (defer) dptr = reinterpret_cast<h_t*>(g.y) + (int64_t)(cm0 + wm * WTM + rl + 32 * MB_DEF) * g.ldy + cn0 + wn * WTN + 8 * kc;
     // The lane's row and column scales, read once per tile and waited for once: its
     // columns are the same for every row block.
     float sa_r[MBLK];
@@ -786,7 +823,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const u4v w = {s0[0], s1[0], s0[1], s1[1]};
             const int no = cn0 + wn * WTN + nb * 32 + 16 * pr + 8 * kc;
             h_t* dst = reinterpret_cast<h_t*>(g.y) + (int64_t)m * g.ldy + no;
-            if (full) {
+            if (defer && mb >= MB_DEF) {
+              dq[4 * (mb - MB_DEF) + 2 * nb + pr] = w;
+            } else if (full) {
               *reinterpret_cast<u4v*>(dst) = w;
             } else if (m < g.m && no < g.n) {
               if (g.vec_store && no + 8 <= g.n) {
