@@ -666,6 +666,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   int t = blockIdx.x;
   if (t >= g.items) return;
+  // Staggered start: every CU changes tiles at the same moment, so their output stores
+  // would fall into the same few microseconds.  When the last round is partial, the
+  // workgroups with one tile fewer than the others (a whole tile of slack) start late,
+  // spread evenly over about a quarter of a tile (about 360 counter ticks per 64-code
+  // stage plus the tile change; measured at the fused-QKV shape), so that the critical
+  // path, the workgroups with the extra tile, is not delayed.
+  {
+    const int G = (int)gridDim.x, rem = g.items % G;
+    if (rem > 0 && g.items > G && t >= rem) {
+      const uint64_t quarter = (uint64_t)nk * 360 + 3100;
+      const uint64_t delay = quarter * (uint64_t)(t - rem) / (uint64_t)(G - rem);
+      const uint64_t s0 = __builtin_amdgcn_s_memtime();
+      while (__builtin_amdgcn_s_memtime() - s0 < delay) __builtin_amdgcn_s_sleep(8);
+    }
+  }
   set_tile(t);
   load_scales(0);
 #pragma unroll
